@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Throughput of FP32 SGEMM C = A.B on one MI355X.
+
+A step is one call of ``sgemm`` (every kernel the default plan enqueues) on
+the workload's seeded synthetic inputs, already resident in HBM.  The default
+workload is M = N = K = 4096 with A, B i.i.d. uniform on [-1, 1).
+
+Prints one JSON line with the throughput (TFLOP/s, 2MNK per step), the
+roofline of the dominant kernel (its own launch time from HIP events on the
+launch stream, against the FP32 matrix-core peak), and the host oracle's
+throughput on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_TFLOPS = 157.3        # MI355X dense FP32 (vector and matrix), 256 CU x 2.4 GHz x 256 FLOP/clk
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+METRIC = "FP32 SGEMM TFLOPS at M=N=K=4096 and % of MI355X FP32 peak"
+DEFAULT_WORKLOAD = "sgemm_4096"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--path", default="auto")
+    ap.add_argument("--tile", type=int, default=-1)
+    ap.add_argument("--split-k", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target host time of the oracle sample (0 = skip the CPU baseline)")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="size of the cache-flush buffer for the flushed per-launch median")
+    return ap.parse_args()
+
+
+def algorithmic(w):
+    flops = 2 * w.M * w.N * w.K
+    bytes_ = 4 * (w.M * w.K + w.K * w.N + w.M * w.N)
+    return flops, bytes_
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, digest):
+    """HBM traffic per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            db = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    rec = db.get(kernel_key)
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, A, B, target_s):
+    """The host oracle on the first R rows of the workload (R chosen so the
+    timed run takes about target_s seconds), scaled to TFLOP/s."""
+    import oracle
+    An = A.numpy()
+    Bn = B.numpy()
+    rows = max(1, min(w.M, 8))
+    t0 = time.perf_counter()
+    oracle.sgemm(An[:rows], Bn)
+    t = time.perf_counter() - t0
+    rows = max(1, min(w.M, int(rows * target_s / max(t, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.sgemm(An[:rows], Bn)
+    t = time.perf_counter() - t0
+    flops = 2 * rows * w.N * w.K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {rows} of {w.M} rows of C ({rows}x{w.N}x{w.K}), fp64 accumulation, {t:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the library is a single-GPU SGEMM)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dense_fp32_matrix_amd as lib
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    lib.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = workloads.CONFIGS[args.workload]
+    A_host = w.a()
+    B_host = w.b()
+    A = A_host.to(dev)
+    B = B_host.to(dev)
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    opts = {}
+    if args.path != "auto" or args.tile >= 0 or args.split_k:
+        opts = {"path": args.path, "tile": args.tile, "split_k": args.split_k}
+    plan = lib.sgemm_plan_query(w.M, w.N, w.K, A.data_ptr(), w.lda, B.data_ptr(), w.ldb, C.data_ptr(), w.N,
+                                **opts)
+
+    def step():
+        if opts:
+            lib.sgemm_ex(A, B, C, **opts)
+        else:
+            lib.sgemm(A, B, C)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back steps, plus events around every step on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = wall * 1e3 / args.steps
+
+    flops, alg_bytes = algorithmic(w)
+    value = flops * args.steps / wall / 1e12
+
+    # flushed per-launch median: overwrite a buffer larger than L2 + MALL before each launch
+    flush = torch.empty(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    fl = []
+    for _ in range(10):
+        flush.fill_(1.0)
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        step()
+        e.record(stream)
+        torch.cuda.synchronize()
+        fl.append(s.elapsed_time(e))
+    del flush
+
+    kernel_ms = statistics.mean(per_step_ms)
+    main_kernel = {1: "naive_gemm_kernel", 2: "valu_gemm_kernel", 3: "mfma_gemm_kernel",
+                   4: "skinny_gemm_kernel"}.get(plan["path"], "?")
+    src = {1: "simple.hip", 2: "valu.hip", 3: "mfma.hip", 4: "skinny.hip"}.get(plan["path"], "mfma.hip")
+    digest = source_digest([f"dense_fp32_matrix_amd/csrc/{src}", "dense_fp32_matrix_amd/csrc/kernels.hpp"])
+    key = f"{main_kernel}:{w.name}:tile{plan['tile']}:split{plan['split_k']}:vec{plan['vector']}"
+    hbm_bound = w.M <= 16
+    if hbm_bound:
+        achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = flops / (kernel_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma" if plan["path"] in (3, 4) else "alu", "achieved": achieved,
+                "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS}
+    roof["traffic"] = load_traffic(key, digest)
+    roof["kernel"] = main_kernel
+    roof["launch_ms"] = kernel_ms
+    roof["launches_per_step"] = plan["launches"]
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, A_host, B_host, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_fp32_peak": 100.0 * value / PEAK_FP32_TFLOPS,
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda, "ldb": w.ldb, "ldc": w.N,
+                   "inputs": f"A~{w.a_kind}, B~{w.b_kind}", "path": plan["path_name"], "tile": plan["tile"],
+                   "bm": plan["bm"], "bn": plan["bn"], "bk": plan["bk"], "split_k": plan["split_k"],
+                   "vector_loads": bool(plan["vector"]), "workgroups": plan["workgroups"]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "flushed_launch_ms_median": statistics.median(fl),
+        "flushed_tflops": flops / (statistics.median(fl) * 1e-3) / 1e12,
+        "step_ms_min": min(per_step_ms),
+        "step_ms_median": statistics.median(per_step_ms),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

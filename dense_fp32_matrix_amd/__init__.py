@@ -1,0 +1,207 @@
+"""Python binding of ``libsgemm.so``: row-major FP32 C = A.B on an MI355X.
+
+Argument marshalling only -- every step of the product runs in the library's
+gfx950 kernels.  The functions carry the C interface's names
+(``include/sgemm.h``); tensors are torch CUDA (HIP) float32 matrices with unit
+column stride, and the row stride is passed as the leading dimension.  If the
+library has not been built, every call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "SgemmError", "PATHS", "sgemm", "sgemm_ex", "sgemm_raw", "sgemm_plan_query", "sgemm_workspace_size",
+    "sgemm_tile_info", "sgemm_status_string", "sgemm_version", "library_path", "load_library",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsgemm.so")
+_lib = None
+
+PATHS = {"auto": 0, "naive": 1, "valu": 2, "mfma": 3, "skinny": 4}
+_PATH_NAMES = {v: k for k, v in PATHS.items()}
+
+SGEMM_OK = 0
+_STATUS = {0: "SGEMM_OK", 1: "SGEMM_ERR_INVALID_ARG", 2: "SGEMM_ERR_UNSUPPORTED", 3: "SGEMM_ERR_HIP",
+           4: "SGEMM_ERR_ALLOC"}
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {sgemm_status_string(status)}" if what else sgemm_status_string(status))
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("tile", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("vector", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("tile", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("vector", ctypes.c_int32), ("bm", ctypes.c_int32), ("bn", ctypes.c_int32),
+                ("bk", ctypes.c_int32), ("threads", ctypes.c_int32), ("tiles_m", ctypes.c_int64),
+                ("tiles_n", ctypes.c_int64), ("k_chunk", ctypes.c_int64), ("workgroups", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_size_t), ("launches", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load ``libsgemm.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with dense_fp32_matrix_amd.build.build()")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32
+    mm = [i64, i64, i64, p, i64, p, i64, p, i64]
+    lib.sgemm.argtypes = mm + [p]
+    lib.sgemm.restype = ctypes.c_int
+    lib.sgemm_ex.argtypes = mm + [p, ctypes.POINTER(_Options)]
+    lib.sgemm_ex.restype = ctypes.c_int
+    lib.sgemm_plan_query.argtypes = mm + [ctypes.POINTER(_Options), ctypes.POINTER(_Plan)]
+    lib.sgemm_plan_query.restype = ctypes.c_int
+    lib.sgemm_workspace_size.argtypes = [i64] * 6
+    lib.sgemm_workspace_size.restype = ctypes.c_size_t
+    ip = ctypes.POINTER(i32)
+    lib.sgemm_tile_info.argtypes = [i32, i32, ip, ip, ip, ip, ip]
+    lib.sgemm_tile_info.restype = ctypes.c_int
+    lib.sgemm_status_string.argtypes = [ctypes.c_int]
+    lib.sgemm_status_string.restype = ctypes.c_char_p
+    lib.sgemm_version.argtypes = []
+    lib.sgemm_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _options(path="auto", tile=-1, split_k=0, vector=0, workspace=None, workspace_bytes=0) -> _Options:
+    o = _Options()
+    o.path = PATHS[path] if isinstance(path, str) else int(path)
+    o.tile = int(tile)
+    o.split_k = int(split_k)
+    o.vector = int(vector)
+    if workspace is not None and not isinstance(workspace, int):
+        workspace_bytes = workspace.numel() * workspace.element_size()
+        workspace = workspace.data_ptr()
+    o.workspace = workspace
+    o.workspace_bytes = int(workspace_bytes)
+    return o
+
+
+def _matrix(t, name):
+    """(pointer, rows, cols, ld) of a 2-D float32 device tensor with unit column stride."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D torch tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be on a GPU")
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride (row-major)")
+    ld = t.stride(0) if rows > 1 else max(cols, 1)
+    return (t.data_ptr() if t.numel() else None), rows, cols, max(ld, cols, 1)
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def sgemm_raw(M, N, K, A, lda, B, ldb, C, ldc, stream=0, opts: Optional[_Options] = None) -> int:
+    """The C call with integer device addresses; returns the status code."""
+    lib = load_library()
+    if opts is None:
+        return lib.sgemm(M, N, K, A, lda, B, ldb, C, ldc, stream)
+    return lib.sgemm_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, ctypes.byref(opts))
+
+
+def _call(A, B, C, stream, opts):
+    import torch
+    a, M, K, lda = _matrix(A, "A")
+    b, K2, N, ldb = _matrix(B, "B")
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: A is {M}x{K}, B is {K2}x{N}")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    c, Mc, Nc, ldc = _matrix(C, "C")
+    if (Mc, Nc) != (M, N):
+        raise ValueError(f"C must be {M}x{N}, got {Mc}x{Nc}")
+    if not (A.device == B.device == C.device):
+        raise ValueError("A, B and C must be on the same device")
+    with torch.cuda.device(A.device):
+        st = sgemm_raw(M, N, K, a, lda, b, ldb, c, ldc, _stream_handle(stream, A.device), opts)
+    if st != SGEMM_OK:
+        raise SgemmError(st, "sgemm")
+    return C
+
+
+def sgemm(A, B, C=None, stream=None):
+    """C = A.B (overwrites and returns C; allocates it when None), enqueued on
+    ``stream`` (default: torch's current stream of A's device)."""
+    return _call(A, B, C, stream, None)
+
+
+def sgemm_ex(A, B, C=None, stream=None, *, path="auto", tile=-1, split_k=0, vector=0, workspace=None):
+    """``sgemm`` with explicit options: ``path`` in PATHS, ``tile`` index, ``split_k``
+    slices, ``vector=1`` to force 4-byte loads, optional ``workspace`` tensor."""
+    return _call(A, B, C, stream, _options(path, tile, split_k, vector, workspace))
+
+
+def sgemm_plan_query(M, N, K, A=0x100000, lda=None, B=0x200000000, ldb=None, C=0x400000000, ldc=None,
+                     **options) -> dict:
+    """The plan sgemm_ex would use for these sizes, leading dimensions and
+    (integer) addresses.  Host only.  Raises SgemmError on invalid arguments."""
+    lib = load_library()
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    o = _options(**options)
+    pl = _Plan()
+    st = lib.sgemm_plan_query(M, N, K, A, lda, B, ldb, C, ldc, ctypes.byref(o), ctypes.byref(pl))
+    if st != SGEMM_OK:
+        raise SgemmError(st, "sgemm_plan_query")
+    out = {name: getattr(pl, name) for name, _ in _Plan._fields_ if name != "reserved"}
+    out["path_name"] = _PATH_NAMES.get(out["path"], "?")
+    return out
+
+
+def sgemm_workspace_size(M, N, K, lda=None, ldb=None, ldc=None) -> int:
+    lib = load_library()
+    return int(lib.sgemm_workspace_size(M, N, K, max(K, 1) if lda is None else lda,
+                                        max(N, 1) if ldb is None else ldb, max(N, 1) if ldc is None else ldc))
+
+
+def sgemm_tile_info(path, tile=0) -> Optional[dict]:
+    lib = load_library()
+    vals = [ctypes.c_int32() for _ in range(5)]
+    p = PATHS[path] if isinstance(path, str) else int(path)
+    st = lib.sgemm_tile_info(p, tile, *[ctypes.byref(v) for v in vals])
+    if st != SGEMM_OK:
+        return None
+    count, bm, bn, bk, threads = (v.value for v in vals)
+    return {"count": count, "bm": bm, "bn": bn, "bk": bk, "threads": threads}
+
+
+def sgemm_status_string(status: int) -> str:
+    try:
+        return load_library().sgemm_status_string(status).decode()
+    except RuntimeError:
+        return _STATUS.get(status, f"status {status}")
+
+
+def sgemm_version() -> str:
+    return load_library().sgemm_version().decode()

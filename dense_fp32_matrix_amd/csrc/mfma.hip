@@ -1,0 +1,280 @@
+// FP32 matrix-core SGEMM for gfx950.
+//
+// Structure (the block -> wave -> lane tiling of "GEMM from naive to tiled",
+// sections 四-六, carried onto CDNA4 matrix cores):
+//   * Each workgroup owns one BM x BN tile of C (output-stationary, as in the
+//     throughput-matching page "如何让计算受限问题真正达到计算受限", section 1.2)
+//     and walks K in steps of BK.
+//   * Per K-step, the A tile (BM x BK) and B tile (BK x BN) go global -> VGPR
+//     -> LDS with coalesced loads; 16-byte loads when rows are 16-byte
+//     aligned, 4-byte loads otherwise; out-of-range elements are zero-filled
+//     (the padding argument of section 七: a zero term leaves the sum alone).
+//   * Two LDS stages: the loads of step t+1 are issued before step t is
+//     computed and land in the other stage afterwards, so one barrier per
+//     K-step suffices (section 六.1; "SGEMM 纯 CUDA 优化总结", ex9).
+//   * Each wave owns a WM x WN sub-tile as (WM/32) x (WN/32) blocks of
+//     v_mfma_f32_32x32x2_f32: true FP32 products, FP32 accumulation.
+//
+// Operand layout of v_mfma_f32_32x32x2_f32 (wave64):
+//   A operand: lane l holds A[i = l % 32][kk = l / 32]           (32 x 2)
+//   B operand: lane l holds B[kk = l / 32][j = l % 32]           (2 x 32)
+//   D        : lane l, register r holds D[i][j] with j = l % 32,
+//              i = 8 * (r / 4) + 4 * (l / 32) + (r % 4)          (32 x 32)
+// A k-group of 8 is split so that lane half h = l / 32 takes k = 4h + q for
+// q = 0..3 and instruction q contracts k in {q, 4 + q}: every k of the group
+// is used once, and the A fragment of a lane is 4 consecutive k of one row,
+// read from LDS with a single 16-byte read.
+//
+// LDS layout, per stage:
+//   As[BM][BK + 4]  (row-major like A; the +4 floats make the row stride an
+//                    odd multiple of 16 bytes, so the 16-byte fragment reads
+//                    of consecutive rows fall in distinct bank groups)
+//   Bs[BK][BN + 8]  (row-major like B; the two lane halves read rows 4 apart,
+//                    offset by 4 * (BN + 8) = 32 (mod 64) banks)
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+namespace sgemm_impl {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+struct MfmaCfg {
+    static constexpr int T = 64 * WGM * WGN;
+    static constexpr int WM = BM / WGM;
+    static constexpr int WN = BN / WGN;
+    static constexpr int MB = WM / 32;
+    static constexpr int NB = WN / 32;
+    static constexpr int LDA_S = BK + 4;
+    static constexpr int LDB_S = BN + 8;
+    static constexpr int A_STAGE = BM * LDA_S;
+    static constexpr int B_STAGE = BK * LDB_S;
+    static constexpr int STAGE = A_STAGE + B_STAGE;
+    // elements per thread per K-step
+    static constexpr int A_PER = BM * BK / T;
+    static constexpr int B_PER = BK * BN / T;
+    // 16-byte vectors per thread per K-step
+    static constexpr int A_V = A_PER / 4;
+    static constexpr int B_V = B_PER / 4;
+    static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+    static_assert(A_PER * T == BM * BK && B_PER * T == BK * BN, "loader must cover the tile");
+    static_assert(!VEC || (A_V * 4 == A_PER && B_V * 4 == B_PER), "vector loader must cover the tile");
+    static_assert(T % (BK / 4) == 0 && T % (BN / 4) == 0, "vector loader rows");
+    static_assert(T % BK == 0 && T % BN == 0, "scalar loader rows");
+    static_assert(2 * STAGE * 4 <= 160 * 1024, "LDS budget");
+};
+
+template <int BM, int BN, int BK, int WGM, int WGN, bool VEC, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
+                          amdgpu_waves_per_eu(WPE, WPE)))
+void mfma_gemm_kernel(GemmArgs g) {
+    using P = MfmaCfg<BM, BN, BK, WGM, WGN, VEC>;
+    __shared__ __attribute__((aligned(16))) float smem[2 * P::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WGN;
+    const int wn = wave % WGN;
+
+    const int bid = blockIdx.x;
+    const int tm = bid % g.tiles_m;
+    const int tn = bid / g.tiles_m;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+
+    const int kb = blockIdx.z * g.k_chunk;
+    const int ke = min(g.K, kb + g.k_chunk);
+    const int steps = (ke - kb + BK - 1) / BK;
+
+    // ---- loader bookkeeping (constant over the K loop) ----
+    // VEC: vector r of A covers row q / (BK/4), columns 4 * (q % (BK/4)) .. +3, q = tid + r*T
+    //      vector r of B covers row q / (BN/4), columns 4 * (q % (BN/4)) .. +3
+    // scalar: element r of A is row q / BK, column q % BK; of B row q / BN, column q % BN
+    constexpr int AN = VEC ? P::A_V : P::A_PER;
+    constexpr int BNL = VEC ? P::B_V : P::B_PER;
+    constexpr int A_COLS = VEC ? BK / 4 : BK;     // loader slots per A row
+    constexpr int B_COLS = VEC ? BN / 4 : BN;     // loader slots per B row
+    constexpr int A_W = VEC ? 4 : 1;              // elements per slot
+
+    int64_t a_off[AN];
+    int a_kc[AN];          // column within the K-step
+    bool a_rok[AN];
+    int a_lds[AN];
+#pragma unroll
+    for (int r = 0; r < AN; ++r) {
+        const int q = tid + r * P::T;
+        const int row = q / A_COLS;
+        const int col = (q % A_COLS) * A_W;
+        const int gm = m0 + row;
+        a_rok[r] = gm < g.M;
+        a_off[r] = (int64_t)(a_rok[r] ? gm : 0) * g.lda + col;
+        a_kc[r] = col;
+        a_lds[r] = row * P::LDA_S + col;
+    }
+    int64_t b_off[BNL];
+    int b_kr[BNL];         // row within the K-step
+    bool b_cok[BNL];
+    int b_lds[BNL];
+#pragma unroll
+    for (int r = 0; r < BNL; ++r) {
+        const int q = tid + r * P::T;
+        const int row = q / B_COLS;
+        const int col = (q % B_COLS) * A_W;
+        const int gn = n0 + col;
+        b_cok[r] = gn < g.N;
+        b_off[r] = (int64_t)row * g.ldb + (b_cok[r] ? gn : 0);
+        b_kr[r] = row;
+        b_lds[r] = P::A_STAGE + row * P::LDB_S + col;
+    }
+
+    f32x4 va[VEC ? AN : 1], vb[VEC ? BNL : 1];
+    float sa[VEC ? 1 : AN], sb[VEC ? 1 : BNL];
+
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int r = 0; r < AN; ++r) {
+            const bool ok = a_rok[r] && (k0 + a_kc[r] < ke);
+            const float* p = ok ? g.A + a_off[r] + k0 : g.A;
+            if constexpr (VEC) {
+                const f32x4 t = *reinterpret_cast<const f32x4*>(p);
+                va[r] = ok ? t : f32x4{0.f, 0.f, 0.f, 0.f};
+            } else {
+                const float t = *p;
+                sa[r] = ok ? t : 0.f;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < BNL; ++r) {
+            const bool ok = b_cok[r] && (k0 + b_kr[r] < ke);
+            const float* p = ok ? g.B + b_off[r] + (int64_t)k0 * g.ldb : g.B;
+            if constexpr (VEC) {
+                const f32x4 t = *reinterpret_cast<const f32x4*>(p);
+                vb[r] = ok ? t : f32x4{0.f, 0.f, 0.f, 0.f};
+            } else {
+                const float t = *p;
+                sb[r] = ok ? t : 0.f;
+            }
+        }
+    };
+    auto store = [&](int buf) {
+        float* s = smem + buf * P::STAGE;
+#pragma unroll
+        for (int r = 0; r < AN; ++r) {
+            if constexpr (VEC) *reinterpret_cast<f32x4*>(s + a_lds[r]) = va[r];
+            else s[a_lds[r]] = sa[r];
+        }
+#pragma unroll
+        for (int r = 0; r < BNL; ++r) {
+            if constexpr (VEC) *reinterpret_cast<f32x4*>(s + b_lds[r]) = vb[r];
+            else s[b_lds[r]] = sb[r];
+        }
+    };
+
+    f32x16 acc[P::MB][P::NB];
+#pragma unroll
+    for (int mb = 0; mb < P::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < P::NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
+
+    const int l32 = lane & 31;
+    const int lh = lane >> 5;
+    // fragment offsets within a stage (floats)
+    const int a_frag = (wm * P::WM + l32) * P::LDA_S + 4 * lh;
+    const int b_frag = P::A_STAGE + (4 * lh) * P::LDB_S + wn * P::WN + l32;
+
+    auto compute = [&](int buf) {
+        const float* s = smem + buf * P::STAGE;
+#pragma unroll
+        for (int kg = 0; kg < BK / 8; ++kg) {
+            f32x4 a[P::MB];
+            float b[P::NB][4];
+#pragma unroll
+            for (int mb = 0; mb < P::MB; ++mb)
+                a[mb] = *reinterpret_cast<const f32x4*>(s + a_frag + mb * 32 * P::LDA_S + 8 * kg);
+#pragma unroll
+            for (int nb = 0; nb < P::NB; ++nb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    b[nb][q] = s[b_frag + (8 * kg + q) * P::LDB_S + nb * 32];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int mb = 0; mb < P::MB; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < P::NB; ++nb)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mb][q], b[nb][q],
+                                                                           acc[mb][nb], 0, 0, 0);
+        }
+    };
+
+    if (steps > 0) {
+        load(kb);
+        store(0);
+        __syncthreads();
+        for (int s = 0; s < steps; ++s) {
+            const bool more = s + 1 < steps;
+            if (more) load(kb + (s + 1) * BK);
+            compute(s & 1);
+            if (more) store((s & 1) ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: overwrite C (masked at the M / N edges) ----
+    float* C = g.C + (int64_t)blockIdx.z * g.c_slice;
+#pragma unroll
+    for (int mb = 0; mb < P::MB; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < P::NB; ++nb) {
+            const int j = n0 + wn * P::WN + nb * 32 + l32;
+            const int ib = m0 + wm * P::WM + mb * 32 + 4 * lh;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = ib + 8 * (r >> 2) + (r & 3);
+                if (i < g.M && j < g.N) C[(int64_t)i * g.ldc + j] = acc[mb][nb][r];
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, int WPE>
+hipError_t launch_one(bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
+    dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n), 1, (unsigned)splits);
+    dim3 block(64 * WGM * WGN);
+    if (vec)
+        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, true, WPE>), grid, block, 0, stream, g);
+    else
+        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, false, WPE>), grid, block, 0, stream, g);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mfma(int tile, bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
+#define SGEMM_MFMA_CASE(ID)                                                                     \
+    case ID:                                                                                    \
+        return launch_one<kMfmaTiles[ID].bm, kMfmaTiles[ID].bn, kMfmaTiles[ID].bk,             \
+                          kMfmaTiles[ID].waves_m, kMfmaTiles[ID].waves_n,                      \
+                          kMfmaTiles[ID].waves_per_simd>(vec, g, splits, stream);
+    switch (tile) {
+        SGEMM_MFMA_CASE(0)
+        SGEMM_MFMA_CASE(1)
+        SGEMM_MFMA_CASE(2)
+        SGEMM_MFMA_CASE(3)
+        SGEMM_MFMA_CASE(4)
+        SGEMM_MFMA_CASE(5)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef SGEMM_MFMA_CASE
+}
+static_assert(kNumMfmaTiles == 6, "launch_mfma covers every MFMA tile");
+
+}  // namespace sgemm_impl

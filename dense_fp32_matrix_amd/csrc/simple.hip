@@ -1,0 +1,103 @@
+// Small kernels: the one-thread-per-output product, the split-K reduction and
+// the zero fill for K == 0.
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+namespace sgemm_impl {
+namespace {
+
+// One thread per C element, operands read straight from global memory
+// ("GEMM from naive to tiled", section 三; the first rung of "SGEMM 纯 CUDA
+// 优化总结").  threadIdx.x runs along N so a wave reads 64 consecutive B
+// floats and one broadcast A float per k.  The sum runs in ascending k with
+// one rounding per fused multiply-add.  Kept as the bring-up and
+// cross-check kernel, not a performance path.
+constexpr int kNaiveX = 64;
+constexpr int kNaiveY = 4;
+
+__global__ __launch_bounds__(kNaiveX * kNaiveY)
+void naive_gemm_kernel(GemmArgs g) {
+    const int64_t tiles_n = g.tiles_n;
+    const int64_t t = blockIdx.x;
+    const int64_t i = (t / tiles_n) * kNaiveY + threadIdx.y;
+    const int64_t j = (t % tiles_n) * kNaiveX + threadIdx.x;
+    if (i >= g.M || j >= g.N) return;
+    const float* a = g.A + i * g.lda;
+    const float* b = g.B + j;
+    float acc = 0.f;
+    for (int k = 0; k < g.K; ++k) acc = __builtin_fmaf(a[k], b[(int64_t)k * g.ldb], acc);
+    g.C[i * g.ldc + j] = acc;
+}
+
+// Deterministic split-K reduction: each output is the sum of the slices'
+// partial products taken in slice order (the workspace variant of "GEMM from
+// naive to tiled", section 十.1, which, unlike atomic adds, always yields the
+// same bits).  The workspace rows are padded to a multiple of 4 floats and
+// 16-byte aligned, so each thread reads 4 consecutive outputs of every slice
+// with one 16-byte load.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256)
+void splitk_reduce_kernel(const float* __restrict__ W, int64_t ldw, int64_t w_slice, int splits,
+                          float* __restrict__ C, int64_t ldc, int32_t M, int32_t N) {
+    const int64_t groups_per_row = ldw / 4;
+    const int64_t total = (int64_t)M * groups_per_row;
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total;
+         v += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = v / groups_per_row;
+        const int64_t j = (v - i * groups_per_row) * 4;
+        if (j >= N) continue;
+        const float* w = W + i * ldw + j;
+        f32x4 s = *reinterpret_cast<const f32x4*>(w);
+        for (int z = 1; z < splits; ++z) s += *reinterpret_cast<const f32x4*>(w + z * w_slice);
+        float* c = C + i * ldc + j;
+        c[0] = s[0];
+        if (j + 1 < N) c[1] = s[1];
+        if (j + 2 < N) c[2] = s[2];
+        if (j + 3 < N) c[3] = s[3];
+    }
+}
+
+__global__ __launch_bounds__(256)
+void fill_zero_kernel(float* __restrict__ C, int64_t ldc, int32_t M, int32_t N) {
+    const int64_t total = (int64_t)M * N;
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total;
+         v += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = v / N;
+        const int64_t j = v - i * N;
+        C[i * ldc + j] = 0.f;
+    }
+}
+
+unsigned grid_for(int64_t items, int64_t per_block) {
+    int64_t blocks = (items + per_block - 1) / per_block;
+    if (blocks > 256 * 16) blocks = 256 * 16;   // grid-stride beyond 16 workgroups per CU
+    if (blocks < 1) blocks = 1;
+    return (unsigned)blocks;
+}
+
+}  // namespace
+
+hipError_t launch_naive(const GemmArgs& g, hipStream_t stream) {
+    dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n));
+    dim3 block(kNaiveX, kNaiveY);
+    hipLaunchKernelGGL(naive_gemm_kernel, grid, block, 0, stream, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const float* W, int64_t ldw, int64_t w_slice, int splits,
+                                float* C, int64_t ldc, int32_t M, int32_t N, hipStream_t stream) {
+    const int64_t items = (int64_t)M * (ldw / 4);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for(items, 256)), dim3(256), 0, stream,
+                       W, ldw, w_slice, splits, C, ldc, M, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* C, int64_t ldc, int32_t M, int32_t N, hipStream_t stream) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for((int64_t)M * N, 256)), dim3(256), 0, stream,
+                       C, ldc, M, N);
+    return hipGetLastError();
+}
+
+}  // namespace sgemm_impl

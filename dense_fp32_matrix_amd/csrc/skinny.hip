@@ -1,0 +1,159 @@
+// Skinny SGEMM (M <= 16) on FP32 matrix cores.
+//
+// With few rows of A every element of B is used at most M times, so the
+// product is bound by reading B once from HBM, not by arithmetic -- the
+// GEMV / decode regime of "GEMM from naive to tiled", section 十.2, and the
+// GEMV example of "如何让计算受限问题真正达到计算受限", section 7.  The kernel
+// is therefore built to stream B with deep memory-level parallelism and no
+// LDS staging:
+//   * a wave owns 64 columns of C and a quarter of the workgroup's K slice;
+//     a workgroup (4 waves) owns 64 columns and one K slice, and slices of
+//     K across workgroups are summed by the split-K reduction;
+//   * lane l = 16 * kk + jj loads B[k][n + 4jj .. 4jj+3] as one 16-byte read
+//     for k = k0 + 4kk + t (t = 0..3): 16 lanes cover a 256-byte run of a row;
+//   * component c of that vector is the B operand of v_mfma_f32_16x16x4_f32
+//     number c, whose 16 output columns are n + 4j + c (j = 0..15): the four
+//     instructions together cover the 64 columns, and lane jj of each stores
+//     its 4 outputs of a row as 4 consecutive columns;
+//   * A (M x K, at most 16 rows) is read from L2 as 16-byte runs of one row;
+//   * two register stages of 4 k-groups of 16 each keep 2 x 4 x 4 = 32 16-byte
+//     B loads per lane in flight while the previous stage is contracted;
+//   * the 4 waves' partial tiles are summed through LDS in wave order.
+// Operand layout of v_mfma_f32_16x16x4_f32 (wave64):
+//   A: lane l holds A[i = l % 16][kk = l / 16];  B: lane l holds B[kk = l / 16][j = l % 16];
+//   D: lane l, register r holds D[4 * (l / 16) + r][l % 16].
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+namespace sgemm_impl {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGroups = 4;                 // k-groups of 16 per register stage
+constexpr int kStageK = 16 * kGroups;      // K elements per stage per wave
+
+template <bool VEC>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void skinny_gemm_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) float red[4][16][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int jj = lane & 15;
+    const int kk = lane >> 4;
+
+    const int n_w = blockIdx.x * 64;
+    const int kb = blockIdx.z * g.k_chunk;
+    const int ke = min(g.K, kb + g.k_chunk);
+    const int kq = g.k_chunk / 4;                 // a multiple of 16 (host guarantees)
+    const int wkb = min(ke, kb + wave * kq);
+    const int wke = min(ke, wkb + kq);
+
+    const bool a_row_ok = jj < g.M;
+    const float* a_row = g.A + (int64_t)(a_row_ok ? jj : 0) * g.lda;
+    const int ncol = n_w + 4 * jj;               // first of this lane's 4 columns
+
+    f32x4 ra[2][kGroups];
+    f32x4 rb[2][kGroups][4];
+
+    auto load_stage = [&](int buf, int k0) {
+#pragma unroll
+        for (int gi = 0; gi < kGroups; ++gi) {
+            const int ka = k0 + 16 * gi + 4 * kk;          // this lane's 4 k's
+            if constexpr (VEC) {
+                const bool ok = a_row_ok && ka < wke;
+                const f32x4 t = *reinterpret_cast<const f32x4*>(ok ? a_row + ka : g.A);
+                ra[buf][gi] = ok ? t : f32x4{0.f, 0.f, 0.f, 0.f};
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const bool ok = a_row_ok && ka + t < wke;
+                    const float v = *(ok ? a_row + ka + t : g.A);
+                    ra[buf][gi][t] = ok ? v : 0.f;
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int k = ka + t;
+                const float* brow = g.B + (int64_t)k * g.ldb;
+                if constexpr (VEC) {
+                    const bool ok = k < wke && ncol < g.N;
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(ok ? brow + ncol : g.B);
+                    rb[buf][gi][t] = ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const bool ok = k < wke && ncol + c < g.N;
+                        const float v = *(ok ? brow + ncol + c : g.B);
+                        rb[buf][gi][t][c] = ok ? v : 0.f;
+                    }
+                }
+            }
+        }
+    };
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute_stage = [&](int buf) {
+#pragma unroll
+        for (int gi = 0; gi < kGroups; ++gi)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[buf][gi][t], rb[buf][gi][t][c],
+                                                                  acc[c], 0, 0, 0);
+    };
+
+    const int nst = (wke - wkb + kStageK - 1) / kStageK;
+    if (nst > 0) {
+        load_stage(0, wkb);
+        int s = 0;
+        for (; s + 2 <= nst; s += 2) {
+            load_stage(1, wkb + (s + 1) * kStageK);
+            compute_stage(0);
+            if (s + 2 < nst) load_stage(0, wkb + (s + 2) * kStageK);
+            compute_stage(1);
+        }
+        if (s < nst) compute_stage(0);
+    }
+
+    // wave partials -> LDS: block c, register r is row 4kk + r, column 4jj + c
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<f32x4*>(&red[wave][4 * kk + r][4 * jj]) =
+            f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+    __syncthreads();
+
+    // sum the 4 wave partials in wave order and write rows < M, columns < N
+    const int i = tid >> 4;
+    const int c4 = (tid & 15) * 4;
+    f32x4 s4 = *reinterpret_cast<const f32x4*>(&red[0][i][c4]);
+#pragma unroll
+    for (int w = 1; w < 4; ++w) s4 += *reinterpret_cast<const f32x4*>(&red[w][i][c4]);
+    if (i < g.M) {
+        float* crow = g.C + (int64_t)blockIdx.z * g.c_slice + (int64_t)i * g.ldc;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (n_w + c4 + c < g.N) crow[n_w + c4 + c] = s4[c];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_skinny(int tile, bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
+    if (tile != 0) return hipErrorInvalidValue;
+    dim3 grid((unsigned)g.tiles_n, 1, (unsigned)splits);
+    if (vec)
+        hipLaunchKernelGGL(skinny_gemm_kernel<true>, grid, dim3(256), 0, stream, g);
+    else
+        hipLaunchKernelGGL(skinny_gemm_kernel<false>, grid, dim3(256), 0, stream, g);
+    return hipGetLastError();
+}
+
+}  // namespace sgemm_impl

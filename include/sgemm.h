@@ -1,0 +1,156 @@
+/*
+ * sgemm.h -- row-major FP32 matrix product C = A.B on one AMD Instinct
+ * MI355X (gfx950), C-ABI.
+ *
+ * Operation (the plain definition of the product, "CUDA 算子优化：GEMM",
+ * section "矩阵乘法"; notation of "GEMM from naive to tiled", section 一.2):
+ *
+ *     C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j],   0 <= i < M, 0 <= j < N
+ *
+ * with A an M x K, B a K x N and C an M x N matrix, all row-major binary32:
+ *     A[i][k] is at A[i*lda + k],  B[k][j] at B[k*ldb + j],  C[i][j] at C[i*ldc + j].
+ * Leading dimensions are passed separately from the widths (the advice of
+ * the inner/outer-product GEMM page on hotelren.com, section 4.2), so
+ * sub-matrices and padded rows work; the gap between a row's width and its
+ * leading dimension is never read or written.
+ *
+ * Arithmetic: every product and sum is IEEE binary32 with round-to-nearest-
+ * even and one rounding per fused multiply-add; there is no reduced-precision
+ * mode.  The summation order over k is the library's and may differ between
+ * kernels, tiles and split counts, but a given call (same shapes, alignment,
+ * options) always produces the same bits.  On inputs whose products and
+ * partial sums are exact in binary32 (small integers) every kernel returns
+ * the exact result.
+ *
+ * Semantics: C is overwritten (no alpha/beta).  M == 0 or N == 0 is a no-op.
+ * K == 0 writes +0.0 to every element of C (the empty sum).
+ *
+ * Memory and streams: A, B and C are device pointers owned by the caller, on
+ * the device that is current when the call is made.  The library keeps no
+ * reference to them after the call returns.  All work is enqueued on
+ * `stream` (0 = the null stream) and the call returns without waiting;
+ * the caller synchronises.  Calls on one stream run in order.  When split-K
+ * needs scratch memory, `sgemm` allocates it stream-ordered on `stream`
+ * (hipMallocAsync / hipFreeAsync); `sgemm_ex` can take a caller buffer.
+ *
+ * Errors: every argument check below runs on the host before any HIP call;
+ * on failure nothing is enqueued and C is untouched.  No exception crosses
+ * this interface.
+ */
+#ifndef DENSE_FP32_MATRIX_AMD_SGEMM_H
+#define DENSE_FP32_MATRIX_AMD_SGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sgemm_status {
+    SGEMM_OK = 0,
+    SGEMM_ERR_INVALID_ARG = 1,  /* negative size, ld too small, NULL pointer with a
+                                   nonzero extent, C overlapping A or B, bad option */
+    SGEMM_ERR_UNSUPPORTED = 2,  /* a size beyond the kernels' index range */
+    SGEMM_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed */
+    SGEMM_ERR_ALLOC = 4         /* scratch allocation failed, or the caller's
+                                   workspace is too small */
+} sgemm_status;
+
+/*
+ * C = A.B (see the file comment).
+ *   M, N, K : sizes, each >= 0 and < 2^31.
+ *   A, lda  : M x K, lda >= max(1, K).   May be NULL when M == 0 or K == 0.
+ *   B, ldb  : K x N, ldb >= max(1, N).   May be NULL when K == 0 or N == 0.
+ *   C, ldc  : M x N, ldc >= max(1, N).   May be NULL when M == 0 or N == 0.
+ * Pointers need only 4-byte alignment; 16-byte aligned rows take a faster
+ * loader.  The byte ranges of C and of A or B must not overlap.
+ */
+sgemm_status sgemm(int64_t M, int64_t N, int64_t K,
+                   const float* A, int64_t lda,
+                   const float* B, int64_t ldb,
+                   float* C, int64_t ldc,
+                   hipStream_t stream);
+
+/* Kernel families ("paths"). */
+typedef enum sgemm_path {
+    SGEMM_PATH_AUTO = 0,    /* per-shape choice */
+    SGEMM_PATH_NAIVE = 1,   /* one thread per output, operands straight from memory */
+    SGEMM_PATH_VALU = 2,    /* LDS-tiled, per-lane 8x8 outer-product update on FP32 FMA */
+    SGEMM_PATH_MFMA = 3,    /* LDS-tiled, FP32 matrix-core contraction (v_mfma_f32_32x32x2_f32) */
+    SGEMM_PATH_SKINNY = 4   /* M <= 16: streams B once, FP32 matrix cores (16x16x4) */
+} sgemm_path;
+
+/*
+ * Options for sgemm_ex.  Zero-initialised options mean "same as sgemm".
+ *   path      : an sgemm_path.
+ *   tile      : index into the path's tile table (sgemm_tile_info), or -1 to choose.
+ *   split_k   : 0 = choose, 1 = no split, S >= 2 = split K into S slices whose
+ *               partial products are summed in slice order 0..S-1 by a second kernel.
+ *   vector    : 0 = choose (16-byte loads when the operands allow them),
+ *               1 = force 4-byte loads.
+ *   workspace : device buffer of workspace_bytes for split-K partials, or NULL
+ *               to let the library allocate it stream-ordered.
+ */
+typedef struct sgemm_options {
+    int32_t path;
+    int32_t tile;
+    int32_t split_k;
+    int32_t vector;
+    void* workspace;
+    size_t workspace_bytes;
+} sgemm_options;
+
+/* sgemm with explicit options (tests and benchmarks).  opts may be NULL. */
+sgemm_status sgemm_ex(int64_t M, int64_t N, int64_t K,
+                      const float* A, int64_t lda,
+                      const float* B, int64_t ldb,
+                      float* C, int64_t ldc,
+                      hipStream_t stream, const sgemm_options* opts);
+
+/* The launch plan a call would use.  Host only: validates the arguments
+ * exactly as sgemm_ex does and fills *plan, without any HIP call. */
+typedef struct sgemm_plan {
+    int32_t path;            /* sgemm_path actually used */
+    int32_t tile;            /* tile table index */
+    int32_t split_k;         /* slices (1 = no split) */
+    int32_t vector;          /* 1 if the 16-byte loaders are used */
+    int32_t bm, bn, bk;      /* block tile */
+    int32_t threads;         /* threads per workgroup */
+    int64_t tiles_m, tiles_n;/* output tiles along M and N */
+    int64_t k_chunk;         /* K elements per slice */
+    int64_t workgroups;      /* workgroups of the main kernel */
+    size_t workspace_bytes;  /* split-K scratch (0 if none) */
+    int32_t launches;        /* kernels enqueued by the call (0, 1 or 2) */
+    int32_t reserved;
+} sgemm_plan;
+
+sgemm_status sgemm_plan_query(int64_t M, int64_t N, int64_t K,
+                              const float* A, int64_t lda,
+                              const float* B, int64_t ldb,
+                              const float* C, int64_t ldc,
+                              const sgemm_options* opts, sgemm_plan* plan);
+
+/* Scratch bytes the default plan of sgemm would need (0 when it does not
+ * split K).  Host only. */
+size_t sgemm_workspace_size(int64_t M, int64_t N, int64_t K,
+                            int64_t lda, int64_t ldb, int64_t ldc);
+
+/* Tile table of a path: returns SGEMM_OK and fills bm/bn/bk/threads for a
+ * valid (path, tile), SGEMM_ERR_INVALID_ARG otherwise.  *count receives the
+ * number of tiles of the path (any out-parameter may be NULL). */
+sgemm_status sgemm_tile_info(int32_t path, int32_t tile, int32_t* count,
+                             int32_t* bm, int32_t* bn, int32_t* bk, int32_t* threads);
+
+/* Static string naming a status code. */
+const char* sgemm_status_string(sgemm_status status);
+
+/* Library version as "major.minor.patch". */
+const char* sgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DENSE_FP32_MATRIX_AMD_SGEMM_H */

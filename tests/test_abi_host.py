@@ -1,0 +1,156 @@
+"""Host-only checks of the C interface: the library loads, exports what the
+header declares, rejects bad arguments before any HIP call, and plans
+launches as the tile arithmetic says.  No compute runs here."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+import dense_fp32_matrix_amd as lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(sgemm[a-z_0-9]*)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"sgemm", "sgemm_ex", "sgemm_plan_query", "sgemm_workspace_size", "sgemm_tile_info",
+            "sgemm_status_string", "sgemm_version"} <= set(names)
+    so = ctypes.CDLL(lib.library_path())
+    for n in names:
+        assert hasattr(so, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", lib.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(names) <= exported
+
+
+def test_header_is_valid_c(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "sgemm.h"\nint main(void){ sgemm_options o = {0}; (void)o; '
+                   'return (int)sizeof(sgemm_plan) > 0 ? 0 : 1; }\n')
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__",
+                    f"-I{os.path.join(ROOT, 'include')}", "-I/opt/rocm/include", str(src)], check=True)
+
+
+def test_status_strings_and_version():
+    assert lib.sgemm_status_string(0) == "SGEMM_OK"
+    assert lib.sgemm_status_string(1).startswith("SGEMM_ERR_INVALID_ARG")
+    assert lib.sgemm_status_string(99) == "unknown sgemm_status"
+    assert re.fullmatch(r"\d+\.\d+\.\d+", lib.sgemm_version())
+
+
+# Arguments are rejected on the host: with fake, never-dereferenced addresses
+# the calls below must return an error code without reaching the GPU.
+A, B, C = 0x10000000, 0x20000000000, 0x30000000000
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 4, 4, A, 4, B, 4, C, 4), 1),            # negative M
+    ((4, -1, 4, A, 4, B, 4, C, 4), 1),            # negative N
+    ((4, 4, -1, A, 4, B, 4, C, 4), 1),            # negative K
+    ((4, 4, 8, A, 7, B, 4, C, 4), 1),             # lda < K
+    ((4, 8, 4, A, 4, B, 7, C, 8), 1),             # ldb < N
+    ((4, 8, 4, A, 4, B, 8, C, 7), 1),             # ldc < N
+    ((4, 4, 4, 0, 4, B, 4, C, 4), 1),             # A NULL with M, K > 0
+    ((4, 4, 4, A, 4, 0, 4, C, 4), 1),             # B NULL with K, N > 0
+    ((4, 4, 4, A, 4, B, 4, 0, 4), 1),             # C NULL with M, N > 0
+    ((4, 4, 4, A + 2, 4, B, 4, C, 4), 1),         # A not 4-byte aligned
+    ((4, 4, 4, A, 4, B, 4, A + 8, 4), 1),         # C overlaps A
+    ((4, 4, 4, A, 4, B, 4, B + 60, 4), 1),        # C overlaps the end of B
+    ((1 << 30, 4, 4, A, 4, B, 4, C, 4), 2),       # beyond the kernels' index range
+])
+def test_invalid_arguments_rejected_before_hip(args, status):
+    assert lib.sgemm_raw(*args, stream=0) == status
+    assert lib.sgemm_raw(*args, stream=0, opts=lib._options()) == status
+
+
+def test_bad_options_rejected():
+    base = (64, 64, 64, A, 64, B, 64, C, 64)
+    assert lib.sgemm_raw(*base, opts=lib._options(path=7)) == 1
+    assert lib.sgemm_raw(*base, opts=lib._options(path="mfma", tile=99)) == 1
+    assert lib.sgemm_raw(*base, opts=lib._options(split_k=-2)) == 1
+    assert lib.sgemm_raw(*base, opts=lib._options(path="skinny")) == 1          # M > 16
+    assert lib.sgemm_raw(*base, opts=lib._options(path="naive", split_k=2)) == 1
+    assert lib.sgemm_raw(*base, opts=lib._options(workspace=A + 16, workspace_bytes=1 << 20)) == 1
+
+
+def test_empty_problems_plan_no_launch():
+    assert lib.sgemm_plan_query(0, 5, 7)["launches"] == 0
+    assert lib.sgemm_plan_query(5, 0, 7)["launches"] == 0
+    p = lib.sgemm_plan_query(5, 6, 0)
+    assert p["launches"] == 1 and p["workspace_bytes"] == 0      # the zero fill
+    # M == 0 or N == 0 may pass NULL pointers
+    assert lib.sgemm_raw(0, 5, 7, 0, 7, B, 5, 0, 5) == 0
+    assert lib.sgemm_raw(5, 0, 7, A, 7, 0, 1, 0, 1) == 0
+
+
+def test_tile_tables():
+    info = lib.sgemm_tile_info("mfma", 0)
+    assert info["count"] >= 5 and (info["bm"], info["bn"], info["bk"]) == (256, 128, 16)
+    for t in range(info["count"]):
+        ti = lib.sgemm_tile_info("mfma", t)
+        assert ti["bm"] % 32 == 0 and ti["bn"] % 32 == 0 and ti["bk"] % 8 == 0
+    assert lib.sgemm_tile_info("valu", 0)["bk"] == 8
+    assert lib.sgemm_tile_info("mfma", 99) is None
+    assert lib.sgemm_tile_info("naive", 0)["threads"] == 256
+
+
+def test_boundary_worked_example():
+    """The page's edge-handling example: M=300, N=200, K=20 with 128 x 128
+    tiles and BK = 8 gives a 3 x 2 grid and 3 K-steps, i.e. the product padded
+    to 384 x 256 x 24 ("GEMM from naive to tiled", section 七)."""
+    g = json.load(open(os.path.join(GOLDEN, "boundary_example.json")))
+    p = lib.sgemm_plan_query(g["M"], g["N"], g["K"], path="valu", tile=0, split_k=1)
+    assert (p["bm"], p["bn"], p["bk"]) == (g["BM"], g["BN"], g["BK"])
+    assert (p["tiles_m"], p["tiles_n"]) == tuple(g["grid"])
+    k_steps = -(-p["k_chunk"] // p["bk"])
+    assert k_steps == g["k_steps"]
+    assert [p["tiles_m"] * p["bm"], p["tiles_n"] * p["bn"], k_steps * p["bk"]] == g["padded"]
+
+
+def test_vector_loader_selection():
+    # 16-byte aligned, ld and widths multiples of 4 -> 16-byte loaders
+    assert lib.sgemm_plan_query(512, 512, 512)["vector"] == 1
+    # odd leading dimensions (the ragged workload) -> 4-byte loaders
+    assert lib.sgemm_plan_query(4097, 3001, 2049, lda=2049, ldb=3001, ldc=3001)["vector"] == 0
+    # a base pointer offset by one float
+    assert lib.sgemm_plan_query(512, 512, 512, A=0x100004)["vector"] == 0
+    # forced off
+    assert lib.sgemm_plan_query(512, 512, 512, vector=1)["vector"] == 0
+
+
+def test_default_plans_fill_the_chip():
+    """Every benchmark shape gets at least one workgroup per CU (256), with
+    split-K where the output alone has too few tiles."""
+    shapes = [(4096, 4096, 4096), (4097, 3001, 2049), (8192, 11008, 4096), (16, 11008, 4096),
+              (512, 512, 65536)]
+    for M, N, K in shapes:
+        p = lib.sgemm_plan_query(M, N, K, lda=K, ldb=N, ldc=N)
+        assert p["workgroups"] >= 256, (M, N, K, p)
+        assert p["k_chunk"] * p["split_k"] >= K
+        assert p["k_chunk"] * (p["split_k"] - 1) < K
+        if p["split_k"] > 1:
+            assert p["workspace_bytes"] >= p["split_k"] * M * N * 4
+            assert p["launches"] == 2
+            assert lib.sgemm_workspace_size(M, N, K) == p["workspace_bytes"]
+    assert lib.sgemm_plan_query(16, 11008, 4096)["path_name"] == "skinny"
+    assert lib.sgemm_plan_query(512, 512, 65536)["split_k"] > 1
+
+
+def test_forced_split_k_slices_cover_k():
+    for S in (1, 2, 3, 7, 16):
+        p = lib.sgemm_plan_query(300, 200, 1000, path="mfma", tile=2, split_k=S)
+        assert p["k_chunk"] % p["bk"] == 0
+        assert p["split_k"] <= S
+        assert (p["split_k"] - 1) * p["k_chunk"] < 1000 <= p["split_k"] * p["k_chunk"]

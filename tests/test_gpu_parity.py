@@ -1,0 +1,298 @@
+"""GPU parity: the HIP kernels, called through the C interface, against the
+host oracle on the same seeded inputs.
+
+Bar (tests/checks.py): |C - C_ref| <= 1e-5 * sum_k |A_ik||B_kj| elementwise
+for floating-point inputs; bit-exact on small-integer inputs, where every
+partial sum is exact in FP32 whatever the order.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_fp32_matrix_amd as lib
+import workloads
+from checks import assert_bit_exact, assert_within_bound
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def inputs(M, N, K, kind, seed, lda=None, ldb=None):
+    A = workloads.with_ld(workloads.draw(M, K, kind, seed), lda or K)
+    B = workloads.with_ld(workloads.draw(K, N, kind, seed + 1), ldb or N)
+    return A, B
+
+
+def to_dev(x):
+    """Device copy keeping the row stride (padding included)."""
+    if x.dim() == 2 and x.shape[0] > 0 and x.stride(0) != x.shape[1]:
+        base = torch.empty((x.shape[0], x.stride(0)), dtype=torch.float32)
+        base.fill_(float("nan"))
+        base[:, :x.shape[1]] = x
+        return base.to(DEV)[:, :x.shape[1]]
+    return x.contiguous().to(DEV)
+
+
+def run(A, B, ldc=None, **opts):
+    Ad, Bd = to_dev(A), to_dev(B)
+    M, N = A.shape[0], B.shape[1]
+    if ldc is None:
+        C = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    else:
+        C = torch.full((M, ldc), float("nan"), dtype=torch.float32, device=DEV)[:, :N]
+    if opts:
+        lib.sgemm_ex(Ad, Bd, C, **opts)
+    else:
+        lib.sgemm(Ad, Bd, C)
+    torch.cuda.synchronize()
+    return C
+
+
+def check_case(oracle_mod, M, N, K, what, lda=None, ldb=None, **opts):
+    say(f"{what} M={M} N={N} K={K} opts={opts}")
+    # floating-point inputs: normalized bound
+    A, B = inputs(M, N, K, "uniform", 100 + M + 7 * N + 13 * K, lda, ldb)
+    C = run(A, B, **opts).cpu().numpy()
+    Cref, D = oracle_mod.sgemm(A.numpy(), B.numpy(), with_denominator=True)
+    assert_within_bound(C, Cref, D, what=what)
+    # integer inputs: bit-exact
+    Ai, Bi = inputs(M, N, K, "integer", 200 + M + 7 * N + 13 * K, lda, ldb)
+    Ci = run(Ai, Bi, **opts).cpu().numpy()
+    assert_bit_exact(Ci, oracle_mod.round_to_f32(oracle_mod.sgemm(Ai.numpy(), Bi.numpy())), what=what + " int")
+
+
+# --- every path and tile on shapes that span several tiles with ragged tails ---------
+
+SMALL_SHAPES = [
+    (256, 256, 256),      # the 256^3 workload
+    (300, 200, 20),       # the edge-handling example of the pages
+    (1, 1, 1),
+    (1, 65, 3),
+    (33, 47, 65),
+    (513, 385, 272),
+    (130, 260, 100),
+]
+
+
+def _mfma_tiles():
+    n = lib.sgemm_tile_info("mfma", 0)["count"]
+    return list(range(n))
+
+
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_naive(oracle_mod, shape):
+    check_case(oracle_mod, *shape, "naive", path="naive")
+
+
+@pytest.mark.parametrize("tile", _mfma_tiles())
+@pytest.mark.parametrize("vector", [0, 1])
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_mfma_tiles(oracle_mod, shape, tile, vector):
+    check_case(oracle_mod, *shape, f"mfma/{tile}/v{vector}", path="mfma", tile=tile, vector=vector, split_k=1)
+
+
+@pytest.mark.parametrize("tile", [0, 1])
+@pytest.mark.parametrize("vector", [0, 1])
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_valu_tiles(oracle_mod, shape, tile, vector):
+    check_case(oracle_mod, *shape, f"valu/{tile}/v{vector}", path="valu", tile=tile, vector=vector, split_k=1)
+
+
+@pytest.mark.parametrize("vector", [0, 1])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (16, 64, 64), (5, 300, 1000), (16, 1000, 4100), (9, 11008, 512),
+                                   (16, 7, 3)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("split_k", [1, 3])
+def test_skinny(oracle_mod, shape, vector, split_k):
+    check_case(oracle_mod, *shape, f"skinny/v{vector}/s{split_k}", path="skinny", vector=vector, split_k=split_k)
+
+
+@pytest.mark.parametrize("path,tile", [("mfma", 0), ("mfma", 2), ("mfma", 4), ("valu", 0)])
+@pytest.mark.parametrize("split_k", [2, 5, 16])
+def test_split_k(oracle_mod, path, tile, split_k):
+    check_case(oracle_mod, 200, 136, 2000, f"{path}/{tile}/split{split_k}", path=path, tile=tile,
+               split_k=split_k)
+
+
+@pytest.mark.parametrize("shape", SMALL_SHAPES + [(64, 64, 8192), (20, 11008, 4096)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_default_plan(oracle_mod, shape):
+    check_case(oracle_mod, *shape, "auto")
+
+
+# --- layouts: leading dimensions with NaN padding, misaligned bases -------------------------
+
+@pytest.mark.parametrize("path", ["naive", "valu", "mfma", "skinny"])
+def test_padded_leading_dimensions(oracle_mod, path):
+    M = 16 if path == "skinny" else 150
+    N, K = 170, 90
+    lda, ldb, ldc = K + 3, N + 5, N + 7
+    say(f"padded ld path={path}")
+    A, B = inputs(M, N, K, "integer", 7, lda, ldb)
+    C = run(A, B, ldc=ldc, path=path)
+    Cbuf = C.cpu()  # the (M, N) view
+    full = torch.as_strided(C, (M, ldc), (ldc, 1)).cpu().numpy()
+    assert np.all(np.isnan(full[:, N:])), "wrote into the ldc gap"
+    ref = oracle_mod.round_to_f32(oracle_mod.sgemm(A.numpy(), B.numpy()))
+    assert_bit_exact(Cbuf.numpy(), ref, what=f"{path} padded")
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma", "skinny"])
+def test_misaligned_base_pointers(oracle_mod, path):
+    """Views starting one float into their buffers: 4-byte aligned only."""
+    M = 12 if path == "skinny" else 97
+    N, K = 132, 76
+    say(f"misaligned path={path}")
+    A, B = inputs(M, N, K, "integer", 9)
+    Abuf = torch.zeros((M * K + 1,), dtype=torch.float32, device=DEV)
+    Bbuf = torch.zeros((K * N + 1,), dtype=torch.float32, device=DEV)
+    Cbuf = torch.full((M * N + 2,), float("nan"), dtype=torch.float32, device=DEV)
+    Ad = Abuf[1:].view(M, K)
+    Bd = Bbuf[1:].view(K, N)
+    Cd = Cbuf[1:M * N + 1].view(M, N)
+    Ad.copy_(A.to(DEV))
+    Bd.copy_(B.to(DEV))
+    plan = lib.sgemm_plan_query(M, N, K, Ad.data_ptr(), K, Bd.data_ptr(), N, Cd.data_ptr(), N, path=path)
+    assert plan["vector"] == 0
+    lib.sgemm_ex(Ad, Bd, Cd, path=path)
+    torch.cuda.synchronize()
+    c = Cbuf.cpu().numpy()
+    assert np.isnan(c[0]) and np.isnan(c[-1]), "wrote outside C"
+    ref = oracle_mod.round_to_f32(oracle_mod.sgemm(A.numpy(), B.numpy()))
+    assert_bit_exact(c[1:M * N + 1].reshape(M, N), ref, what=f"{path} misaligned")
+
+
+# --- degenerate sizes ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["auto", "naive", "valu", "mfma"])
+def test_k_zero_writes_zeros(path):
+    say(f"K=0 path={path}")
+    A = torch.empty((5, 0), device=DEV)
+    B = torch.empty((0, 7), device=DEV)
+    C = torch.full((5, 7), float("nan"), device=DEV)
+    lib.sgemm_ex(A, B, C, path=path)
+    torch.cuda.synchronize()
+    c = C.cpu().numpy()
+    assert np.all(c == 0) and not np.any(np.signbit(c))
+
+
+def test_empty_m_or_n_is_noop():
+    say("M=0 / N=0")
+    C = torch.full((0, 7), 1.0, device=DEV)
+    lib.sgemm(torch.empty((0, 3), device=DEV), torch.ones((3, 7), device=DEV), C)
+    C2 = torch.full((4, 0), 1.0, device=DEV)
+    lib.sgemm(torch.ones((4, 3), device=DEV), torch.empty((3, 0), device=DEV), C2)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("path", ["naive", "valu", "mfma", "skinny"])
+def test_k_one_single_rounding(oracle_mod, path):
+    """K = 1: each output is one rounded product, equal to the binary32 product."""
+    M = 16 if path == "skinny" else 77
+    say(f"K=1 path={path}")
+    A, B = inputs(M, 91, 1, "uniform", 11)
+    C = run(A, B, path=path).cpu().numpy()
+    ref = oracle_mod.round_to_f32(oracle_mod.sgemm(A.numpy(), B.numpy()))
+    assert_bit_exact(C, ref, what=f"{path} K=1")
+    assert_bit_exact(C, A.numpy() * B.numpy(), what=f"{path} K=1 vs fp32 product")
+
+
+def test_zero_row_and_column_exact(oracle_mod):
+    """Where D = 0 (a zero row of A or zero column of B) C must be exactly 0."""
+    say("zero row/column")
+    A, B = inputs(130, 140, 150, "uniform", 12)
+    A[5] = 0
+    B[:, 17] = 0
+    C = run(A, B).cpu().numpy()
+    assert np.all(C[5] == 0) and np.all(C[:, 17] == 0)
+
+
+@pytest.mark.parametrize("opts", [{}, {"path": "mfma", "tile": 2, "split_k": 4}, {"path": "skinny"}],
+                         ids=["auto", "split4", "skinny"])
+def test_run_to_run_determinism(opts):
+    say(f"determinism {opts}")
+    M = 16 if opts.get("path") == "skinny" else 300
+    A, B = inputs(M, 500, 3000, "uniform", 13)
+    C1 = run(A, B, **opts).cpu()
+    C2 = run(A, B, **opts).cpu()
+    assert torch.equal(C1.view(torch.int32), C2.view(torch.int32))
+
+
+def test_caller_workspace_and_stream(oracle_mod):
+    say("caller workspace + side stream")
+    M, N, K = 200, 136, 2000
+    A, B = inputs(M, N, K, "integer", 14)
+    need = lib.sgemm_plan_query(M, N, K, path="mfma", tile=2, split_k=4)["workspace_bytes"]
+    ws = torch.empty(need // 4 + 64, dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    Ad, Bd = to_dev(A), to_dev(B)
+    C = torch.empty((M, N), device=DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        lib.sgemm_ex(Ad, Bd, C, stream=s, path="mfma", tile=2, split_k=4, workspace=ws)
+    s.synchronize()
+    ref = oracle_mod.round_to_f32(oracle_mod.sgemm(A.numpy(), B.numpy()))
+    assert_bit_exact(C.cpu().numpy(), ref, what="caller workspace")
+    small = torch.empty(16, dtype=torch.float32, device=DEV)
+    with pytest.raises(lib.SgemmError):
+        lib.sgemm_ex(Ad, Bd, C, path="mfma", tile=2, split_k=4, workspace=small)
+
+
+# --- the benchmark workloads at full size, in the benchmark's launch configuration ---------
+
+def _full_size_check(oracle_mod, w, kind):
+    say(f"full size {w.name} inputs={kind}")
+    A = workloads.with_ld(workloads.draw(w.M, w.K, kind, w.seed_base + 0, w.a_std if kind != "integer" else 1.0),
+                          w.lda)
+    B = workloads.with_ld(workloads.draw(w.K, w.N, kind, w.seed_base + 1, w.b_std if kind != "integer" else 1.0),
+                          w.ldb)
+    Ad, Bd = to_dev(A), to_dev(B)
+    C = torch.full((w.M, w.N), float("nan"), dtype=torch.float32, device=DEV)
+    lib.sgemm(Ad, Bd, C)                 # the default plan, as the benchmark runs it
+    torch.cuda.synchronize()
+    del Ad, Bd
+    Ch = C.cpu().numpy()
+    del C
+    assert np.all(np.isfinite(Ch))
+    An, Bn = A.numpy(), B.numpy()
+    rows, cols = workloads.sample_indices(w.M, w.N, 2048, seed=w.seed_base + 7)
+    cref, dref = oracle_mod.sgemm_entries(An, Bn, rows, cols)
+    got = Ch[rows, cols]
+    if kind == "integer":
+        assert np.array_equal(got.astype(np.float64), cref), "sampled entries differ"
+    else:
+        err = np.abs(got.astype(np.float64) - cref) / np.where(dref == 0, 1, dref)
+        assert err.max() <= 1e-5, f"sampled normalized error {err.max():.3e}"
+    # (AB)x = A(Bx) over the whole output, for two vectors x
+    g = np.random.default_rng(w.seed_base + 9)
+    for t in range(2):
+        if kind == "integer":
+            x = g.integers(-4, 5, size=w.N).astype(np.float64)
+        else:
+            x = g.uniform(-1, 1, size=w.N)
+        cx = np.empty(w.M)
+        for r0 in range(0, w.M, 512):
+            cx[r0:r0 + 512] = Ch[r0:r0 + 512].astype(np.float64) @ x
+        abx = oracle_mod.gemv(An, oracle_mod.gemv(Bn, x))
+        if kind == "integer":
+            assert np.array_equal(cx, abx), "(AB)x != A(Bx) on integer inputs"
+        else:
+            scale = oracle_mod.gemv(An, oracle_mod.gemv(Bn, np.abs(x), absolute=True), absolute=True)
+            r = np.abs(cx - abx) / scale
+            assert r.max() <= 1e-5 + 1e-12, f"(AB)x vs A(Bx): {r.max():.3e}"
+
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_full_size_workload(oracle_mod, name):
+    w = workloads.CONFIGS[name]
+    _full_size_check(oracle_mod, w, w.a_kind)
+
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_full_size_workload_integer(oracle_mod, name):
+    w = workloads.CONFIGS[name]
+    _full_size_check(oracle_mod, w, "integer")
