@@ -286,6 +286,9 @@ sgemm_status run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, c
     g.ldb = ldb;
     g.tiles_m = (int32_t)q.tiles_m;
     g.tiles_n = (int32_t)q.tiles_n;
+    // 8 tile rows per raster group: the 64 workgroups one XCD holds at a time
+    // (32 CUs x 2) then cover about an 8 x 8 block of tiles
+    g.group_m = (int32_t)std::min<int64_t>(q.tiles_m, 8);
     if (q.split_k > 1) {
         g.C = static_cast<float*>(ws);
         g.ldc = p.ldw;

@@ -20,7 +20,30 @@ struct GemmArgs {
     int64_t lda, ldb, ldc;
     int64_t c_slice;    // elements between consecutive slices' outputs
     int32_t tiles_m, tiles_n;
+    int32_t group_m;    // tile rows per raster group (tile-order swizzle), >= 1
 };
+
+// Workgroup -> output tile.  Consecutive workgroup ids are dispatched
+// round-robin over the chip's 8 XCDs (each with its own L2), so id b is first
+// renumbered so that every XCD receives one contiguous range of logical
+// tiles; logical tiles are then walked in groups of group_m tile rows,
+// column by column, so the tiles one XCD holds at a time share rows of A
+// and columns of B.
+__host__ __device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int group_m, int* tm, int* tn) {
+    const int total = tiles_m * tiles_n;
+    const int xcd = bid % 8;
+    const int local = bid / 8;
+    const int per = total / 8;
+    const int rem = total % 8;
+    const int t = xcd * per + (xcd < rem ? xcd : rem) + local;
+    const int span = group_m * tiles_n;
+    const int group = t / span;
+    const int first_m = group * group_m;
+    const int gm = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
+    const int within = t - group * span;
+    *tm = first_m + within % gm;
+    *tn = within / gm;
+}
 
 // Tile shapes of each path.  The kernels are instantiated for exactly these;
 // the dispatcher and sgemm_tile_info read the same table.
@@ -66,5 +89,12 @@ hipError_t launch_splitk_reduce(const float* W, int64_t ldw, int64_t w_slice, in
 
 // C[i][j] = +0.0 for i < M, j < N (the empty sum, K == 0).
 hipError_t launch_fill_zero(float* C, int64_t ldc, int32_t M, int32_t N, hipStream_t stream);
+
+// Sixteen zero bytes in device memory, defined once per kernel source.  A
+// masked-off load (outside the matrix, or past the end of a K slice) reads
+// from here instead of being followed by a select, so no instruction waits on
+// the load until its data is consumed.  The block is externally visible and
+// never written, so the compiler cannot fold the loads into selects.
+#define SGEMM_DEFINE_ZERO_BLOCK(name) __device__ __attribute__((aligned(16))) float name[4] = {0.f, 0.f, 0.f, 0.f}
 
 }  // namespace sgemm_impl

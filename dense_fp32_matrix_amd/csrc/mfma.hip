@@ -36,6 +36,9 @@
 #include "kernels.hpp"
 
 namespace sgemm_impl {
+
+SGEMM_DEFINE_ZERO_BLOCK(kZeroMfma);
+
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -81,9 +84,8 @@ void mfma_gemm_kernel(GemmArgs g) {
     const int wm = wave / WGN;
     const int wn = wave % WGN;
 
-    const int bid = blockIdx.x;
-    const int tm = bid % g.tiles_m;
-    const int tn = bid / g.tiles_m;
+    int tm, tn;
+    tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
     const int m0 = tm * BM;
     const int n0 = tn * BN;
 
@@ -135,30 +137,22 @@ void mfma_gemm_kernel(GemmArgs g) {
     f32x4 va[VEC ? AN : 1], vb[VEC ? BNL : 1];
     float sa[VEC ? 1 : AN], sb[VEC ? 1 : BNL];
 
+    // Masked-off elements load from kZeroMfma, so the loaded registers are
+    // final and nothing waits on them before they are written to LDS.
     auto load = [&](int k0) {
 #pragma unroll
         for (int r = 0; r < AN; ++r) {
             const bool ok = a_rok[r] && (k0 + a_kc[r] < ke);
-            const float* p = ok ? g.A + a_off[r] + k0 : g.A;
-            if constexpr (VEC) {
-                const f32x4 t = *reinterpret_cast<const f32x4*>(p);
-                va[r] = ok ? t : f32x4{0.f, 0.f, 0.f, 0.f};
-            } else {
-                const float t = *p;
-                sa[r] = ok ? t : 0.f;
-            }
+            const float* p = ok ? g.A + a_off[r] + k0 : kZeroMfma;
+            if constexpr (VEC) va[r] = *reinterpret_cast<const f32x4*>(p);
+            else sa[r] = *p;
         }
 #pragma unroll
         for (int r = 0; r < BNL; ++r) {
             const bool ok = b_cok[r] && (k0 + b_kr[r] < ke);
-            const float* p = ok ? g.B + b_off[r] + (int64_t)k0 * g.ldb : g.B;
-            if constexpr (VEC) {
-                const f32x4 t = *reinterpret_cast<const f32x4*>(p);
-                vb[r] = ok ? t : f32x4{0.f, 0.f, 0.f, 0.f};
-            } else {
-                const float t = *p;
-                sb[r] = ok ? t : 0.f;
-            }
+            const float* p = ok ? g.B + b_off[r] + (int64_t)k0 * g.ldb : kZeroMfma;
+            if constexpr (VEC) vb[r] = *reinterpret_cast<const f32x4*>(p);
+            else sb[r] = *p;
         }
     };
     auto store = [&](int buf) {

@@ -5,6 +5,7 @@
 #include "kernels.hpp"
 
 namespace sgemm_impl {
+
 namespace {
 
 // One thread per C element, operands read straight from global memory

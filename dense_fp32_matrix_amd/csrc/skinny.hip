@@ -16,6 +16,8 @@
 //     instructions together cover the 64 columns, and lane jj of each stores
 //     its 4 outputs of a row as 4 consecutive columns;
 //   * A (M x K, at most 16 rows) is read from L2 as 16-byte runs of one row;
+//   * masked-off elements (rows >= M, columns >= N, k past the slice) load
+//     from a 16-byte zero block, so loads are never followed by a select;
 //   * two register stages of 4 k-groups of 16 each keep 2 x 4 x 4 = 32 16-byte
 //     B loads per lane in flight while the previous stage is contracted;
 //   * the 4 waves' partial tiles are summed through LDS in wave order.
@@ -27,6 +29,9 @@
 #include "kernels.hpp"
 
 namespace sgemm_impl {
+
+SGEMM_DEFINE_ZERO_BLOCK(kZeroSkinny);
+
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -65,14 +70,12 @@ void skinny_gemm_kernel(GemmArgs g) {
             const int ka = k0 + 16 * gi + 4 * kk;          // this lane's 4 k's
             if constexpr (VEC) {
                 const bool ok = a_row_ok && ka < wke;
-                const f32x4 t = *reinterpret_cast<const f32x4*>(ok ? a_row + ka : g.A);
-                ra[buf][gi] = ok ? t : f32x4{0.f, 0.f, 0.f, 0.f};
+                ra[buf][gi] = *reinterpret_cast<const f32x4*>(ok ? a_row + ka : kZeroSkinny);
             } else {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const bool ok = a_row_ok && ka + t < wke;
-                    const float v = *(ok ? a_row + ka + t : g.A);
-                    ra[buf][gi][t] = ok ? v : 0.f;
+                    ra[buf][gi][t] = *(ok ? a_row + ka + t : kZeroSkinny);
                 }
             }
 #pragma unroll
@@ -81,14 +84,12 @@ void skinny_gemm_kernel(GemmArgs g) {
                 const float* brow = g.B + (int64_t)k * g.ldb;
                 if constexpr (VEC) {
                     const bool ok = k < wke && ncol < g.N;
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(ok ? brow + ncol : g.B);
-                    rb[buf][gi][t] = ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+                    rb[buf][gi][t] = *reinterpret_cast<const f32x4*>(ok ? brow + ncol : kZeroSkinny);
                 } else {
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         const bool ok = k < wke && ncol + c < g.N;
-                        const float v = *(ok ? brow + ncol + c : g.B);
-                        rb[buf][gi][t][c] = ok ? v : 0.f;
+                        rb[buf][gi][t][c] = *(ok ? brow + ncol + c : kZeroSkinny);
                     }
                 }
             }
