@@ -26,11 +26,24 @@
 // read from LDS with a single 16-byte read.
 //
 // LDS layout, per stage:
-//   As[BM][BK + 4]  (row-major like A; the +4 floats make the row stride an
-//                    odd multiple of 16 bytes, so the 16-byte fragment reads
-//                    of consecutive rows fall in distinct bank groups)
-//   Bs[BK][BN + 8]  (row-major like B; the two lane halves read rows 4 apart,
-//                    offset by 4 * (BN + 8) = 32 (mod 64) banks)
+//   As[BM][BK]      row-major like A, no padding; the 16-byte chunk c of row
+//                   r is stored at chunk position c ^ swz(r).  The XOR
+//                   swizzle (one of the three bank-conflict fixes of "SGEMM
+//                   纯 CUDA 优化总结", Q7) is chosen so that both the 16-byte
+//                   fragment reads (32 rows, one chunk each) and the 16-byte
+//                   tile writes (BK/4 lanes per row) hit distinct banks, for
+//                   32 or 64 four-byte banks.
+//   Bs[BK][BN + 8]  row-major like B; the two lane halves read rows 4 apart,
+//                   offset by 4 * (BN + 8) = 32 (mod 64) banks.
+//
+// Schedule of one K-step t (stages alternate between two LDS buffers):
+//   issue the global loads of step t+1;
+//   for each k-group but the last: read the next group's fragments from
+//     LDS, then issue this group's MFMAs;
+//   write step t+1's registers to the other buffer; barrier;
+//   read the first fragments of step t+1, then issue the last group's MFMAs
+//     of step t, whose registers were read before the barrier -- so the LDS
+//     latency after the barrier is covered by matrix-core work.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -51,8 +64,9 @@ struct MfmaCfg {
     static constexpr int WN = BN / WGN;
     static constexpr int MB = WM / 32;
     static constexpr int NB = WN / 32;
-    static constexpr int LDA_S = BK + 4;
+    static constexpr int LDA_S = BK;
     static constexpr int LDB_S = BN + 8;
+    static constexpr int KG = BK / 8;           // k-groups of 8 per K-step
     static constexpr int A_STAGE = BM * LDA_S;
     static constexpr int B_STAGE = BK * LDB_S;
     static constexpr int STAGE = A_STAGE + B_STAGE;
@@ -63,13 +77,20 @@ struct MfmaCfg {
     static constexpr int A_V = A_PER / 4;
     static constexpr int B_V = B_PER / 4;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+    static_assert(BK == 16 || BK == 32, "A-tile swizzle is defined for BK = 16 and 32");
     static_assert(A_PER * T == BM * BK && B_PER * T == BK * BN, "loader must cover the tile");
     static_assert(!VEC || (A_V * 4 == A_PER && B_V * 4 == B_PER), "vector loader must cover the tile");
     static_assert(T % (BK / 4) == 0 && T % (BN / 4) == 0, "vector loader rows");
     static_assert(T % BK == 0 && T % BN == 0, "scalar loader rows");
     static_assert(2 * STAGE * 4 <= 160 * 1024, "LDS budget");
 };
+
+// Chunk-position swizzle of A-tile row r (BK/4 chunks of 16 bytes per row).
+template <int BK>
+__device__ __forceinline__ int a_swizzle(int r) {
+    if constexpr (BK == 16) return ((r >> 1) ^ (r >> 3)) & 3;
+    else return (r ^ (r >> 3)) & 7;
+}
 
 template <int BM, int BN, int BK, int WGM, int WGN, bool VEC, int WPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
@@ -116,7 +137,7 @@ void mfma_gemm_kernel(GemmArgs g) {
         a_rok[r] = gm < g.M;
         a_off[r] = (int64_t)(a_rok[r] ? gm : 0) * g.lda + col;
         a_kc[r] = col;
-        a_lds[r] = row * P::LDA_S + col;
+        a_lds[r] = row * P::LDA_S + 4 * ((col >> 2) ^ a_swizzle<BK>(row)) + (col & 3);
     }
     int64_t b_off[BNL];
     int b_kr[BNL];         // row within the K-step
@@ -179,45 +200,62 @@ void mfma_gemm_kernel(GemmArgs g) {
 
     const int l32 = lane & 31;
     const int lh = lane >> 5;
-    // fragment offsets within a stage (floats)
-    const int a_frag = (wm * P::WM + l32) * P::LDA_S + 4 * lh;
+    // fragment offsets within a stage (floats).  A: row wm*WM + mb*32 + l32,
+    // logical chunk 2*kg + lh, stored at chunk (2*kg + lh) ^ swz(row).
+    int a_frag[P::KG][P::MB];
+#pragma unroll
+    for (int mb = 0; mb < P::MB; ++mb) {
+        const int row = wm * P::WM + mb * 32 + l32;
+        const int sw = a_swizzle<BK>(row);
+#pragma unroll
+        for (int kg = 0; kg < P::KG; ++kg) a_frag[kg][mb] = row * P::LDA_S + 4 * ((2 * kg + lh) ^ sw);
+    }
     const int b_frag = P::A_STAGE + (4 * lh) * P::LDB_S + wn * P::WN + l32;
 
-    auto compute = [&](int buf) {
+    // two fragment sets: group kg's operands live in set kg & 1
+    f32x4 fa[2][P::MB];
+    float fb[2][P::NB][4];
+    auto read_frags = [&](int buf, int kg, int set) {
         const float* s = smem + buf * P::STAGE;
 #pragma unroll
-        for (int kg = 0; kg < BK / 8; ++kg) {
-            f32x4 a[P::MB];
-            float b[P::NB][4];
+        for (int mb = 0; mb < P::MB; ++mb)
+            fa[set][mb] = *reinterpret_cast<const f32x4*>(s + a_frag[kg][mb]);
+#pragma unroll
+        for (int nb = 0; nb < P::NB; ++nb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) fb[set][nb][q] = s[b_frag + (8 * kg + q) * P::LDB_S + nb * 32];
+    };
+    auto mfmas = [&](int set) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int mb = 0; mb < P::MB; ++mb)
-                a[mb] = *reinterpret_cast<const f32x4*>(s + a_frag + mb * 32 * P::LDA_S + 8 * kg);
 #pragma unroll
-            for (int nb = 0; nb < P::NB; ++nb)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    b[nb][q] = s[b_frag + (8 * kg + q) * P::LDB_S + nb * 32];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int mb = 0; mb < P::MB; ++mb)
-#pragma unroll
-                    for (int nb = 0; nb < P::NB; ++nb)
-                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mb][q], b[nb][q],
-                                                                           acc[mb][nb], 0, 0, 0);
-        }
+                for (int nb = 0; nb < P::NB; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[set][mb][q], fb[set][nb][q],
+                                                                       acc[mb][nb], 0, 0, 0);
     };
 
     if (steps > 0) {
         load(kb);
         store(0);
         __syncthreads();
+        read_frags(0, 0, 0);
         for (int s = 0; s < steps; ++s) {
+            const int cur = s & 1;
             const bool more = s + 1 < steps;
             if (more) load(kb + (s + 1) * BK);
-            compute(s & 1);
-            if (more) store((s & 1) ^ 1);
+#pragma unroll
+            for (int kg = 0; kg + 1 < P::KG; ++kg) {
+                read_frags(cur, kg + 1, (kg + 1) & 1);
+                mfmas(kg & 1);
+            }
+            if (more) store(cur ^ 1);
             __syncthreads();
+            // KG is even, so the next step's first group goes to set 0 while
+            // this step's last group (set 1) is contracted
+            if (more) read_frags(cur ^ 1, 0, 0);
+            mfmas((P::KG - 1) & 1);
         }
     }
 
