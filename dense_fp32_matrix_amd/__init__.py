@@ -13,7 +13,7 @@ import os
 from typing import Optional
 
 __all__ = [
-    "SgemmError", "PATHS", "sgemm", "sgemm_ex", "sgemm_raw", "sgemm_plan_query", "sgemm_workspace_size",
+    "SgemmError", "PATHS", "DECOMPOSITIONS", "sgemm", "sgemm_ex", "sgemm_raw", "sgemm_plan_query", "sgemm_workspace_size",
     "sgemm_tile_info", "sgemm_status_string", "sgemm_version", "library_path", "load_library",
 ]
 
@@ -35,9 +35,14 @@ class SgemmError(RuntimeError):
         super().__init__(f"{what}: {sgemm_status_string(status)}" if what else sgemm_status_string(status))
 
 
+DECOMPOSITIONS = {"auto": 0, "tiles": 1, "stream_k": 2}
+_DECOMP_NAMES = {v: k for k, v in DECOMPOSITIONS.items()}
+
+
 class _Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("tile", ctypes.c_int32), ("split_k", ctypes.c_int32),
-                ("vector", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("vector", ctypes.c_int32), ("decomposition", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class _Plan(ctypes.Structure):
@@ -46,7 +51,8 @@ class _Plan(ctypes.Structure):
                 ("bk", ctypes.c_int32), ("threads", ctypes.c_int32), ("tiles_m", ctypes.c_int64),
                 ("tiles_n", ctypes.c_int64), ("k_chunk", ctypes.c_int64), ("workgroups", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_size_t), ("launches", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("decomposition", ctypes.c_int32), ("dp_tiles", ctypes.c_int64), ("sk_tiles", ctypes.c_int64),
+                ("sk_units_per_wg", ctypes.c_int64)]
 
 
 def library_path() -> str:
@@ -82,12 +88,14 @@ def load_library():
     return lib
 
 
-def _options(path="auto", tile=-1, split_k=0, vector=0, workspace=None, workspace_bytes=0) -> _Options:
+def _options(path="auto", tile=-1, split_k=0, vector=0, decomposition="auto", workspace=None,
+             workspace_bytes=0) -> _Options:
     o = _Options()
     o.path = PATHS[path] if isinstance(path, str) else int(path)
     o.tile = int(tile)
     o.split_k = int(split_k)
     o.vector = int(vector)
+    o.decomposition = DECOMPOSITIONS[decomposition] if isinstance(decomposition, str) else int(decomposition)
     if workspace is not None and not isinstance(workspace, int):
         workspace_bytes = workspace.numel() * workspace.element_size()
         workspace = workspace.data_ptr()
@@ -155,10 +163,12 @@ def sgemm(A, B, C=None, stream=None):
     return _call(A, B, C, stream, None)
 
 
-def sgemm_ex(A, B, C=None, stream=None, *, path="auto", tile=-1, split_k=0, vector=0, workspace=None):
+def sgemm_ex(A, B, C=None, stream=None, *, path="auto", tile=-1, split_k=0, vector=0, decomposition="auto",
+             workspace=None):
     """``sgemm`` with explicit options: ``path`` in PATHS, ``tile`` index, ``split_k``
-    slices, ``vector=1`` to force 4-byte loads, optional ``workspace`` tensor."""
-    return _call(A, B, C, stream, _options(path, tile, split_k, vector, workspace))
+    slices, ``vector=1`` to force 4-byte loads, ``decomposition`` in DECOMPOSITIONS,
+    optional ``workspace`` tensor."""
+    return _call(A, B, C, stream, _options(path, tile, split_k, vector, decomposition, workspace))
 
 
 def sgemm_plan_query(M, N, K, A=0x100000, lda=None, B=0x200000000, ldb=None, C=0x400000000, ldc=None,
@@ -174,8 +184,9 @@ def sgemm_plan_query(M, N, K, A=0x100000, lda=None, B=0x200000000, ldb=None, C=0
     st = lib.sgemm_plan_query(M, N, K, A, lda, B, ldb, C, ldc, ctypes.byref(o), ctypes.byref(pl))
     if st != SGEMM_OK:
         raise SgemmError(st, "sgemm_plan_query")
-    out = {name: getattr(pl, name) for name, _ in _Plan._fields_ if name != "reserved"}
+    out = {name: getattr(pl, name) for name, _ in _Plan._fields_}
     out["path_name"] = _PATH_NAMES.get(out["path"], "?")
+    out["decomposition_name"] = _DECOMP_NAMES.get(out["decomposition"], "?")
     return out
 
 

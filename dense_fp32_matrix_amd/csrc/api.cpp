@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstring>
 #include <limits>
+#include <vector>
 
 #include "../../include/sgemm.h"
 #include "kernels.hpp"
@@ -46,6 +47,7 @@ bool extent_ok(int64_t rows, int64_t cols, int64_t ld) {
 struct Plan {
     sgemm_plan pub;
     int64_t ldw = 0;       // split-K workspace leading dimension (floats)
+    int64_t k_steps = 0;   // stream-K: K-steps per tile
 };
 
 const TileShape& tile_of(int path, int tile) {
@@ -70,47 +72,92 @@ int tile_count(int path) {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
-// Relative throughput of a workgroup tile on the matrix cores, and how many
-// of its workgroups one CU holds at once (from the register and LDS budgets).
-// Used only to rank candidate plans.
-double mfma_tile_efficiency(int tile) {
+// ---------------------------------------------------------------------------
+// Planning.  Candidates are ranked by a simple time model: a CU retires
+// kMacRate multiply-adds per second times the tile's measured efficiency;
+// workgroups run in waves of (CUs x workgroups per CU); split-K and stream-K
+// add their partial-product traffic and one more launch.
+// ---------------------------------------------------------------------------
+constexpr double kMacRate = 128.0 * 2.4e9;   // FP32 MACs per second per CU at peak
+constexpr double kPartialBw = 4e12;          // bytes/s for partial tiles (mostly cache resident)
+constexpr double kLaunch = 4e-6;             // one more dependent kernel launch
+
+// Share of the CU's peak one tile shape sustains when its CU is full.
+double mfma_efficiency(int tile) {
     switch (tile) {
-        case 0: case 1: return 1.00;
-        case 3: return 1.00;
-        case 2: case 5: return 0.90;
-        default: return 0.60;
+        case 3: case 6: return 0.89;
+        case 0: case 1: case 7: return 0.85;
+        case 2: case 5: return 0.83;
+        default: return 0.70;
     }
 }
 
-// Modelled time (arbitrary units) of an MFMA plan: waves of workgroups times
-// the per-workgroup work, plus the reduction's traffic and launch when split.
-double mfma_cost(int tile, int64_t M, int64_t N, int64_t K, int64_t splits, int64_t k_chunk) {
+int wgs_per_cu(const TileShape& t) { return std::max(1, t.waves_per_simd * 4 / (t.waves_m * t.waves_n)); }
+
+struct Candidate {
+    int tile = 0;
+    int decomposition = SGEMM_DECOMP_TILES;
+    int64_t splits = 1, k_chunk = 0;
+    int64_t dp_tiles = 0, sk_tiles = 0, sk_ipw = 0, k_steps = 0, grid = 0;
+    double time = 0;
+};
+
+// One tile per workgroup, K split into `splits` slices.
+Candidate tiles_candidate(int tile, int64_t M, int64_t N, int64_t K, int64_t splits) {
     const TileShape& t = kMfmaTiles[tile];
+    Candidate c;
+    c.tile = tile;
+    c.decomposition = SGEMM_DECOMP_TILES;
+    splits = std::max<int64_t>(1, std::min(splits, cdiv(K, t.bk)));
+    c.k_chunk = round_up(cdiv(K, splits), t.bk);
+    c.splits = cdiv(K, c.k_chunk);
     const int64_t tiles = cdiv(M, t.bm) * cdiv(N, t.bn);
-    const int64_t per_cu = t.waves_per_simd * 4 / (t.waves_m * t.waves_n);   // WGs resident per CU
-    const int64_t slots = kNumCUs * std::max<int64_t>(per_cu, 1);
-    const int64_t waves = cdiv(tiles * splits, slots);
-    // one resident set shares the CU: each of its WGs takes per_cu times as long
-    const double wg_work = (double)t.bm * t.bn * round_up(std::min(k_chunk, K), t.bk);
-    const double cu_rate = 128.0 * 2.4e9 * 0.8;    // MACs/s per CU at ~80% of peak
-    double time = waves * wg_work * per_cu / (cu_rate * mfma_tile_efficiency(tile));
-    if (splits > 1) {
-        const double bytes = 2.0 * splits * M * N * 4 + M * N * 4.0;
-        time += bytes / 5e12 + 4e-6;              // reduction pass + one more launch
-    }
-    return time;
+    const int64_t per_cu = wgs_per_cu(t);
+    const int64_t wgs = tiles * c.splits;
+    const int64_t full_waves = wgs / (kNumCUs * per_cu);
+    const int64_t tail = wgs - full_waves * kNumCUs * per_cu;
+    const double wg_time = (double)t.bm * t.bn * c.k_chunk * per_cu / (kMacRate * mfma_efficiency(tile));
+    // a tail of at most one workgroup per CU runs alone on its CU (about 0.8 of the shared time)
+    double tail_time = 0;
+    if (tail > 0) tail_time = (tail <= kNumCUs && per_cu > 1) ? wg_time * 0.8 / per_cu * 1.25 : wg_time;
+    c.time = full_waves * wg_time + tail_time;
+    if (c.splits > 1) c.time += (2.0 * c.splits + 1) * M * N * 4 / kPartialBw + kLaunch;
+    return c;
 }
 
-void choose_split(int64_t tiles, int64_t K, int bk, int64_t target_wgs, int64_t max_splits,
-                  int64_t* splits, int64_t* k_chunk) {
-    int64_t s = 1;
-    if (tiles < target_wgs) s = cdiv(target_wgs, tiles);
-    s = std::min(s, std::max<int64_t>(1, K / (4 * bk)));   // at least 4 K-steps per slice
-    s = std::min(s, max_splits);
-    int64_t kc = round_up(cdiv(K, s), bk);
-    s = cdiv(K, kc);
-    *splits = std::max<int64_t>(s, 1);
-    *k_chunk = kc;
+// Stream-K on a persistent grid of one wave of workgroups: all but the last
+// full wave of tiles data-parallel, the rest shared out evenly by K-steps.
+Candidate streamk_candidate(int tile, int64_t M, int64_t N, int64_t K) {
+    const TileShape& t = kMfmaTiles[tile];
+    Candidate c;
+    c.tile = tile;
+    c.decomposition = SGEMM_DECOMP_STREAM_K;
+    const int64_t tiles = cdiv(M, t.bm) * cdiv(N, t.bn);
+    const int64_t grid = (int64_t)kNumCUs * wgs_per_cu(t);
+    c.grid = grid;
+    c.k_steps = cdiv(K, t.bk);
+    c.k_chunk = K;
+    c.dp_tiles = tiles >= grid ? (tiles / grid - 1) * grid : 0;
+    c.sk_tiles = tiles - c.dp_tiles;
+    const int64_t units = c.sk_tiles * c.k_steps;
+    c.sk_ipw = cdiv(units, grid);
+    const double step_time = (double)t.bm * t.bn * t.bk * wgs_per_cu(t) / (kMacRate * mfma_efficiency(tile));
+    c.time = (double)(c.dp_tiles / grid) * c.k_steps * step_time + c.sk_ipw * step_time;
+    // partial tiles: count the workgroup ranges' segments that do not cover a
+    // whole tile; each is written to a slot and read back once
+    int64_t partial = 0;
+    for (int64_t w = 0; w < grid; ++w) {
+        int64_t it = w * c.sk_ipw;
+        const int64_t end = std::min(it + c.sk_ipw, units);
+        while (it < end) {
+            const int64_t ks0 = it % c.k_steps;
+            const int64_t ks1 = std::min(c.k_steps, ks0 + (end - it));
+            if (ks0 != 0 || ks1 != c.k_steps) ++partial;
+            it += ks1 - ks0;
+        }
+    }
+    if (partial > 0) c.time += 2.0 * partial * t.bm * t.bn * 4 / kPartialBw + kLaunch;
+    return c;
 }
 
 sgemm_status validate(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
@@ -129,6 +176,18 @@ sgemm_status validate(int64_t M, int64_t N, int64_t K, const float* A, int64_t l
     return SGEMM_OK;
 }
 
+void choose_split(int64_t tiles, int64_t K, int bk, int64_t target_wgs, int64_t max_splits,
+                  int64_t* splits, int64_t* k_chunk) {
+    int64_t s = 1;
+    if (tiles < target_wgs) s = cdiv(target_wgs, tiles);
+    s = std::min(s, std::max<int64_t>(1, K / (4 * bk)));   // at least 4 K-steps per slice
+    s = std::min(s, max_splits);
+    int64_t kc = round_up(cdiv(K, s), bk);
+    s = cdiv(K, kc);
+    *splits = std::max<int64_t>(s, 1);
+    *k_chunk = kc;
+}
+
 sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
                        int64_t ldb, const float* C, int64_t ldc, const sgemm_options* opts, Plan* out) {
     sgemm_status st = validate(M, N, K, A, lda, B, ldb, C, ldc);
@@ -137,21 +196,17 @@ sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
     if (opts) o = *opts;
     if (o.path < SGEMM_PATH_AUTO || o.path > SGEMM_PATH_SKINNY) return SGEMM_ERR_INVALID_ARG;
     if (o.split_k < 0 || o.vector < 0 || o.vector > 1) return SGEMM_ERR_INVALID_ARG;
+    if (o.decomposition < SGEMM_DECOMP_AUTO || o.decomposition > SGEMM_DECOMP_STREAM_K) return SGEMM_ERR_INVALID_ARG;
     if (o.workspace != nullptr && !aligned(o.workspace, 256)) return SGEMM_ERR_INVALID_ARG;
 
     Plan p;
     std::memset(&p.pub, 0, sizeof(p.pub));
     sgemm_plan& q = p.pub;
     q.split_k = 1;
-    if (M == 0 || N == 0) {          // nothing to write
+    q.decomposition = SGEMM_DECOMP_TILES;
+    if (M == 0 || N == 0 || K == 0) {   // nothing to write, or the empty sum (C = 0)
         q.path = o.path == SGEMM_PATH_AUTO ? SGEMM_PATH_MFMA : o.path;
-        q.launches = 0;
-        *out = p;
-        return SGEMM_OK;
-    }
-    if (K == 0) {                    // the empty sum: C = 0
-        q.path = o.path == SGEMM_PATH_AUTO ? SGEMM_PATH_MFMA : o.path;
-        q.launches = 1;
+        q.launches = (M == 0 || N == 0) ? 0 : 1;
         *out = p;
         return SGEMM_OK;
     }
@@ -161,88 +216,115 @@ sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
     q.vector = (vec_ok && o.vector == 0) ? 1 : 0;
 
     int path = o.path;
-    if (path == SGEMM_PATH_AUTO) path = (M <= 16) ? SGEMM_PATH_SKINNY : SGEMM_PATH_MFMA;
+    if (path == SGEMM_PATH_AUTO) {
+        path = (M <= 16) ? SGEMM_PATH_SKINNY : SGEMM_PATH_MFMA;
+        o.tile = -1;                 // the tile index belongs to an explicit path
+    }
     if (path == SGEMM_PATH_SKINNY && M > 16) return SGEMM_ERR_INVALID_ARG;
     const int ntiles = tile_count(path);
     if (o.tile < -1 || o.tile >= ntiles) return SGEMM_ERR_INVALID_ARG;
     if (path == SGEMM_PATH_NAIVE && o.split_k > 1) return SGEMM_ERR_INVALID_ARG;
+    if (o.decomposition == SGEMM_DECOMP_STREAM_K && (path != SGEMM_PATH_MFMA || o.split_k > 1))
+        return SGEMM_ERR_INVALID_ARG;
 
-    int tile = o.tile;
-    int64_t splits = 1, k_chunk = K;
+    Candidate best;
     if (path == SGEMM_PATH_NAIVE) {
-        tile = 0;
+        best.tile = 0;
+        best.k_chunk = K;
     } else if (path == SGEMM_PATH_SKINNY) {
-        tile = 0;
+        best.tile = 0;
         const TileShape& t = kSkinnyTiles[0];
         const int64_t tiles = cdiv(N, t.bn);
+        int64_t splits = 1, k_chunk = K;
         if (o.split_k > 0) {
             splits = std::min<int64_t>(o.split_k, cdiv(K, t.bk));
-            k_chunk = round_up(cdiv(K, splits), t.bk);
-            splits = cdiv(K, k_chunk);
         } else {
             // enough workgroups to keep every CU streaming: about 4 per CU
             choose_split(tiles, K, t.bk / 4, 4 * kNumCUs, 64, &splits, &k_chunk);
-            k_chunk = round_up(k_chunk, t.bk);
-            splits = cdiv(K, k_chunk);
         }
-    } else if (path == SGEMM_PATH_MFMA && tile < 0) {
-        // rank candidate (tile, split) plans with the cost model
-        double best = 0;
-        for (int cand : {0, 1, 2, 3, 4}) {
-            const TileShape& t = kMfmaTiles[cand];
-            const int64_t tiles = cdiv(M, t.bm) * cdiv(N, t.bn);
-            int64_t s = 1, kc = K;
-            if (o.split_k > 0) {
-                s = std::min<int64_t>(o.split_k, cdiv(K, t.bk));
-                kc = round_up(cdiv(K, s), t.bk);
-                s = cdiv(K, kc);
-            } else {
-                const int64_t per_cu = t.waves_per_simd * 4 / (t.waves_m * t.waves_n);
-                choose_split(tiles, K, t.bk, kNumCUs * per_cu, 32, &s, &kc);
+        k_chunk = round_up(cdiv(K, splits), t.bk);
+        best.splits = cdiv(K, k_chunk);
+        best.k_chunk = k_chunk;
+    } else if (path == SGEMM_PATH_MFMA) {
+        std::vector<int> cands;
+        if (o.tile >= 0) cands.push_back(o.tile);
+        else cands = {3, 0, 1, 2, 5, 4};
+        bool have = false;
+        for (int tile : cands) {
+            std::vector<Candidate> cs;
+            if (o.decomposition != SGEMM_DECOMP_STREAM_K) {
+                if (o.split_k > 0) {
+                    cs.push_back(tiles_candidate(tile, M, N, K, o.split_k));
+                } else {
+                    const TileShape& t = kMfmaTiles[tile];
+                    const int64_t tiles = cdiv(M, t.bm) * cdiv(N, t.bn);
+                    const int64_t slots = (int64_t)kNumCUs * wgs_per_cu(t);
+                    cs.push_back(tiles_candidate(tile, M, N, K, 1));
+                    if (tiles < slots) {
+                        int64_t s = 1, kc = K;
+                        choose_split(tiles, K, t.bk, slots, 32, &s, &kc);
+                        cs.push_back(tiles_candidate(tile, M, N, K, s));
+                    }
+                }
             }
-            const double c = mfma_cost(cand, M, N, K, s, kc);
-            if (tile < 0 || c < best) {
-                best = c;
-                tile = cand;
-                splits = s;
-                k_chunk = kc;
+            if (o.decomposition != SGEMM_DECOMP_TILES && o.split_k <= 1) cs.push_back(streamk_candidate(tile, M, N, K));
+            for (const Candidate& c : cs) {
+                if (!have || c.time < best.time) {
+                    best = c;
+                    have = true;
+                }
             }
         }
-    } else {
-        if (tile < 0) tile = 0;
-        const TileShape& t = tile_of(path, tile);
+    } else {   // VALU
+        best.tile = o.tile < 0 ? 0 : o.tile;
+        const TileShape& t = kValuTiles[best.tile];
         const int64_t tiles = cdiv(M, t.bm) * cdiv(N, t.bn);
+        int64_t splits = 1, k_chunk = K;
         if (o.split_k > 0) {
             splits = std::min<int64_t>(o.split_k, cdiv(K, t.bk));
             k_chunk = round_up(cdiv(K, splits), t.bk);
             splits = cdiv(K, k_chunk);
         } else {
-            const int64_t per_cu = std::max(1, t.waves_per_simd * 4 / (t.waves_m * t.waves_n));
-            choose_split(tiles, K, t.bk, kNumCUs * per_cu, 32, &splits, &k_chunk);
+            choose_split(tiles, K, t.bk, (int64_t)kNumCUs * wgs_per_cu(t), 32, &splits, &k_chunk);
         }
+        best.splits = splits;
+        best.k_chunk = k_chunk;
     }
 
-    const TileShape& t = tile_of(path, tile);
+    const TileShape& t = tile_of(path, best.tile);
     q.path = path;
-    q.tile = tile;
+    q.tile = best.tile;
     q.bm = t.bm;
     q.bn = t.bn;
     q.bk = t.bk;
-    q.threads = 64 * t.waves_m * t.waves_n;
-    if (path == SGEMM_PATH_NAIVE) q.threads = 256;
+    q.threads = path == SGEMM_PATH_NAIVE ? 256 : 64 * t.waves_m * t.waves_n;
     q.tiles_m = cdiv(M, t.bm);
     q.tiles_n = cdiv(N, t.bn);
-    q.split_k = (int32_t)splits;
-    q.k_chunk = k_chunk;
-    q.workgroups = q.tiles_m * q.tiles_n * splits;
-    if (q.tiles_m * q.tiles_n * (int64_t)q.threads >= (int64_t(1) << 32) || splits > 65535)
-        return SGEMM_ERR_UNSUPPORTED;
-    if (splits > 1) {
-        p.ldw = round_up(N, 4);
-        q.workspace_bytes = (size_t)(splits * M * p.ldw * (int64_t)sizeof(float));
-        q.launches = 2;
+    q.decomposition = best.decomposition;
+    if (q.tiles_m * q.tiles_n * (int64_t)q.threads >= (int64_t(1) << 32)) return SGEMM_ERR_UNSUPPORTED;
+    if (best.decomposition == SGEMM_DECOMP_STREAM_K) {
+        q.split_k = 1;
+        q.k_chunk = K;
+        q.workgroups = best.grid;
+        q.dp_tiles = best.dp_tiles;
+        q.sk_tiles = best.sk_tiles;
+        q.sk_units_per_wg = best.sk_ipw;
+        p.k_steps = best.k_steps;
+        const bool splits_tiles = best.sk_ipw % best.k_steps != 0 || best.sk_ipw < best.k_steps;
+        q.workspace_bytes = splits_tiles ? (size_t)(2 * best.grid) * t.bm * t.bn * sizeof(float) : 0;
+        q.launches = splits_tiles ? 2 : 1;
     } else {
-        q.launches = 1;
+        if (best.splits > 65535) return SGEMM_ERR_UNSUPPORTED;
+        q.split_k = (int32_t)best.splits;
+        q.k_chunk = best.k_chunk;
+        q.workgroups = q.tiles_m * q.tiles_n * best.splits;
+        if (best.splits > 1) {
+            p.ldw = round_up(N, 4);
+            q.workspace_bytes = (size_t)(best.splits * M * p.ldw * (int64_t)sizeof(float));
+            q.launches = 2;
+        } else {
+            q.launches = 1;
+        }
     }
     *out = p;
     return SGEMM_OK;
@@ -262,7 +344,7 @@ sgemm_status run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, c
 
     void* ws = nullptr;
     bool owned = false;
-    if (q.split_k > 1) {
+    if (q.workspace_bytes > 0) {
         if (opts != nullptr && opts->workspace != nullptr) {
             if (opts->workspace_bytes < q.workspace_bytes) return SGEMM_ERR_ALLOC;
             ws = opts->workspace;
@@ -276,6 +358,7 @@ sgemm_status run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, c
     }
 
     GemmArgs g;
+    std::memset(&g, 0, sizeof(g));
     g.A = A;
     g.B = B;
     g.M = (int32_t)M;
@@ -286,17 +369,22 @@ sgemm_status run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, c
     g.ldb = ldb;
     g.tiles_m = (int32_t)q.tiles_m;
     g.tiles_n = (int32_t)q.tiles_n;
-    // 8 tile rows per raster group: the 64 workgroups one XCD holds at a time
-    // (32 CUs x 2) then cover about an 8 x 8 block of tiles
+    // 8 tile rows per raster group: the workgroups one XCD holds at a time
+    // then cover a roughly square block of tiles
     g.group_m = (int32_t)std::min<int64_t>(q.tiles_m, 8);
-    if (q.split_k > 1) {
+    g.C = C;
+    g.ldc = ldc;
+    if (q.decomposition == SGEMM_DECOMP_STREAM_K) {
+        g.sk_grid = (int32_t)q.workgroups;
+        g.dp_tiles = (int32_t)q.dp_tiles;
+        g.k_steps = (int32_t)p.k_steps;
+        g.sk_iters = q.sk_tiles * p.k_steps;
+        g.sk_ipw = q.sk_units_per_wg;
+        g.ws = static_cast<float*>(ws);
+    } else if (q.split_k > 1) {
         g.C = static_cast<float*>(ws);
         g.ldc = p.ldw;
         g.c_slice = M * p.ldw;
-    } else {
-        g.C = C;
-        g.ldc = ldc;
-        g.c_slice = 0;
     }
 
     hipError_t e;
@@ -306,9 +394,13 @@ sgemm_status run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, c
         case SGEMM_PATH_SKINNY: e = launch_skinny(q.tile, q.vector != 0, g, q.split_k, stream); break;
         default: e = launch_mfma(q.tile, q.vector != 0, g, q.split_k, stream); break;
     }
-    if (e == hipSuccess && q.split_k > 1)
-        e = launch_splitk_reduce(static_cast<const float*>(ws), p.ldw, M * p.ldw, q.split_k, C, ldc,
-                                 (int32_t)M, (int32_t)N, stream);
+    if (e == hipSuccess && q.launches == 2) {
+        if (q.decomposition == SGEMM_DECOMP_STREAM_K)
+            e = launch_streamk_fixup(g, q.bm, q.bn, (int)q.sk_tiles, stream);
+        else
+            e = launch_splitk_reduce(static_cast<const float*>(ws), p.ldw, M * p.ldw, q.split_k, C, ldc,
+                                     (int32_t)M, (int32_t)N, stream);
+    }
     if (owned) {
         if (hipFreeAsync(ws, stream) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
     }

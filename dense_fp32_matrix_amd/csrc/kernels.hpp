@@ -21,6 +21,13 @@ struct GemmArgs {
     int64_t c_slice;    // elements between consecutive slices' outputs
     int32_t tiles_m, tiles_n;
     int32_t group_m;    // tile rows per raster group (tile-order swizzle), >= 1
+    // stream-K decomposition (MFMA path only; sk_iters == 0 disables it)
+    int32_t sk_grid;    // persistent workgroups
+    int32_t dp_tiles;   // tiles computed whole, before the stream-K tiles
+    int32_t k_steps;    // K-steps per tile, ceil(K / BK)
+    int64_t sk_iters;   // (tile, K-step) units of the stream-K tiles
+    int64_t sk_ipw;     // units per workgroup
+    float* ws;          // partial-tile slots, 2 per workgroup, BM * BN floats each
 };
 
 // Workgroup -> output tile.  Consecutive workgroup ids are dispatched
@@ -51,15 +58,18 @@ struct TileShape {
     int bm, bn, bk;
     int waves_m, waves_n;   // waves per workgroup along M and N
     int waves_per_simd;     // occupancy the register budget is sized for
+    int sched = 1;          // 1: interleave LDS and global memory instructions between MFMAs
 };
 
 constexpr TileShape kMfmaTiles[] = {
-    {256, 128, 16, 2, 2, 2},   // 0: large products
-    {128, 256, 16, 2, 2, 2},   // 1: large products, wide N
-    {128, 128, 16, 2, 2, 2},   // 2: medium
-    {256, 256, 16, 2, 2, 1},   // 3: one workgroup per CU
-    {64, 64, 16, 2, 2, 4},     // 4: small products / split-K
-    {128, 128, 32, 2, 2, 2},   // 5: medium, deeper K-step
+    {256, 128, 16, 2, 2, 2, 0},   // 0: two workgroups per CU
+    {128, 256, 16, 2, 2, 2, 0},   // 1: two workgroups per CU, wide N
+    {128, 128, 16, 2, 2, 2, 0},   // 2: medium
+    {256, 256, 16, 2, 2, 1, 1},   // 3: one workgroup (one wave per SIMD) per CU, interleaved schedule
+    {64, 64, 16, 2, 2, 4, 0},     // 4: small products / split-K
+    {128, 128, 32, 2, 2, 2, 0},   // 5: medium, deeper K-step
+    {256, 256, 32, 2, 2, 1, 1},   // 6: as 3 with a deeper K-step (half the barriers)
+    {128, 256, 16, 2, 2, 2, 1},   // 7: as 1, interleaved schedule
 };
 constexpr int kNumMfmaTiles = sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]);
 
@@ -86,6 +96,10 @@ hipError_t launch_skinny(int tile, bool vec, const GemmArgs& g, int splits, hipS
 // C[i][j] = sum_{z=0}^{splits-1} W[z*w_slice + i*ldw + j], summed in order z = 0, 1, ...
 hipError_t launch_splitk_reduce(const float* W, int64_t ldw, int64_t w_slice, int splits,
                                 float* C, int64_t ldc, int32_t M, int32_t N, hipStream_t stream);
+
+// Stream-K fix-up: for each stream-K tile split over several workgroups, sum
+// its partial slots in workgroup order and write the tile to C.
+hipError_t launch_streamk_fixup(const GemmArgs& g, int bm, int bn, int sk_tiles, hipStream_t stream);
 
 // C[i][j] = +0.0 for i < M, j < N (the empty sum, K == 0).
 hipError_t launch_fill_zero(float* C, int64_t ldc, int32_t M, int32_t N, hipStream_t stream);

@@ -83,6 +83,7 @@ struct MfmaCfg {
     static_assert(T % (BK / 4) == 0 && T % (BN / 4) == 0, "vector loader rows");
     static_assert(T % BK == 0 && T % BN == 0, "scalar loader rows");
     static_assert(2 * STAGE * 4 <= 160 * 1024, "LDS budget");
+    static_assert(KG % 2 == 0, "the fragment sets alternate within a K-step");
 };
 
 // Chunk-position swizzle of A-tile row r (BK/4 chunks of 16 bytes per row).
@@ -92,26 +93,62 @@ __device__ __forceinline__ int a_swizzle(int r) {
     else return (r ^ (r >> 3)) & 7;
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, bool VEC, int WPE>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
-                          amdgpu_waves_per_eu(WPE, WPE)))
-void mfma_gemm_kernel(GemmArgs g) {
-    using P = MfmaCfg<BM, BN, BK, WGM, WGN, VEC>;
-    __shared__ __attribute__((aligned(16))) float smem[2 * P::STAGE];
+// Scheduling hints for one K-loop iteration of KG groups of NM MFMAs each:
+// in every group one LDS read (the next group's fragments, NR of them) is
+// placed after each of the first MFMAs; the next MFMA slots of the first
+// group take the NV global loads of the next K-step, and the last NV slots
+// of the last group its NV LDS writes.  __builtin_amdgcn_sched_group_barrier needs
+// constant arguments, hence the recursion over template parameters.
+constexpr int kMaskMfma = 0x008, kMaskVmemRead = 0x020, kMaskDsRead = 0x100, kMaskDsWrite = 0x200;
 
+template <int I, int NM, int NR, int NV, int EXTRA_MASK>
+__device__ __forceinline__ void interleave_group() {
+    if constexpr (I < NM) {
+        __builtin_amdgcn_sched_group_barrier(kMaskMfma, 1, 0);
+        if constexpr (I < NR) {
+            __builtin_amdgcn_sched_group_barrier(kMaskDsRead, 1, 0);
+        } else if constexpr (EXTRA_MASK == kMaskVmemRead) {
+            if constexpr (I - NR < NV) __builtin_amdgcn_sched_group_barrier(EXTRA_MASK, 1, 0);
+        } else if constexpr (EXTRA_MASK == kMaskDsWrite) {
+            // LDS writes go last, as far as possible from the loads they wait for
+            if constexpr (I >= NM - NV) __builtin_amdgcn_sched_group_barrier(EXTRA_MASK, 1, 0);
+        }
+        interleave_group<I + 1, NM, NR, NV, EXTRA_MASK>();
+    }
+}
+
+template <int NM, int NR, int NV, int KG, int G = 0>
+__device__ __forceinline__ void interleave_hints() {
+    if constexpr (G < KG) {
+        constexpr int extra = G == 0 ? kMaskVmemRead : (G == KG - 1 ? kMaskDsWrite : 0);
+        interleave_group<0, NM, NR, NV, extra>();
+        interleave_hints<NM, NR, NV, KG, G + 1>();
+    }
+}
+
+// Where a tile's result goes: element (i, j) of the tile (tile-local
+// coordinates) is written to out[(row0 + i) * ldo + col0 + j] when
+// row0 + i < row_lim and col0 + j < col_lim.
+struct TileOut {
+    float* out;
+    int64_t ldo;
+    int row0, col0, row_lim, col_lim;
+};
+
+// One output tile (tm, tn) over k in [kb, ke): load, contract, write.  All
+// threads of the workgroup call it together; smem is the workgroup's LDS.
+template <int BM, int BN, int BK, int WGM, int WGN, bool VEC, int SCHED>
+__device__ __forceinline__ void mfma_tile(const GemmArgs& g, float* smem, int tm, int tn, int kb, int ke,
+                                          const TileOut& o) {
+    using P = MfmaCfg<BM, BN, BK, WGM, WGN, VEC>;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave / WGN;
     const int wn = wave % WGN;
 
-    int tm, tn;
-    tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
     const int m0 = tm * BM;
     const int n0 = tn * BN;
-
-    const int kb = blockIdx.z * g.k_chunk;
-    const int ke = min(g.K, kb + g.k_chunk);
     const int steps = (ke - kb + BK - 1) / BK;
 
     // ---- loader bookkeeping (constant over the K loop) ----
@@ -160,18 +197,22 @@ void mfma_gemm_kernel(GemmArgs g) {
 
     // Masked-off elements load from kZeroMfma, so the loaded registers are
     // final and nothing waits on them before they are written to LDS.
+    // The K-step's base addresses are uniform (scalar) and every per-lane
+    // address is a plain select, so the loads never sit behind a branch.
     auto load = [&](int k0) {
+        const float* abase = g.A + k0;
+        const float* bbase = g.B + (int64_t)k0 * g.ldb;
 #pragma unroll
         for (int r = 0; r < AN; ++r) {
             const bool ok = a_rok[r] && (k0 + a_kc[r] < ke);
-            const float* p = ok ? g.A + a_off[r] + k0 : kZeroMfma;
+            const float* p = ok ? abase + a_off[r] : kZeroMfma;
             if constexpr (VEC) va[r] = *reinterpret_cast<const f32x4*>(p);
             else sa[r] = *p;
         }
 #pragma unroll
         for (int r = 0; r < BNL; ++r) {
             const bool ok = b_cok[r] && (k0 + b_kr[r] < ke);
-            const float* p = ok ? g.B + b_off[r] + (int64_t)k0 * g.ldb : kZeroMfma;
+            const float* p = ok ? bbase + b_off[r] : kZeroMfma;
             if constexpr (VEC) vb[r] = *reinterpret_cast<const f32x4*>(p);
             else sb[r] = *p;
         }
@@ -236,54 +277,126 @@ void mfma_gemm_kernel(GemmArgs g) {
                                                                        acc[mb][nb], 0, 0, 0);
     };
 
+    // The K loop is rotated so that its body is one basic block that starts
+    // at a barrier: nothing in it is conditional (a load past the end of the
+    // slice reads the zero block, and the last stage write lands in a buffer
+    // nobody reads), which lets the scheduler interleave the memory
+    // instructions with the MFMAs.  Iteration s (1 <= s < steps):
+    //   barrier; read group 0 of step s; MFMAs of the last group of step s-1;
+    //   load step s+1; groups 0..KG-2 of step s (each reading the next
+    //   group's fragments first); write step s+1 to the other buffer.
     if (steps > 0) {
         load(kb);
         store(0);
         __syncthreads();
         read_frags(0, 0, 0);
-        for (int s = 0; s < steps; ++s) {
+        load(kb + BK);
+#pragma unroll
+        for (int kg = 0; kg + 1 < P::KG; ++kg) {
+            read_frags(0, kg + 1, (kg + 1) & 1);
+            mfmas(kg & 1);
+        }
+        store(1);
+        for (int s = 1; s < steps; ++s) {
             const int cur = s & 1;
-            const bool more = s + 1 < steps;
-            if (more) load(kb + (s + 1) * BK);
+            __syncthreads();
+            read_frags(cur, 0, 0);          // KG is even: group 0 goes to set 0 ...
+            mfmas(1);                        // ... while step s-1's last group (set 1) runs
+            load(kb + (s + 1) * BK);
 #pragma unroll
             for (int kg = 0; kg + 1 < P::KG; ++kg) {
                 read_frags(cur, kg + 1, (kg + 1) & 1);
                 mfmas(kg & 1);
             }
-            if (more) store(cur ^ 1);
-            __syncthreads();
-            // KG is even, so the next step's first group goes to set 0 while
-            // this step's last group (set 1) is contracted
-            if (more) read_frags(cur ^ 1, 0, 0);
-            mfmas((P::KG - 1) & 1);
+            store(cur ^ 1);
+            if constexpr (SCHED) interleave_hints<P::MB * P::NB * 4, P::MB + 2 * P::NB, AN + BNL, P::KG>();
         }
+        mfmas(1);                            // last group of the last step
     }
 
-    // ---- epilogue: overwrite C (masked at the M / N edges) ----
-    float* C = g.C + (int64_t)blockIdx.z * g.c_slice;
+    // ---- epilogue: overwrite the destination (masked at its edges) ----
 #pragma unroll
     for (int mb = 0; mb < P::MB; ++mb) {
 #pragma unroll
         for (int nb = 0; nb < P::NB; ++nb) {
-            const int j = n0 + wn * P::WN + nb * 32 + l32;
-            const int ib = m0 + wm * P::WM + mb * 32 + 4 * lh;
+            const int j = o.col0 + wn * P::WN + nb * 32 + l32;
+            const int ib = o.row0 + wm * P::WM + mb * 32 + 4 * lh;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = ib + 8 * (r >> 2) + (r & 3);
-                if (i < g.M && j < g.N) C[(int64_t)i * g.ldc + j] = acc[mb][nb][r];
+                if (i < o.row_lim && j < o.col_lim) o.out[(int64_t)i * o.ldo + j] = acc[mb][nb][r];
             }
         }
     }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int WPE>
+// The kernel has two work decompositions.
+//  * One tile per workgroup (sk_iters == 0): workgroup x owns tile x (in the
+//    XCD-aware order) and slice z = blockIdx.z of K; the slices' partial
+//    products go to C + z * c_slice (split-K, summed by a second kernel).
+//  * Stream-K (sk_iters > 0), a persistent grid of P workgroups: first the
+//    dp_tiles "data-parallel" tiles, tile t on workgroup t % P, each over all
+//    of K; then the remaining tiles' K-steps, flattened to sk_iters
+//    (tile, K-step) units and cut into P equal ranges of sk_ipw units.  A
+//    range covering a whole tile writes C; a partial tile is written to the
+//    workspace slot 2 * wg + (0 for the range's first tile, 1 for its last)
+//    and the stream-K fix-up kernel sums the slots of each tile in range
+//    order.  The cut depends only on the shapes, so the sums always happen in
+//    the same order (the work-splitting of "GEMM from naive to tiled", 十.1).
+template <int BM, int BN, int BK, int WGM, int WGN, bool VEC, int WPE, int SCHED>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
+                          amdgpu_waves_per_eu(WPE, WPE)))
+void mfma_gemm_kernel(GemmArgs g) {
+    using P = MfmaCfg<BM, BN, BK, WGM, WGN, VEC>;
+    __shared__ __attribute__((aligned(16))) float smem[2 * P::STAGE];
+    int tm, tn;
+    if (g.sk_iters == 0) {
+        tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
+        const int kb = blockIdx.z * g.k_chunk;
+        const int ke = min(g.K, kb + g.k_chunk);
+        const TileOut o{g.C + (int64_t)blockIdx.z * g.c_slice, g.ldc, tm * BM, tn * BN, g.M, g.N};
+        mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, smem, tm, tn, kb, ke, o);
+        return;
+    }
+    for (int t = blockIdx.x; t < g.dp_tiles; t += gridDim.x) {
+        tile_coords(t, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
+        const TileOut o{g.C, g.ldc, tm * BM, tn * BN, g.M, g.N};
+        mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, smem, tm, tn, 0, g.K, o);
+        __syncthreads();                 // the next tile's prologue overwrites LDS
+    }
+    int64_t it = (int64_t)blockIdx.x * g.sk_ipw;
+    const int64_t it_end = min(it + g.sk_ipw, g.sk_iters);
+    int which = 0;
+    while (it < it_end) {
+        const int j = (int)(it / g.k_steps);
+        const int ks0 = (int)(it - (int64_t)j * g.k_steps);
+        const int ks1 = (int)min((int64_t)g.k_steps, ks0 + (it_end - it));
+        tile_coords(g.dp_tiles + j, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
+        const int kb = ks0 * BK;
+        const int ke = min(g.K, ks1 * BK);
+        if (ks0 == 0 && ks1 == g.k_steps) {
+            const TileOut o{g.C, g.ldc, tm * BM, tn * BN, g.M, g.N};
+            mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, smem, tm, tn, kb, ke, o);
+        } else {
+            float* slot = g.ws + (int64_t)(2 * blockIdx.x + which) * (BM * BN);
+            const TileOut o{slot, BN, 0, 0, BM, BN};
+            mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, smem, tm, tn, kb, ke, o);
+        }
+        __syncthreads();
+        which = 1;
+        it += ks1 - ks0;
+    }
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, int WPE, int SCHED>
 hipError_t launch_one(bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
-    dim3 grid((unsigned)((int64_t)g.tiles_m * g.tiles_n), 1, (unsigned)splits);
+    dim3 grid(g.sk_iters > 0 ? (unsigned)g.sk_grid : (unsigned)((int64_t)g.tiles_m * g.tiles_n), 1,
+              g.sk_iters > 0 ? 1u : (unsigned)splits);
     dim3 block(64 * WGM * WGN);
     if (vec)
-        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, true, WPE>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, true, WPE, SCHED>), grid, block, 0, stream, g);
     else
-        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, false, WPE>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, false, WPE, SCHED>), grid, block, 0, stream, g);
     return hipGetLastError();
 }
 
@@ -294,7 +407,7 @@ hipError_t launch_mfma(int tile, bool vec, const GemmArgs& g, int splits, hipStr
     case ID:                                                                                    \
         return launch_one<kMfmaTiles[ID].bm, kMfmaTiles[ID].bn, kMfmaTiles[ID].bk,             \
                           kMfmaTiles[ID].waves_m, kMfmaTiles[ID].waves_n,                      \
-                          kMfmaTiles[ID].waves_per_simd>(vec, g, splits, stream);
+                          kMfmaTiles[ID].waves_per_simd, kMfmaTiles[ID].sched>(vec, g, splits, stream);
     switch (tile) {
         SGEMM_MFMA_CASE(0)
         SGEMM_MFMA_CASE(1)
@@ -302,11 +415,13 @@ hipError_t launch_mfma(int tile, bool vec, const GemmArgs& g, int splits, hipStr
         SGEMM_MFMA_CASE(3)
         SGEMM_MFMA_CASE(4)
         SGEMM_MFMA_CASE(5)
+        SGEMM_MFMA_CASE(6)
+        SGEMM_MFMA_CASE(7)
         default:
             return hipErrorInvalidValue;
     }
 #undef SGEMM_MFMA_CASE
 }
-static_assert(kNumMfmaTiles == 6, "launch_mfma covers every MFMA tile");
+static_assert(kNumMfmaTiles == 8, "launch_mfma covers every MFMA tile");
 
 }  // namespace sgemm_impl

@@ -71,6 +71,40 @@ void fill_zero_kernel(float* __restrict__ C, int64_t ldc, int32_t M, int32_t N) 
     }
 }
 
+// Stream-K fix-up (see the stream-K decomposition of the MFMA kernel): one
+// workgroup per stream-K tile.  A tile whose K-steps fall in one workgroup's
+// range was written whole; otherwise its partial slots, from workgroups
+// w0..w1 in that order, are summed and the tile is written to C.
+__global__ __launch_bounds__(256)
+void streamk_fixup_kernel(GemmArgs g, int bm, int bn) {
+    const int j = blockIdx.x;
+    const int64_t first = (int64_t)j * g.k_steps;
+    const int64_t last = first + g.k_steps - 1;
+    const int w0 = (int)(first / g.sk_ipw);
+    const int w1 = (int)(last / g.sk_ipw);
+    if (w0 == w1) return;
+    int tm, tn;
+    tile_coords(g.dp_tiles + j, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
+    const int m0 = tm * bm;
+    const int n0 = tn * bn;
+    const int64_t slot = (int64_t)bm * bn;
+    for (int e = 4 * threadIdx.x; e < bm * bn; e += 4 * blockDim.x) {
+        const int i = e / bn;
+        const int c = e - i * bn;
+        if (m0 + i >= g.M || n0 + c >= g.N) continue;
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        for (int w = w0; w <= w1; ++w) {
+            const int which = (int64_t)w * g.sk_ipw >= first ? 0 : 1;
+            s += *reinterpret_cast<const f32x4*>(g.ws + (int64_t)(2 * w + which) * slot + e);
+        }
+        float* crow = g.C + (int64_t)(m0 + i) * g.ldc + n0 + c;
+        crow[0] = s[0];
+        if (n0 + c + 1 < g.N) crow[1] = s[1];
+        if (n0 + c + 2 < g.N) crow[2] = s[2];
+        if (n0 + c + 3 < g.N) crow[3] = s[3];
+    }
+}
+
 unsigned grid_for(int64_t items, int64_t per_block) {
     int64_t blocks = (items + per_block - 1) / per_block;
     if (blocks > 256 * 16) blocks = 256 * 16;   // grid-stride beyond 16 workgroups per CU
@@ -92,6 +126,11 @@ hipError_t launch_splitk_reduce(const float* W, int64_t ldw, int64_t w_slice, in
     const int64_t items = (int64_t)M * (ldw / 4);
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for(items, 256)), dim3(256), 0, stream,
                        W, ldw, w_slice, splits, C, ldc, M, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_streamk_fixup(const GemmArgs& g, int bm, int bn, int sk_tiles, hipStream_t stream) {
+    hipLaunchKernelGGL(streamk_fixup_kernel, dim3((unsigned)sk_tiles), dim3(256), 0, stream, g, bm, bn);
     return hipGetLastError();
 }
 

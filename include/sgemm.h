@@ -82,22 +82,36 @@ typedef enum sgemm_path {
     SGEMM_PATH_SKINNY = 4   /* M <= 16: streams B once, FP32 matrix cores (16x16x4) */
 } sgemm_path;
 
+/* Work decompositions of the tiled paths. */
+typedef enum sgemm_decomposition {
+    SGEMM_DECOMP_AUTO = 0,      /* per-shape choice */
+    SGEMM_DECOMP_TILES = 1,     /* one output tile (and K slice) per workgroup */
+    SGEMM_DECOMP_STREAM_K = 2   /* persistent workgroups share the tiles' K-steps evenly
+                                   (MFMA path only) */
+} sgemm_decomposition;
+
 /*
  * Options for sgemm_ex.  Zero-initialised options mean "same as sgemm".
- *   path      : an sgemm_path.
- *   tile      : index into the path's tile table (sgemm_tile_info), or -1 to choose.
- *   split_k   : 0 = choose, 1 = no split, S >= 2 = split K into S slices whose
- *               partial products are summed in slice order 0..S-1 by a second kernel.
- *   vector    : 0 = choose (16-byte loads when the operands allow them),
- *               1 = force 4-byte loads.
- *   workspace : device buffer of workspace_bytes for split-K partials, or NULL
- *               to let the library allocate it stream-ordered.
+ *   path          : an sgemm_path.
+ *   tile          : index into the path's tile table (sgemm_tile_info), or -1 to choose;
+ *                   ignored when path is SGEMM_PATH_AUTO.
+ *   split_k       : 0 = choose, 1 = no split, S >= 2 = split K into S slices whose
+ *                   partial products are summed in slice order 0..S-1 by a second
+ *                   kernel (one-tile-per-workgroup decomposition only).
+ *   vector        : 0 = choose (16-byte loads when the operands allow them),
+ *                   1 = force 4-byte loads.
+ *   decomposition : an sgemm_decomposition.
+ *   workspace     : 256-byte aligned device buffer of workspace_bytes for split-K or
+ *                   stream-K partials, or NULL to let the library allocate it
+ *                   stream-ordered.  The caller keeps it alive until the work completes.
  */
 typedef struct sgemm_options {
     int32_t path;
     int32_t tile;
     int32_t split_k;
     int32_t vector;
+    int32_t decomposition;
+    int32_t reserved;
     void* workspace;
     size_t workspace_bytes;
 } sgemm_options;
@@ -114,16 +128,19 @@ sgemm_status sgemm_ex(int64_t M, int64_t N, int64_t K,
 typedef struct sgemm_plan {
     int32_t path;            /* sgemm_path actually used */
     int32_t tile;            /* tile table index */
-    int32_t split_k;         /* slices (1 = no split) */
+    int32_t split_k;         /* K slices (1 = no split) */
     int32_t vector;          /* 1 if the 16-byte loaders are used */
     int32_t bm, bn, bk;      /* block tile */
     int32_t threads;         /* threads per workgroup */
     int64_t tiles_m, tiles_n;/* output tiles along M and N */
     int64_t k_chunk;         /* K elements per slice */
     int64_t workgroups;      /* workgroups of the main kernel */
-    size_t workspace_bytes;  /* split-K scratch (0 if none) */
+    size_t workspace_bytes;  /* split-K / stream-K scratch (0 if none) */
     int32_t launches;        /* kernels enqueued by the call (0, 1 or 2) */
-    int32_t reserved;
+    int32_t decomposition;   /* sgemm_decomposition actually used */
+    int64_t dp_tiles;        /* stream-K: tiles computed whole first */
+    int64_t sk_tiles;        /* stream-K: tiles whose K-steps are shared out */
+    int64_t sk_units_per_wg; /* stream-K: (tile, K-step) units per workgroup */
 } sgemm_plan;
 
 sgemm_status sgemm_plan_query(int64_t M, int64_t N, int64_t K,

@@ -143,14 +143,37 @@ def test_default_plans_fill_the_chip():
         if p["split_k"] > 1:
             assert p["workspace_bytes"] >= p["split_k"] * M * N * 4
             assert p["launches"] == 2
-            assert lib.sgemm_workspace_size(M, N, K) == p["workspace_bytes"]
+        assert lib.sgemm_workspace_size(M, N, K) == p["workspace_bytes"]
     assert lib.sgemm_plan_query(16, 11008, 4096)["path_name"] == "skinny"
-    assert lib.sgemm_plan_query(512, 512, 65536)["split_k"] > 1
+    p = lib.sgemm_plan_query(512, 512, 65536)
+    assert p["split_k"] > 1 or p["decomposition_name"] == "stream_k"   # long K is shared out
 
 
 def test_forced_split_k_slices_cover_k():
     for S in (1, 2, 3, 7, 16):
-        p = lib.sgemm_plan_query(300, 200, 1000, path="mfma", tile=2, split_k=S)
+        p = lib.sgemm_plan_query(300, 200, 1000, path="mfma", tile=2, split_k=S, decomposition="tiles")
         assert p["k_chunk"] % p["bk"] == 0
         assert p["split_k"] <= S
         assert (p["split_k"] - 1) * p["k_chunk"] < 1000 <= p["split_k"] * p["k_chunk"]
+
+
+def test_stream_k_plans():
+    """Stream-K on the 256 x 256 tile: all but the last full wave of tiles are
+    data-parallel, the rest is cut into equal K-step ranges, one per CU."""
+    p = lib.sgemm_plan_query(8192, 11008, 4096, path="mfma", tile=3, decomposition="stream_k")
+    tiles = p["tiles_m"] * p["tiles_n"]
+    assert (p["tiles_m"], p["tiles_n"]) == (32, 43) and tiles == 1376
+    assert p["decomposition_name"] == "stream_k" and p["workgroups"] == 256
+    assert p["dp_tiles"] == 4 * 256 and p["sk_tiles"] == tiles - 4 * 256
+    k_steps = 4096 // p["bk"]
+    assert p["sk_units_per_wg"] == -(-p["sk_tiles"] * k_steps // 256)
+    assert p["launches"] == 2 and p["workspace_bytes"] == 2 * 256 * 256 * 256 * 4
+    # whole tiles per workgroup: no partial tiles, no fix-up
+    q = lib.sgemm_plan_query(4608, 4608, 32, path="mfma", tile=3, decomposition="stream_k")
+    assert q["sk_tiles"] == 324 and q["launches"] == 1 and q["workspace_bytes"] == 0 or \
+        q["sk_units_per_wg"] % (32 // q["bk"]) != 0
+    # stream-K is for the MFMA path without split-K
+    with pytest.raises(lib.SgemmError):
+        lib.sgemm_plan_query(512, 512, 512, path="valu", decomposition="stream_k")
+    with pytest.raises(lib.SgemmError):
+        lib.sgemm_plan_query(512, 512, 512, path="mfma", split_k=2, decomposition="stream_k")

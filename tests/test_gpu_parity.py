@@ -93,7 +93,8 @@ def test_naive(oracle_mod, shape):
 @pytest.mark.parametrize("vector", [0, 1])
 @pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_mfma_tiles(oracle_mod, shape, tile, vector):
-    check_case(oracle_mod, *shape, f"mfma/{tile}/v{vector}", path="mfma", tile=tile, vector=vector, split_k=1)
+    check_case(oracle_mod, *shape, f"mfma/{tile}/v{vector}", path="mfma", tile=tile, vector=vector, split_k=1,
+               decomposition="tiles")
 
 
 @pytest.mark.parametrize("tile", [0, 1])
@@ -116,6 +117,23 @@ def test_skinny(oracle_mod, shape, vector, split_k):
 def test_split_k(oracle_mod, path, tile, split_k):
     check_case(oracle_mod, 200, 136, 2000, f"{path}/{tile}/split{split_k}", path=path, tile=tile,
                split_k=split_k)
+
+
+STREAMK_SHAPES = [
+    (300, 200, 20),        # fewer tiles than workgroups, one K-step per tile
+    (513, 385, 1000),      # ragged tiles, K not a multiple of BK
+    (1000, 1000, 3000),    # 16 tiles of 256x256 over 256 workgroups
+    (4352, 4352, 48),      # 289 tiles: one data-parallel wave is not possible, all stream-K
+    (4608, 4608, 32),      # 324 tiles: stream-K with whole tiles per workgroup
+]
+
+
+@pytest.mark.parametrize("tile", [3, 0, 2])
+@pytest.mark.parametrize("vector", [0, 1])
+@pytest.mark.parametrize("shape", STREAMK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_stream_k(oracle_mod, shape, tile, vector):
+    check_case(oracle_mod, *shape, f"streamk/{tile}/v{vector}", path="mfma", tile=tile, vector=vector,
+               decomposition="stream_k")
 
 
 @pytest.mark.parametrize("shape", SMALL_SHAPES + [(64, 64, 8192), (20, 11008, 4096)],
@@ -211,8 +229,9 @@ def test_zero_row_and_column_exact(oracle_mod):
     assert np.all(C[5] == 0) and np.all(C[:, 17] == 0)
 
 
-@pytest.mark.parametrize("opts", [{}, {"path": "mfma", "tile": 2, "split_k": 4}, {"path": "skinny"}],
-                         ids=["auto", "split4", "skinny"])
+@pytest.mark.parametrize("opts", [{}, {"path": "mfma", "tile": 2, "split_k": 4}, {"path": "skinny"},
+                                  {"path": "mfma", "tile": 3, "decomposition": "stream_k"}],
+                         ids=["auto", "split4", "skinny", "streamk"])
 def test_run_to_run_determinism(opts):
     say(f"determinism {opts}")
     M = 16 if opts.get("path") == "skinny" else 300
