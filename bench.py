@@ -36,6 +36,7 @@ def parse():
     ap.add_argument("--path", default="auto")
     ap.add_argument("--tile", type=int, default=-1)
     ap.add_argument("--split-k", type=int, default=0)
+    ap.add_argument("--decomposition", default="auto")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time of the oracle sample (0 = skip the CPU baseline)")
     ap.add_argument("--flush-mib", type=int, default=1024,
@@ -116,8 +117,9 @@ def main():
     B = B_host.to(dev)
     C = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
     opts = {}
-    if args.path != "auto" or args.tile >= 0 or args.split_k:
-        opts = {"path": args.path, "tile": args.tile, "split_k": args.split_k}
+    if args.path != "auto" or args.tile >= 0 or args.split_k or args.decomposition != "auto":
+        opts = {"path": args.path, "tile": args.tile, "split_k": args.split_k,
+                "decomposition": args.decomposition}
     plan = lib.sgemm_plan_query(w.M, w.N, w.K, A.data_ptr(), w.lda, B.data_ptr(), w.ldb, C.data_ptr(), w.N,
                                 **opts)
 
@@ -168,7 +170,8 @@ def main():
                    4: "skinny_gemm_kernel"}.get(plan["path"], "?")
     src = {1: "simple.hip", 2: "valu.hip", 3: "mfma.hip", 4: "skinny.hip"}.get(plan["path"], "mfma.hip")
     digest = source_digest([f"dense_fp32_matrix_amd/csrc/{src}", "dense_fp32_matrix_amd/csrc/kernels.hpp"])
-    key = f"{main_kernel}:{w.name}:tile{plan['tile']}:split{plan['split_k']}:vec{plan['vector']}"
+    key = (f"{main_kernel}:{w.name}:tile{plan['tile']}:{plan['decomposition_name']}:split{plan['split_k']}"
+           f":vec{plan['vector']}")
     hbm_bound = w.M <= 16
     if hbm_bound:
         achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
@@ -204,6 +207,7 @@ def main():
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda, "ldb": w.ldb, "ldc": w.N,
                    "inputs": f"A~{w.a_kind}, B~{w.b_kind}", "path": plan["path_name"], "tile": plan["tile"],
                    "bm": plan["bm"], "bn": plan["bn"], "bk": plan["bk"], "split_k": plan["split_k"],
+                   "decomposition": plan["decomposition_name"],
                    "vector_loads": bool(plan["vector"]), "workgroups": plan["workgroups"]},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -232,17 +232,21 @@ sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
         best.tile = 0;
         best.k_chunk = K;
     } else if (path == SGEMM_PATH_SKINNY) {
-        best.tile = 0;
-        const TileShape& t = kSkinnyTiles[0];
+        // The 8-wave tile splits K inside the workgroup; split K across
+        // workgroups only while fewer than ~1024 waves would stream B.
+        best.tile = o.tile >= 0 ? o.tile : 1;
+        const TileShape& t = kSkinnyTiles[best.tile];
+        const int waves = t.waves_m * t.waves_n;
         const int64_t tiles = cdiv(N, t.bn);
-        int64_t splits = 1, k_chunk = K;
+        int64_t splits = 1;
         if (o.split_k > 0) {
-            splits = std::min<int64_t>(o.split_k, cdiv(K, t.bk));
+            splits = o.split_k;
         } else {
-            // enough workgroups to keep every CU streaming: about 4 per CU
-            choose_split(tiles, K, t.bk / 4, 4 * kNumCUs, 64, &splits, &k_chunk);
+            splits = std::max<int64_t>(1, cdiv(4 * kNumCUs, tiles * waves));
+            splits = std::min<int64_t>(splits, std::max<int64_t>(1, K / (4 * t.bk)));
         }
-        k_chunk = round_up(cdiv(K, splits), t.bk);
+        splits = std::min<int64_t>(splits, cdiv(K, t.bk));
+        const int64_t k_chunk = round_up(cdiv(K, splits), t.bk);
         best.splits = cdiv(K, k_chunk);
         best.k_chunk = k_chunk;
     } else if (path == SGEMM_PATH_MFMA) {

@@ -84,9 +84,12 @@ constexpr TileShape kNaiveTiles[] = {{4, 64, 1, 1, 1, 4}};
 constexpr int kNumNaiveTiles = 1;
 
 // Skinny products (M <= 16): a workgroup owns 16 rows x 64 columns and one K
-// slice, split over its 4 waves; K slices are multiples of bk = 64.
-constexpr TileShape kSkinnyTiles[] = {{16, 64, 64, 1, 4, 2}};
-constexpr int kNumSkinnyTiles = 1;
+// slice, split over its waves (4 or 8); K slices are multiples of bk = 16 x waves.
+constexpr TileShape kSkinnyTiles[] = {
+    {16, 64, 64, 1, 4, 2},     // 0: 4 waves
+    {16, 64, 128, 1, 8, 2},    // 1: 8 waves
+};
+constexpr int kNumSkinnyTiles = sizeof(kSkinnyTiles) / sizeof(kSkinnyTiles[0]);
 
 hipError_t launch_naive(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_mfma(int tile, bool vec, const GemmArgs& g, int splits, hipStream_t stream);

@@ -7,8 +7,8 @@
 // is therefore built to stream B with deep memory-level parallelism and no
 // LDS staging:
 //   * a wave owns 64 columns of C and a quarter of the workgroup's K slice;
-//     a workgroup (4 waves) owns 64 columns and one K slice, and slices of
-//     K across workgroups are summed by the split-K reduction;
+//     a workgroup (4 or 8 waves) owns 64 columns and one K slice, and slices
+//     of K across workgroups are summed by the split-K reduction;
 //   * lane l = 16 * kk + jj loads B[k][n + 4jj .. 4jj+3] as one 16-byte read
 //     for k = k0 + 4kk + t (t = 0..3): 16 lanes cover a 256-byte run of a row;
 //   * component c of that vector is the B operand of v_mfma_f32_16x16x4_f32
@@ -20,7 +20,7 @@
 //     from a 16-byte zero block, so loads are never followed by a select;
 //   * two register stages of 4 k-groups of 16 each keep 2 x 4 x 4 = 32 16-byte
 //     B loads per lane in flight while the previous stage is contracted;
-//   * the 4 waves' partial tiles are summed through LDS in wave order.
+//   * the waves' partial tiles are summed through LDS in wave order.
 // Operand layout of v_mfma_f32_16x16x4_f32 (wave64):
 //   A: lane l holds A[i = l % 16][kk = l / 16];  B: lane l holds B[kk = l / 16][j = l % 16];
 //   D: lane l, register r holds D[4 * (l / 16) + r][l % 16].
@@ -39,10 +39,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kGroups = 4;                 // k-groups of 16 per register stage
 constexpr int kStageK = 16 * kGroups;      // K elements per stage per wave
 
-template <bool VEC>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+template <bool VEC, int WAVES>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES), amdgpu_waves_per_eu(2, 2)))
 void skinny_gemm_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) float red[4][16][64];
+    __shared__ __attribute__((aligned(16))) float red[WAVES][16][64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -53,7 +53,7 @@ void skinny_gemm_kernel(GemmArgs g) {
     const int n_w = blockIdx.x * 64;
     const int kb = blockIdx.z * g.k_chunk;
     const int ke = min(g.K, kb + g.k_chunk);
-    const int kq = g.k_chunk / 4;                 // a multiple of 16 (host guarantees)
+    const int kq = g.k_chunk / WAVES;             // a multiple of 16 (host guarantees)
     const int wkb = min(ke, kb + wave * kq);
     const int wke = min(ke, wkb + kq);
 
@@ -131,12 +131,13 @@ void skinny_gemm_kernel(GemmArgs g) {
             f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
     __syncthreads();
 
-    // sum the 4 wave partials in wave order and write rows < M, columns < N
+    // sum the wave partials in wave order and write rows < M, columns < N
+    if (tid >= 256) return;                       // 16 rows x 16 column groups
     const int i = tid >> 4;
     const int c4 = (tid & 15) * 4;
     f32x4 s4 = *reinterpret_cast<const f32x4*>(&red[0][i][c4]);
 #pragma unroll
-    for (int w = 1; w < 4; ++w) s4 += *reinterpret_cast<const f32x4*>(&red[w][i][c4]);
+    for (int w = 1; w < WAVES; ++w) s4 += *reinterpret_cast<const f32x4*>(&red[w][i][c4]);
     if (i < g.M) {
         float* crow = g.C + (int64_t)blockIdx.z * g.c_slice + (int64_t)i * g.ldc;
 #pragma unroll
@@ -145,16 +146,25 @@ void skinny_gemm_kernel(GemmArgs g) {
     }
 }
 
+template <int WAVES>
+hipError_t launch_waves(bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
+    dim3 grid((unsigned)g.tiles_n, 1, (unsigned)splits);
+    if (vec)
+        hipLaunchKernelGGL((skinny_gemm_kernel<true, WAVES>), grid, dim3(64 * WAVES), 0, stream, g);
+    else
+        hipLaunchKernelGGL((skinny_gemm_kernel<false, WAVES>), grid, dim3(64 * WAVES), 0, stream, g);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_skinny(int tile, bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
-    if (tile != 0) return hipErrorInvalidValue;
-    dim3 grid((unsigned)g.tiles_n, 1, (unsigned)splits);
-    if (vec)
-        hipLaunchKernelGGL(skinny_gemm_kernel<true>, grid, dim3(256), 0, stream, g);
-    else
-        hipLaunchKernelGGL(skinny_gemm_kernel<false>, grid, dim3(256), 0, stream, g);
-    return hipGetLastError();
+    switch (tile) {
+        case 0: return launch_waves<kSkinnyTiles[0].waves_n>(vec, g, splits, stream);
+        case 1: return launch_waves<kSkinnyTiles[1].waves_n>(vec, g, splits, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
+static_assert(kNumSkinnyTiles == 2, "launch_skinny covers every skinny tile");
 
 }  // namespace sgemm_impl
