@@ -82,10 +82,25 @@ constexpr double kMacRate = 128.0 * 2.4e9;   // FP32 MACs per second per CU at p
 constexpr double kPartialBw = 4e12;          // bytes/s for partial tiles (mostly cache resident)
 constexpr double kLaunch = 4e-6;             // one more dependent kernel launch
 
-// Share of the CU's peak one tile shape sustains when its CU is full.
-double mfma_efficiency(int tile) {
+// Share of the CU's peak one tile shape sustains when its CU is full, with
+// 16-byte (vec) or 4-byte loaders.  The register-staged 4-byte loaders need
+// more registers than the larger tiles leave and spill; the direct-to-LDS
+// tiles (8-10) stage nothing in registers.
+double mfma_efficiency(int tile, bool vec) {
+    if (!vec) {
+        switch (tile) {
+            case 8: case 9: return 0.86;
+            case 10: return 0.78;
+            case 2: return 0.75;
+            case 4: return 0.65;
+            default: return 0.60;
+        }
+    }
     switch (tile) {
+        case 8: return 0.91;
+        case 9: return 0.905;
         case 3: case 6: return 0.89;
+        case 10: return 0.87;
         case 0: case 1: case 7: return 0.85;
         case 2: case 5: return 0.83;
         default: return 0.70;
@@ -103,7 +118,7 @@ struct Candidate {
 };
 
 // One tile per workgroup, K split into `splits` slices.
-Candidate tiles_candidate(int tile, int64_t M, int64_t N, int64_t K, int64_t splits) {
+Candidate tiles_candidate(int tile, bool vec, int64_t M, int64_t N, int64_t K, int64_t splits) {
     const TileShape& t = kMfmaTiles[tile];
     Candidate c;
     c.tile = tile;
@@ -116,7 +131,7 @@ Candidate tiles_candidate(int tile, int64_t M, int64_t N, int64_t K, int64_t spl
     const int64_t wgs = tiles * c.splits;
     const int64_t full_waves = wgs / (kNumCUs * per_cu);
     const int64_t tail = wgs - full_waves * kNumCUs * per_cu;
-    const double wg_time = (double)t.bm * t.bn * c.k_chunk * per_cu / (kMacRate * mfma_efficiency(tile));
+    const double wg_time = (double)t.bm * t.bn * c.k_chunk * per_cu / (kMacRate * mfma_efficiency(tile, vec));
     // a tail of at most one workgroup per CU runs alone on its CU (about 0.8 of the shared time)
     double tail_time = 0;
     if (tail > 0) tail_time = (tail <= kNumCUs && per_cu > 1) ? wg_time * 0.8 / per_cu * 1.25 : wg_time;
@@ -127,7 +142,7 @@ Candidate tiles_candidate(int tile, int64_t M, int64_t N, int64_t K, int64_t spl
 
 // Stream-K on a persistent grid of one wave of workgroups: all but the last
 // full wave of tiles data-parallel, the rest shared out evenly by K-steps.
-Candidate streamk_candidate(int tile, int64_t M, int64_t N, int64_t K) {
+Candidate streamk_candidate(int tile, bool vec, int64_t M, int64_t N, int64_t K) {
     const TileShape& t = kMfmaTiles[tile];
     Candidate c;
     c.tile = tile;
@@ -141,7 +156,7 @@ Candidate streamk_candidate(int tile, int64_t M, int64_t N, int64_t K) {
     c.sk_tiles = tiles - c.dp_tiles;
     const int64_t units = c.sk_tiles * c.k_steps;
     c.sk_ipw = cdiv(units, grid);
-    const double step_time = (double)t.bm * t.bn * t.bk * wgs_per_cu(t) / (kMacRate * mfma_efficiency(tile));
+    const double step_time = (double)t.bm * t.bn * t.bk * wgs_per_cu(t) / (kMacRate * mfma_efficiency(tile, vec));
     c.time = (double)(c.dp_tiles / grid) * c.k_steps * step_time + c.sk_ipw * step_time;
     // partial tiles: count the workgroup ranges' segments that do not cover a
     // whole tile; each is written to a slot and read back once
@@ -252,26 +267,26 @@ sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
     } else if (path == SGEMM_PATH_MFMA) {
         std::vector<int> cands;
         if (o.tile >= 0) cands.push_back(o.tile);
-        else cands = {3, 0, 1, 2, 5, 4};
+        else cands = {8, 3, 10, 0, 1, 2, 5, 4};
         bool have = false;
         for (int tile : cands) {
             std::vector<Candidate> cs;
             if (o.decomposition != SGEMM_DECOMP_STREAM_K) {
                 if (o.split_k > 0) {
-                    cs.push_back(tiles_candidate(tile, M, N, K, o.split_k));
+                    cs.push_back(tiles_candidate(tile, q.vector, M, N, K, o.split_k));
                 } else {
                     const TileShape& t = kMfmaTiles[tile];
                     const int64_t tiles = cdiv(M, t.bm) * cdiv(N, t.bn);
                     const int64_t slots = (int64_t)kNumCUs * wgs_per_cu(t);
-                    cs.push_back(tiles_candidate(tile, M, N, K, 1));
+                    cs.push_back(tiles_candidate(tile, q.vector, M, N, K, 1));
                     if (tiles < slots) {
                         int64_t s = 1, kc = K;
                         choose_split(tiles, K, t.bk, slots, 32, &s, &kc);
-                        cs.push_back(tiles_candidate(tile, M, N, K, s));
+                        cs.push_back(tiles_candidate(tile, q.vector, M, N, K, s));
                     }
                 }
             }
-            if (o.decomposition != SGEMM_DECOMP_TILES && o.split_k <= 1) cs.push_back(streamk_candidate(tile, M, N, K));
+            if (o.decomposition != SGEMM_DECOMP_TILES && o.split_k <= 1) cs.push_back(streamk_candidate(tile, q.vector, M, N, K));
             for (const Candidate& c : cs) {
                 if (!have || c.time < best.time) {
                     best = c;

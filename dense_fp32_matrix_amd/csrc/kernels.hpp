@@ -58,7 +58,9 @@ struct TileShape {
     int bm, bn, bk;
     int waves_m, waves_n;   // waves per workgroup along M and N
     int waves_per_simd;     // occupancy the register budget is sized for
-    int sched = 1;          // 1: interleave LDS and global memory instructions between MFMAs
+    int sched = 1;          // >= 1: interleave LDS and global memory instructions between MFMAs,
+                            // with 8 * (sched - 1) MFMAs after the last LDS write of a K-step
+    int dtl = 0;            // > 0: stages of the direct-to-LDS loader (16-byte aligned operands)
 };
 
 constexpr TileShape kMfmaTiles[] = {
@@ -70,6 +72,9 @@ constexpr TileShape kMfmaTiles[] = {
     {128, 128, 32, 2, 2, 2, 0},   // 5: medium, deeper K-step
     {256, 256, 32, 2, 2, 1, 1},   // 6: as 3 with a deeper K-step (half the barriers)
     {128, 256, 16, 2, 2, 2, 1},   // 7: as 1, interleaved schedule
+    {256, 256, 16, 2, 2, 1, 1, 3},   // 8: as 3, direct-to-LDS loads, three stages
+    {256, 256, 16, 2, 2, 1, 1, 4},   // 9: as 3, direct-to-LDS loads, four stages
+    {256, 128, 16, 2, 2, 2, 0, 3},   // 10: as 0, direct-to-LDS loads, three stages
 };
 constexpr int kNumMfmaTiles = sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]);
 

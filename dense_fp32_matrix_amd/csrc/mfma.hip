@@ -57,6 +57,11 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
 template <int BM, int BN, int BK, int WGM, int WGN, bool VEC>
 struct MfmaCfg {
     static constexpr int T = 64 * WGM * WGN;
@@ -101,7 +106,7 @@ __device__ __forceinline__ int a_swizzle(int r) {
 // constant arguments, hence the recursion over template parameters.
 constexpr int kMaskMfma = 0x008, kMaskVmemRead = 0x020, kMaskDsRead = 0x100, kMaskDsWrite = 0x200;
 
-template <int I, int NM, int NR, int NV, int EXTRA_MASK>
+template <int I, int NM, int NR, int NV, int EXTRA_MASK, int TAIL>
 __device__ __forceinline__ void interleave_group() {
     if constexpr (I < NM) {
         __builtin_amdgcn_sched_group_barrier(kMaskMfma, 1, 0);
@@ -110,19 +115,22 @@ __device__ __forceinline__ void interleave_group() {
         } else if constexpr (EXTRA_MASK == kMaskVmemRead) {
             if constexpr (I - NR < NV) __builtin_amdgcn_sched_group_barrier(EXTRA_MASK, 1, 0);
         } else if constexpr (EXTRA_MASK == kMaskDsWrite) {
-            // LDS writes go last, as far as possible from the loads they wait for
-            if constexpr (I >= NM - NV) __builtin_amdgcn_sched_group_barrier(EXTRA_MASK, 1, 0);
+            // LDS writes late in the group, far from the loads they wait for,
+            // with TAIL MFMAs left after them to cover the writes' latency
+            // before the barrier
+            if constexpr (I >= NM - NV - TAIL && I < NM - TAIL)
+                __builtin_amdgcn_sched_group_barrier(EXTRA_MASK, 1, 0);
         }
-        interleave_group<I + 1, NM, NR, NV, EXTRA_MASK>();
+        interleave_group<I + 1, NM, NR, NV, EXTRA_MASK, TAIL>();
     }
 }
 
-template <int NM, int NR, int NV, int KG, int G = 0>
+template <int NM, int NR, int NV, int KG, int TAIL, int G = 0>
 __device__ __forceinline__ void interleave_hints() {
     if constexpr (G < KG) {
         constexpr int extra = G == 0 ? kMaskVmemRead : (G == KG - 1 ? kMaskDsWrite : 0);
-        interleave_group<0, NM, NR, NV, extra>();
-        interleave_hints<NM, NR, NV, KG, G + 1>();
+        interleave_group<0, NM, NR, NV, extra, TAIL>();
+        interleave_hints<NM, NR, NV, KG, TAIL, G + 1>();
     }
 }
 
@@ -309,12 +317,276 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& g, float* smem, int tm
                 mfmas(kg & 1);
             }
             store(cur ^ 1);
-            if constexpr (SCHED) interleave_hints<P::MB * P::NB * 4, P::MB + 2 * P::NB, AN + BNL, P::KG>();
+            // SCHED = 1 + (MFMAs left after the LDS writes) / 8
+            if constexpr (SCHED) interleave_hints<P::MB * P::NB * 4, P::MB + 2 * P::NB, AN + BNL, P::KG, 8 * (SCHED - 1)>();
         }
         mfmas(1);                            // last group of the last step
     }
 
     // ---- epilogue: overwrite the destination (masked at its edges) ----
+#pragma unroll
+    for (int mb = 0; mb < P::MB; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < P::NB; ++nb) {
+            const int j = o.col0 + wn * P::WN + nb * 32 + l32;
+            const int ib = o.row0 + wm * P::WM + mb * 32 + 4 * lh;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = ib + 8 * (r >> 2) + (r & 3);
+                if (i < o.row_lim && j < o.col_lim) o.out[(int64_t)i * o.ldo + j] = acc[mb][nb][r];
+            }
+        }
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant of one output tile.
+//
+// gfx950's global_load_lds_dwordx4 moves 16 bytes per lane from global
+// memory straight into LDS: lane l of a wave lands at (wave-uniform base) +
+// 16 * l, so one instruction fills 1 KB of LDS in lane order while the
+// source address of each lane is free.  global_load_lds_dword does the same
+// with 4 bytes per lane (256 B per instruction); it serves operands whose
+// rows are not 16-byte aligned and builds exactly the same stage layout.  That removes the staging registers
+// and the LDS write instructions of the register-staged pipeline (the
+// direct global -> shared copy that "GEMM from naive to tiled" section 六.2
+// describes for cp.async, and the register-free prefetch of "SGEMM 纯 CUDA
+// 优化总结" Q10), and lets DS stages of LDS be in flight at once:
+//   * A stage [BM][BK]: an instruction fills whole rows, and the lane that
+//     lands in physical 4-float chunk c of row r fetches logical chunk
+//     c ^ swz(r), so the swizzled layout of the register-staged path is
+//     produced as is;
+//   * B stage: blocks of R = 256 / BN whole rows (1 KB, one 16-byte-lane
+//     instruction or four 4-byte-lane ones), GS floats apart, GS chosen so
+//     that the fragment reads of rows k and k + 4 (the two lane halves) fall
+//     32 banks apart.
+// Schedule: the loads of step s + DS - 1 are issued during step s into the
+// stage that step s - 1 used; each wave waits (vmcnt) until its own loads
+// of step s have landed, and the barrier makes every wave's part visible.
+// The stages are separate __shared__ arrays and the loop is unrolled by DS,
+// so each access names its stage statically.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glb_void_t;
+
+template <int BM, int BN, int BK, int WGM, int WGN, int W>
+struct DtlCfg {
+    static_assert(W == 4 || W == 1, "16-byte or 4-byte lanes");
+    static constexpr int WAVES = WGM * WGN;
+    static constexpr int SEG = 64 * W;                    // floats one instruction writes
+    static constexpr int A_INSTR = BM * BK / SEG;
+    static constexpr int A_PER_WAVE = A_INSTR / WAVES;
+    static constexpr int B_ROWS = 256 / BN;               // B rows per 1 KB block (R)
+    static constexpr int B_GS = B_ROWS == 1 ? BN + 8 : B_ROWS * BN + 16;   // floats between blocks
+    static constexpr int B_SEGS = 256 / SEG;              // instructions per block
+    static constexpr int B_INSTR = BK / B_ROWS * B_SEGS;
+    static constexpr int B_PER_WAVE = B_INSTR / WAVES;
+    static constexpr int A_STAGE = BM * BK;
+    static constexpr int B_STAGE = BK / B_ROWS * B_GS;
+    static constexpr int STAGE = A_STAGE + B_STAGE;
+    static constexpr int LOADS = A_PER_WAVE + B_PER_WAVE;  // per lane per K-step
+    static_assert(BN == 128 || BN == 256, "B blocks hold one or two rows");
+    static_assert(SEG % BK == 0, "an A instruction fills whole rows");
+    static_assert(A_PER_WAVE * WAVES == A_INSTR && B_PER_WAVE * WAVES == B_INSTR, "instructions per wave");
+    static_assert((4 / B_ROWS) * B_GS % 64 == 32, "lane halves of a B fragment read 32 banks apart");
+    // B row k of a stage starts at this float offset
+    static __device__ __forceinline__ int b_row(int k) { return A_STAGE + (k / B_ROWS) * B_GS + (k % B_ROWS) * BN; }
+};
+
+// Floats per stage of the direct-to-LDS layout (the same for both lane
+// widths; only instantiated when used).
+template <bool ON, int BM, int BN, int BK, int WGM, int WGN>
+struct DtlStageFloats {
+    static constexpr int value = 4;
+};
+template <int BM, int BN, int BK, int WGM, int WGN>
+struct DtlStageFloats<true, BM, BN, BK, WGM, WGN> {
+    static constexpr int value = DtlCfg<BM, BN, BK, WGM, WGN, 4>::STAGE;
+};
+
+// s_waitcnt that waits for vmcnt <= N and nothing else (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Barrier for the direct-to-LDS pipeline: wait until at most N of this
+// wave's direct loads are outstanding and all its LDS reads have returned,
+// then s_barrier.  Written as one asm statement with a memory clobber: the
+// workgroup fence of __syncthreads() would also wait for the loads that are
+// meant to stay in flight.
+template <int N>
+__device__ __forceinline__ void dtl_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// One direct load of W floats per lane from src to LDS byte address
+// lds + 4 * W * lane.  Issued as asm so that the compiler's LDS-DMA
+// tracking, which cannot tell the stages apart across the unrolled loop and
+// would wait for every load in flight, stays out of it: dtl_barrier's
+// explicit vmcnt is the only wait.  M0 holds the LDS base; the s_nop is the
+// wait state the hardware needs between an M0 write and an LDS DMA reading it.
+template <int W>
+__device__ __forceinline__ void dma_lanes(const float* src, const float* lds) {
+    const uint32_t base = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+    if constexpr (W == 4)
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base));
+    else
+        asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(base));
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, int SCHED, int DS, int W>
+__device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, float* st1, float* st2, float* st3,
+                                              int tm, int tn, int kb, int ke, const TileOut& o) {
+    float* const stg[4] = {st0, st1, st2, st3};
+    using P = MfmaCfg<BM, BN, BK, WGM, WGN, true>;
+    using Q = DtlCfg<BM, BN, BK, WGM, WGN, W>;
+    static_assert(DS == 3 || DS == 4, "three or four stages");
+    static_assert((DS - 2) * Q::LOADS < 64, "loads in flight fit the vmcnt counter");
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WGN;
+    const int wn = wave % WGN;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int steps = (ke - kb + BK - 1) / BK;
+
+    // Per-lane sources, fixed over the K loop.  Instruction `ins` fills the
+    // stage floats [ins * SEG, (ins + 1) * SEG) of A, or SEG floats of one B
+    // block, W floats per lane in lane order; each lane fetches the
+    // element(s) that belong at its position.
+    int64_t a_off[Q::A_PER_WAVE];
+    int a_kc[Q::A_PER_WAVE];
+    bool a_rok[Q::A_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < Q::A_PER_WAVE; ++i) {
+        const int p = (i * Q::WAVES + wave) * Q::SEG + W * lane;
+        const int row = p / BK;
+        const int k = 4 * (((p % BK) / 4) ^ a_swizzle<BK>(row)) + p % 4;
+        a_rok[i] = m0 + row < g.M;
+        a_off[i] = (int64_t)(a_rok[i] ? m0 + row : 0) * g.lda + k;
+        a_kc[i] = k;
+    }
+    int64_t b_off[Q::B_PER_WAVE];
+    int b_kr[Q::B_PER_WAVE];
+    bool b_cok[Q::B_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < Q::B_PER_WAVE; ++i) {
+        const int ins = i * Q::WAVES + wave;
+        const int f = (ins % Q::B_SEGS) * Q::SEG + W * lane;    // float within the block
+        const int row = ins / Q::B_SEGS * Q::B_ROWS + f / BN;
+        const int col = f % BN;
+        b_cok[i] = n0 + col < g.N;
+        b_off[i] = (int64_t)row * g.ldb + (b_cok[i] ? n0 + col : 0);
+        b_kr[i] = row;
+    }
+
+    // direct load d (A loads first, then B) of K-step `step` into stage `st`
+    auto issue_one = [&](int step, float* st, int d) {
+        const int k0 = kb + step * BK;
+        if (d < Q::A_PER_WAVE) {
+            const bool ok = a_rok[d] && (k0 + a_kc[d] < ke);
+            dma_lanes<W>(ok ? g.A + k0 + a_off[d] : kZeroMfma, st + (d * Q::WAVES + wave) * Q::SEG);
+        } else {
+            const int i = d - Q::A_PER_WAVE;
+            const int ins = i * Q::WAVES + wave;
+            const bool ok = b_cok[i] && (k0 + b_kr[i] < ke);
+            dma_lanes<W>(ok ? g.B + (int64_t)k0 * g.ldb + b_off[i] : kZeroMfma,
+                         st + Q::A_STAGE + ins / Q::B_SEGS * Q::B_GS + ins % Q::B_SEGS * Q::SEG);
+        }
+    };
+    auto issue = [&](int step, float* st) {
+#pragma unroll
+        for (int d = 0; d < Q::LOADS; ++d) issue_one(step, st, d);
+    };
+
+    f32x16 acc[P::MB][P::NB];
+#pragma unroll
+    for (int mb = 0; mb < P::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < P::NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
+
+    const int l32 = lane & 31;
+    const int lh = lane >> 5;
+    int a_frag[P::KG][P::MB];
+#pragma unroll
+    for (int mb = 0; mb < P::MB; ++mb) {
+        const int row = wm * P::WM + mb * 32 + l32;
+        const int sw = a_swizzle<BK>(row);
+#pragma unroll
+        for (int kg = 0; kg < P::KG; ++kg) a_frag[kg][mb] = row * BK + 4 * ((2 * kg + lh) ^ sw);
+    }
+    const int b_col = wn * P::WN + l32;
+
+    f32x4 fa[2][P::MB];
+    float fb[2][P::NB][4];
+    auto read_frags = [&](const float* st, int kg, int set) {
+#pragma unroll
+        for (int mb = 0; mb < P::MB; ++mb) fa[set][mb] = *reinterpret_cast<const f32x4*>(st + a_frag[kg][mb]);
+#pragma unroll
+        for (int nb = 0; nb < P::NB; ++nb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) fb[set][nb][q] = st[Q::b_row(8 * kg + 4 * lh + q) + b_col + nb * 32];
+    };
+    auto mfmas = [&](int set) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int mb = 0; mb < P::MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < P::NB; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[set][mb][q], fb[set][nb][q],
+                                                                       acc[mb][nb], 0, 0, 0);
+    };
+    if (steps > 0) {
+#pragma unroll
+        for (int j = 0; j + 1 < DS; ++j) issue(j, stg[j]);
+        dtl_barrier<(DS - 2) * Q::LOADS>();
+        read_frags(stg[0], 0, 0);
+        issue(DS - 1, stg[DS - 1]);
+#pragma unroll
+        for (int kg = 0; kg + 1 < P::KG; ++kg) {
+            read_frags(stg[0], kg + 1, (kg + 1) & 1);
+            mfmas(kg & 1);
+        }
+        // iteration s uses stage s % DS and refills stage (s - 1) % DS
+        auto iter = [&](int s, auto j_tag) {
+            constexpr int J = decltype(j_tag)::value;
+            dtl_barrier<(DS - 2) * Q::LOADS>();
+            read_frags(stg[J], 0, 0);
+            mfmas(1);
+            issue(s + DS - 1, stg[(J + DS - 1) % DS]);
+#pragma unroll
+            for (int kg = 0; kg + 1 < P::KG; ++kg) {
+                read_frags(stg[J], kg + 1, (kg + 1) & 1);
+                mfmas(kg & 1);
+            }
+            if constexpr (SCHED)
+                interleave_hints<P::MB * P::NB * 4, P::MB + 2 * P::NB, 0, P::KG, 8 * (SCHED - 1)>();
+        };
+        int s = 1;
+        while (true) {
+            if (s >= steps) break;
+            iter(s++, IntC<1 % DS>{});
+            if (s >= steps) break;
+            iter(s++, IntC<2 % DS>{});
+            if (s >= steps) break;
+            iter(s++, IntC<3 % DS>{});
+            if constexpr (DS == 4) {
+                if (s >= steps) break;
+                iter(s++, IntC<0>{});
+            }
+        }
+        mfmas(1);
+        wait_vmcnt<0>();                     // loads issued past the end land before the LDS is reused
+    }
+
 #pragma unroll
     for (int mb = 0; mb < P::MB; ++mb) {
 #pragma unroll
@@ -343,25 +615,38 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& g, float* smem, int tm
 //    and the stream-K fix-up kernel sums the slots of each tile in range
 //    order.  The cut depends only on the shapes, so the sums always happen in
 //    the same order (the work-splitting of "GEMM from naive to tiled", 十.1).
-template <int BM, int BN, int BK, int WGM, int WGN, bool VEC, int WPE, int SCHED>
+template <int BM, int BN, int BK, int WGM, int WGN, bool VEC, int WPE, int SCHED, int DS>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void mfma_gemm_kernel(GemmArgs g) {
     using P = MfmaCfg<BM, BN, BK, WGM, WGN, VEC>;
-    __shared__ __attribute__((aligned(16))) float smem[2 * P::STAGE];
+    // LDS: two stages for the register-staged loader, or DSE separate stage
+    // arrays for the direct-to-LDS loader (16-byte lanes when the operands
+    // are 16-byte aligned, else 4-byte lanes, which keep three stages so
+    // that the loads in flight fit the vmcnt counter)
+    constexpr bool DTL = DS > 0;
+    constexpr int DSE = VEC ? DS : 3;
+    constexpr int W = VEC ? 4 : 1;
+    constexpr int QS = DtlStageFloats<DTL, BM, BN, BK, WGM, WGN>::value;
+    __shared__ __attribute__((aligned(16))) float lds0[DTL ? QS : 2 * P::STAGE];
+    __shared__ __attribute__((aligned(16))) float lds1[DTL ? QS : 4];
+    __shared__ __attribute__((aligned(16))) float lds2[DTL ? QS : 4];
+    __shared__ __attribute__((aligned(16))) float lds3[DTL && DSE > 3 ? QS : 4];
     int tm, tn;
     if (g.sk_iters == 0) {
         tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
         const int kb = blockIdx.z * g.k_chunk;
         const int ke = min(g.K, kb + g.k_chunk);
         const TileOut o{g.C + (int64_t)blockIdx.z * g.c_slice, g.ldc, tm * BM, tn * BN, g.M, g.N};
-        mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, smem, tm, tn, kb, ke, o);
+        if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W>(g, lds0, lds1, lds2, lds3, tm, tn, kb, ke, o);
+        else mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, lds0, tm, tn, kb, ke, o);
         return;
     }
     for (int t = blockIdx.x; t < g.dp_tiles; t += gridDim.x) {
         tile_coords(t, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
         const TileOut o{g.C, g.ldc, tm * BM, tn * BN, g.M, g.N};
-        mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, smem, tm, tn, 0, g.K, o);
+        if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W>(g, lds0, lds1, lds2, lds3, tm, tn, 0, g.K, o);
+        else mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, lds0, tm, tn, 0, g.K, o);
         __syncthreads();                 // the next tile's prologue overwrites LDS
     }
     int64_t it = (int64_t)blockIdx.x * g.sk_ipw;
@@ -376,11 +661,13 @@ void mfma_gemm_kernel(GemmArgs g) {
         const int ke = min(g.K, ks1 * BK);
         if (ks0 == 0 && ks1 == g.k_steps) {
             const TileOut o{g.C, g.ldc, tm * BM, tn * BN, g.M, g.N};
-            mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, smem, tm, tn, kb, ke, o);
+            if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W>(g, lds0, lds1, lds2, lds3, tm, tn, kb, ke, o);
+        else mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, lds0, tm, tn, kb, ke, o);
         } else {
             float* slot = g.ws + (int64_t)(2 * blockIdx.x + which) * (BM * BN);
             const TileOut o{slot, BN, 0, 0, BM, BN};
-            mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, smem, tm, tn, kb, ke, o);
+            if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W>(g, lds0, lds1, lds2, lds3, tm, tn, kb, ke, o);
+        else mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, lds0, tm, tn, kb, ke, o);
         }
         __syncthreads();
         which = 1;
@@ -388,15 +675,15 @@ void mfma_gemm_kernel(GemmArgs g) {
     }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int WPE, int SCHED>
+template <int BM, int BN, int BK, int WGM, int WGN, int WPE, int SCHED, int DS>
 hipError_t launch_one(bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
     dim3 grid(g.sk_iters > 0 ? (unsigned)g.sk_grid : (unsigned)((int64_t)g.tiles_m * g.tiles_n), 1,
               g.sk_iters > 0 ? 1u : (unsigned)splits);
     dim3 block(64 * WGM * WGN);
     if (vec)
-        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, true, WPE, SCHED>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, true, WPE, SCHED, DS>), grid, block, 0, stream, g);
     else
-        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, false, WPE, SCHED>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, false, WPE, SCHED, DS>), grid, block, 0, stream, g);
     return hipGetLastError();
 }
 
@@ -407,7 +694,7 @@ hipError_t launch_mfma(int tile, bool vec, const GemmArgs& g, int splits, hipStr
     case ID:                                                                                    \
         return launch_one<kMfmaTiles[ID].bm, kMfmaTiles[ID].bn, kMfmaTiles[ID].bk,             \
                           kMfmaTiles[ID].waves_m, kMfmaTiles[ID].waves_n,                      \
-                          kMfmaTiles[ID].waves_per_simd, kMfmaTiles[ID].sched>(vec, g, splits, stream);
+                          kMfmaTiles[ID].waves_per_simd, kMfmaTiles[ID].sched, kMfmaTiles[ID].dtl>(vec, g, splits, stream);
     switch (tile) {
         SGEMM_MFMA_CASE(0)
         SGEMM_MFMA_CASE(1)
@@ -417,11 +704,14 @@ hipError_t launch_mfma(int tile, bool vec, const GemmArgs& g, int splits, hipStr
         SGEMM_MFMA_CASE(5)
         SGEMM_MFMA_CASE(6)
         SGEMM_MFMA_CASE(7)
+        SGEMM_MFMA_CASE(8)
+        SGEMM_MFMA_CASE(9)
+        SGEMM_MFMA_CASE(10)
         default:
             return hipErrorInvalidValue;
     }
 #undef SGEMM_MFMA_CASE
 }
-static_assert(kNumMfmaTiles == 8, "launch_mfma covers every MFMA tile");
+static_assert(kNumMfmaTiles == 11, "launch_mfma covers every MFMA tile");
 
 }  // namespace sgemm_impl
