@@ -37,6 +37,7 @@ def parse():
     ap.add_argument("--tile", type=int, default=-1)
     ap.add_argument("--split-k", type=int, default=0)
     ap.add_argument("--decomposition", default="auto")
+    ap.add_argument("--pack", default="auto", choices=["auto", "never", "always"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time of the oracle sample (0 = skip the CPU baseline)")
     ap.add_argument("--flush-mib", type=int, default=1024,
@@ -117,9 +118,9 @@ def main():
     B = B_host.to(dev)
     C = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
     opts = {}
-    if args.path != "auto" or args.tile >= 0 or args.split_k or args.decomposition != "auto":
+    if args.path != "auto" or args.tile >= 0 or args.split_k or args.decomposition != "auto" or args.pack != "auto":
         opts = {"path": args.path, "tile": args.tile, "split_k": args.split_k,
-                "decomposition": args.decomposition}
+                "decomposition": args.decomposition, "pack": args.pack}
     plan = lib.sgemm_plan_query(w.M, w.N, w.K, A.data_ptr(), w.lda, B.data_ptr(), w.ldb, C.data_ptr(), w.N,
                                 **opts)
 

@@ -13,7 +13,7 @@ import os
 from typing import Optional
 
 __all__ = [
-    "SgemmError", "PATHS", "DECOMPOSITIONS", "sgemm", "sgemm_ex", "sgemm_raw", "sgemm_plan_query", "sgemm_workspace_size",
+    "SgemmError", "PATHS", "DECOMPOSITIONS", "PACK", "sgemm", "sgemm_ex", "sgemm_raw", "sgemm_plan_query", "sgemm_workspace_size",
     "sgemm_tile_info", "sgemm_status_string", "sgemm_version", "library_path", "load_library",
 ]
 
@@ -41,7 +41,7 @@ _DECOMP_NAMES = {v: k for k, v in DECOMPOSITIONS.items()}
 
 class _Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("tile", ctypes.c_int32), ("split_k", ctypes.c_int32),
-                ("vector", ctypes.c_int32), ("decomposition", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("vector", ctypes.c_int32), ("decomposition", ctypes.c_int32), ("pack", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -52,7 +52,7 @@ class _Plan(ctypes.Structure):
                 ("tiles_n", ctypes.c_int64), ("k_chunk", ctypes.c_int64), ("workgroups", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_size_t), ("launches", ctypes.c_int32),
                 ("decomposition", ctypes.c_int32), ("dp_tiles", ctypes.c_int64), ("sk_tiles", ctypes.c_int64),
-                ("sk_units_per_wg", ctypes.c_int64)]
+                ("sk_units_per_wg", ctypes.c_int64), ("packed", ctypes.c_int32), ("k_padded", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -88,9 +88,13 @@ def load_library():
     return lib
 
 
+PACK = {"auto": 0, "never": 1, "always": 2}
+
+
 def _options(path="auto", tile=-1, split_k=0, vector=0, decomposition="auto", workspace=None,
-             workspace_bytes=0) -> _Options:
+             workspace_bytes=0, pack="auto") -> _Options:
     o = _Options()
+    o.pack = PACK[pack] if isinstance(pack, str) else int(pack)
     o.path = PATHS[path] if isinstance(path, str) else int(path)
     o.tile = int(tile)
     o.split_k = int(split_k)
@@ -164,11 +168,12 @@ def sgemm(A, B, C=None, stream=None):
 
 
 def sgemm_ex(A, B, C=None, stream=None, *, path="auto", tile=-1, split_k=0, vector=0, decomposition="auto",
-             workspace=None):
+             workspace=None, pack="auto"):
     """``sgemm`` with explicit options: ``path`` in PATHS, ``tile`` index, ``split_k``
     slices, ``vector=1`` to force 4-byte loads, ``decomposition`` in DECOMPOSITIONS,
-    optional ``workspace`` tensor."""
-    return _call(A, B, C, stream, _options(path, tile, split_k, vector, decomposition, workspace))
+    ``pack`` in PACK (aligned copies of misaligned operands), optional ``workspace``
+    tensor."""
+    return _call(A, B, C, stream, _options(path, tile, split_k, vector, decomposition, workspace, pack=pack))
 
 
 def sgemm_plan_query(M, N, K, A=0x100000, lda=None, B=0x200000000, ldb=None, C=0x400000000, ldc=None,

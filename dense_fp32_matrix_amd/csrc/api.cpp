@@ -48,6 +48,11 @@ struct Plan {
     sgemm_plan pub;
     int64_t ldw = 0;       // split-K workspace leading dimension (floats)
     int64_t k_steps = 0;   // stream-K: K-steps per tile
+    bool second = false;   // a split-K reduce or stream-K fix-up follows the matrix kernel
+    // packing: the matrix kernel reads A' (M x kp, leading dimension kp) and
+    // B' (kp x np, leading dimension np) from the workspace at these offsets
+    int64_t kp = 0, np = 0;
+    size_t pack_a_off = 0, pack_b_off = 0, gemm_ws_off = 0;
 };
 
 const TileShape& tile_of(int path, int tile) {
@@ -89,11 +94,11 @@ constexpr double kLaunch = 4e-6;             // one more dependent kernel launch
 double mfma_efficiency(int tile, bool vec) {
     if (!vec) {
         switch (tile) {
-            case 8: case 9: return 0.86;
-            case 10: return 0.78;
-            case 2: return 0.75;
-            case 4: return 0.65;
-            default: return 0.60;
+            case 8: case 9: return 0.66;
+            case 10: return 0.58;
+            case 2: return 0.62;
+            case 4: return 0.60;
+            default: return 0.55;
         }
     }
     switch (tile) {
@@ -203,6 +208,44 @@ void choose_split(int64_t tiles, int64_t K, int bk, int64_t target_wgs, int64_t 
     *k_chunk = kc;
 }
 
+// Best MFMA plan for the given operand alignment (vec) and K.
+Candidate mfma_best(const sgemm_options& o, bool vec, int64_t M, int64_t N, int64_t K) {
+    std::vector<int> cands;
+    if (o.tile >= 0) cands.push_back(o.tile);
+    else cands = {8, 3, 10, 0, 1, 2, 5, 4};
+    Candidate best;
+    bool have = false;
+    for (int tile : cands) {
+        std::vector<Candidate> cs;
+        if (o.decomposition != SGEMM_DECOMP_STREAM_K) {
+            if (o.split_k > 0) {
+                cs.push_back(tiles_candidate(tile, vec, M, N, K, o.split_k));
+            } else {
+                const TileShape& t = kMfmaTiles[tile];
+                const int64_t tiles = cdiv(M, t.bm) * cdiv(N, t.bn);
+                const int64_t slots = (int64_t)kNumCUs * wgs_per_cu(t);
+                cs.push_back(tiles_candidate(tile, vec, M, N, K, 1));
+                if (tiles < slots) {
+                    int64_t s = 1, kc = K;
+                    choose_split(tiles, K, t.bk, slots, 32, &s, &kc);
+                    cs.push_back(tiles_candidate(tile, vec, M, N, K, s));
+                }
+            }
+        }
+        if (o.decomposition != SGEMM_DECOMP_TILES && o.split_k <= 1)
+            cs.push_back(streamk_candidate(tile, vec, M, N, K));
+        for (const Candidate& c : cs) {
+            if (!have || c.time < best.time) {
+                best = c;
+                have = true;
+            }
+        }
+    }
+    return best;
+}
+
+constexpr double kPackBw = 3e12;   // bytes/s read + written by the pack kernel
+
 sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
                        int64_t ldb, const float* C, int64_t ldc, const sgemm_options* opts, Plan* out) {
     sgemm_status st = validate(M, N, K, A, lda, B, ldb, C, ldc);
@@ -212,6 +255,7 @@ sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
     if (o.path < SGEMM_PATH_AUTO || o.path > SGEMM_PATH_SKINNY) return SGEMM_ERR_INVALID_ARG;
     if (o.split_k < 0 || o.vector < 0 || o.vector > 1) return SGEMM_ERR_INVALID_ARG;
     if (o.decomposition < SGEMM_DECOMP_AUTO || o.decomposition > SGEMM_DECOMP_STREAM_K) return SGEMM_ERR_INVALID_ARG;
+    if (o.pack < 0 || o.pack > 2) return SGEMM_ERR_INVALID_ARG;
     if (o.workspace != nullptr && !aligned(o.workspace, 256)) return SGEMM_ERR_INVALID_ARG;
 
     Plan p;
@@ -222,6 +266,7 @@ sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
     if (M == 0 || N == 0 || K == 0) {   // nothing to write, or the empty sum (C = 0)
         q.path = o.path == SGEMM_PATH_AUTO ? SGEMM_PATH_MFMA : o.path;
         q.launches = (M == 0 || N == 0) ? 0 : 1;
+        q.k_padded = (int32_t)K;
         *out = p;
         return SGEMM_OK;
     }
@@ -265,33 +310,28 @@ sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
         best.splits = cdiv(K, k_chunk);
         best.k_chunk = k_chunk;
     } else if (path == SGEMM_PATH_MFMA) {
-        std::vector<int> cands;
-        if (o.tile >= 0) cands.push_back(o.tile);
-        else cands = {8, 3, 10, 0, 1, 2, 5, 4};
-        bool have = false;
-        for (int tile : cands) {
-            std::vector<Candidate> cs;
-            if (o.decomposition != SGEMM_DECOMP_STREAM_K) {
-                if (o.split_k > 0) {
-                    cs.push_back(tiles_candidate(tile, q.vector, M, N, K, o.split_k));
-                } else {
-                    const TileShape& t = kMfmaTiles[tile];
-                    const int64_t tiles = cdiv(M, t.bm) * cdiv(N, t.bn);
-                    const int64_t slots = (int64_t)kNumCUs * wgs_per_cu(t);
-                    cs.push_back(tiles_candidate(tile, q.vector, M, N, K, 1));
-                    if (tiles < slots) {
-                        int64_t s = 1, kc = K;
-                        choose_split(tiles, K, t.bk, slots, 32, &s, &kc);
-                        cs.push_back(tiles_candidate(tile, q.vector, M, N, K, s));
-                    }
-                }
-            }
-            if (o.decomposition != SGEMM_DECOMP_TILES && o.split_k <= 1) cs.push_back(streamk_candidate(tile, q.vector, M, N, K));
-            for (const Candidate& c : cs) {
-                if (!have || c.time < best.time) {
-                    best = c;
-                    have = true;
-                }
+        best = mfma_best(o, q.vector != 0, M, N, K);
+        // Alternative: copy the misaligned operand(s) into aligned, zero-padded
+        // workspace first and run the 16-byte loaders.  K not a multiple of 4
+        // pads K, which both operands must then carry.
+        if (!vec_ok && o.vector == 0 && o.pack != 1) {
+            const bool a_ok = aligned(A, 16) && lda % 4 == 0;
+            const bool b_ok = aligned(B, 16) && ldb % 4 == 0 && N % 4 == 0;
+            const int64_t kp = round_up(K, 4);
+            const bool pack_a = !a_ok || kp != K;
+            const bool pack_b = !b_ok || kp != K;
+            const int64_t np = pack_b ? round_up(N, 4) : N;
+            double bytes = 0;
+            if (pack_a) bytes += 4.0 * (M * K + M * kp);
+            if (pack_b) bytes += 4.0 * (K * N + kp * np);
+            Candidate c = mfma_best(o, true, M, N, kp);
+            c.time += bytes / kPackBw + (pack_a + pack_b) * kLaunch;
+            if (o.pack == 2 || c.time < best.time) {
+                best = c;
+                q.vector = 1;
+                q.packed = (pack_a ? 1 : 0) | (pack_b ? 2 : 0);
+                p.kp = kp;
+                p.np = np;
             }
         }
     } else {   // VALU
@@ -321,17 +361,20 @@ sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
     q.tiles_n = cdiv(N, t.bn);
     q.decomposition = best.decomposition;
     if (q.tiles_m * q.tiles_n * (int64_t)q.threads >= (int64_t(1) << 32)) return SGEMM_ERR_UNSUPPORTED;
+    const int64_t kg = q.packed ? p.kp : K;     // K as the matrix kernel sees it
+    q.k_padded = (int32_t)kg;
+    size_t gemm_ws = 0;
     if (best.decomposition == SGEMM_DECOMP_STREAM_K) {
         q.split_k = 1;
-        q.k_chunk = K;
+        q.k_chunk = kg;
         q.workgroups = best.grid;
         q.dp_tiles = best.dp_tiles;
         q.sk_tiles = best.sk_tiles;
         q.sk_units_per_wg = best.sk_ipw;
         p.k_steps = best.k_steps;
         const bool splits_tiles = best.sk_ipw % best.k_steps != 0 || best.sk_ipw < best.k_steps;
-        q.workspace_bytes = splits_tiles ? (size_t)(2 * best.grid) * t.bm * t.bn * sizeof(float) : 0;
-        q.launches = splits_tiles ? 2 : 1;
+        gemm_ws = splits_tiles ? (size_t)(2 * best.grid) * t.bm * t.bn * sizeof(float) : 0;
+        p.second = splits_tiles;
     } else {
         if (best.splits > 65535) return SGEMM_ERR_UNSUPPORTED;
         q.split_k = (int32_t)best.splits;
@@ -339,12 +382,24 @@ sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
         q.workgroups = q.tiles_m * q.tiles_n * best.splits;
         if (best.splits > 1) {
             p.ldw = round_up(N, 4);
-            q.workspace_bytes = (size_t)(best.splits * M * p.ldw * (int64_t)sizeof(float));
-            q.launches = 2;
-        } else {
-            q.launches = 1;
+            gemm_ws = (size_t)(best.splits * M * p.ldw * (int64_t)sizeof(float));
+            p.second = true;
         }
     }
+    // workspace: [packed A][packed B][partials], each 256-byte aligned
+    auto align256 = [](size_t b) { return (b + 255) / 256 * 256; };
+    size_t off = 0;
+    if (q.packed & 1) {
+        p.pack_a_off = off;
+        off += align256((size_t)(M * p.kp) * sizeof(float));
+    }
+    if (q.packed & 2) {
+        p.pack_b_off = off;
+        off += align256((size_t)(p.kp * p.np) * sizeof(float));
+    }
+    p.gemm_ws_off = off;
+    q.workspace_bytes = gemm_ws > 0 ? off + gemm_ws : off;
+    q.launches = ((q.packed & 1) ? 1 : 0) + ((q.packed & 2) ? 1 : 0) + 1 + (p.second ? 1 : 0);
     *out = p;
     return SGEMM_OK;
 }
@@ -376,13 +431,29 @@ sgemm_status run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, c
         }
     }
 
+    char* const wsb = static_cast<char*>(ws);
+    hipError_t e = hipSuccess;
+    if (q.packed & 1) {
+        float* Ap = reinterpret_cast<float*>(wsb + p.pack_a_off);
+        e = launch_pack(A, lda, (int32_t)M, (int32_t)K, Ap, (int32_t)M, (int32_t)p.kp, stream);
+        A = Ap;
+        lda = p.kp;
+    }
+    if (e == hipSuccess && (q.packed & 2)) {
+        float* Bp = reinterpret_cast<float*>(wsb + p.pack_b_off);
+        e = launch_pack(B, ldb, (int32_t)K, (int32_t)N, Bp, (int32_t)p.kp, (int32_t)p.np, stream);
+        B = Bp;
+        ldb = p.np;
+    }
+    void* const gws = q.workspace_bytes > p.gemm_ws_off ? static_cast<void*>(wsb + p.gemm_ws_off) : nullptr;
+
     GemmArgs g;
     std::memset(&g, 0, sizeof(g));
     g.A = A;
     g.B = B;
     g.M = (int32_t)M;
     g.N = (int32_t)N;
-    g.K = (int32_t)K;
+    g.K = q.k_padded;
     g.k_chunk = (int32_t)q.k_chunk;
     g.lda = lda;
     g.ldb = ldb;
@@ -399,25 +470,26 @@ sgemm_status run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, c
         g.k_steps = (int32_t)p.k_steps;
         g.sk_iters = q.sk_tiles * p.k_steps;
         g.sk_ipw = q.sk_units_per_wg;
-        g.ws = static_cast<float*>(ws);
+        g.ws = static_cast<float*>(gws);
     } else if (q.split_k > 1) {
-        g.C = static_cast<float*>(ws);
+        g.C = static_cast<float*>(gws);
         g.ldc = p.ldw;
         g.c_slice = M * p.ldw;
     }
 
-    hipError_t e;
-    switch (q.path) {
-        case SGEMM_PATH_NAIVE: e = launch_naive(g, stream); break;
-        case SGEMM_PATH_VALU: e = launch_valu(q.tile, q.vector != 0, g, q.split_k, stream); break;
-        case SGEMM_PATH_SKINNY: e = launch_skinny(q.tile, q.vector != 0, g, q.split_k, stream); break;
-        default: e = launch_mfma(q.tile, q.vector != 0, g, q.split_k, stream); break;
+    if (e == hipSuccess) {
+        switch (q.path) {
+            case SGEMM_PATH_NAIVE: e = launch_naive(g, stream); break;
+            case SGEMM_PATH_VALU: e = launch_valu(q.tile, q.vector != 0, g, q.split_k, stream); break;
+            case SGEMM_PATH_SKINNY: e = launch_skinny(q.tile, q.vector != 0, g, q.split_k, stream); break;
+            default: e = launch_mfma(q.tile, q.vector != 0, g, q.split_k, stream); break;
+        }
     }
-    if (e == hipSuccess && q.launches == 2) {
+    if (e == hipSuccess && p.second) {
         if (q.decomposition == SGEMM_DECOMP_STREAM_K)
             e = launch_streamk_fixup(g, q.bm, q.bn, (int)q.sk_tiles, stream);
         else
-            e = launch_splitk_reduce(static_cast<const float*>(ws), p.ldw, M * p.ldw, q.split_k, C, ldc,
+            e = launch_splitk_reduce(static_cast<const float*>(gws), p.ldw, M * p.ldw, q.split_k, C, ldc,
                                      (int32_t)M, (int32_t)N, stream);
     }
     if (owned) {

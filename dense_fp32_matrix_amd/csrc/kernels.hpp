@@ -112,6 +112,11 @@ hipError_t launch_streamk_fixup(const GemmArgs& g, int bm, int bn, int sk_tiles,
 // C[i][j] = +0.0 for i < M, j < N (the empty sum, K == 0).
 hipError_t launch_fill_zero(float* C, int64_t ldc, int32_t M, int32_t N, hipStream_t stream);
 
+// dst (rows_p x cols_p, leading dimension cols_p % 4 == 0, 16-byte aligned) =
+// src (rows x cols, leading dimension ld) zero-padded.
+hipError_t launch_pack(const float* src, int64_t ld, int32_t rows, int32_t cols, float* dst, int32_t rows_p,
+                       int32_t cols_p, hipStream_t stream);
+
 // Sixteen zero bytes in device memory, defined once per kernel source.  A
 // masked-off load (outside the matrix, or past the end of a K slice) reads
 // from here instead of being followed by a select, so no instruction waits on

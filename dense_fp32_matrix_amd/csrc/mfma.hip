@@ -500,8 +500,21 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
         }
     };
     auto issue = [&](int step, float* st) {
+        const int k0 = kb + step * BK;
+        const float* abase = g.A + k0;
+        const float* bbase = g.B + (int64_t)k0 * g.ldb;
 #pragma unroll
-        for (int d = 0; d < Q::LOADS; ++d) issue_one(step, st, d);
+        for (int i = 0; i < Q::A_PER_WAVE; ++i) {
+            const bool ok = a_rok[i] && (k0 + a_kc[i] < ke);
+            dma_lanes<W>(ok ? abase + a_off[i] : kZeroMfma, st + (i * Q::WAVES + wave) * Q::SEG);
+        }
+#pragma unroll
+        for (int i = 0; i < Q::B_PER_WAVE; ++i) {
+            const int ins = i * Q::WAVES + wave;
+            const bool ok = b_cok[i] && (k0 + b_kr[i] < ke);
+            dma_lanes<W>(ok ? bbase + b_off[i] : kZeroMfma,
+                         st + Q::A_STAGE + ins / Q::B_SEGS * Q::B_GS + ins % Q::B_SEGS * Q::SEG);
+        }
     };
 
     f32x16 acc[P::MB][P::NB];

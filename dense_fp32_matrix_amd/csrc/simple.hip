@@ -2,6 +2,8 @@
 // the zero fill for K == 0.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace sgemm_impl {
@@ -71,10 +73,47 @@ void fill_zero_kernel(float* __restrict__ C, int64_t ldc, int32_t M, int32_t N) 
     }
 }
 
-// Stream-K fix-up (see the stream-K decomposition of the MFMA kernel): one
-// workgroup per stream-K tile.  A tile whose K-steps fall in one workgroup's
-// range was written whole; otherwise its partial slots, from workgroups
-// w0..w1 in that order, are summed and the tile is written to C.
+// Packing: the rows x cols matrix src (leading dimension ld, any 4-byte
+// alignment) is copied into the rows_p x cols_p row-major dst (leading
+// dimension cols_p, a multiple of 4; dst 16-byte aligned), with zeros in the
+// padding rows and columns.  The copy is exact, and the zeros only add +0
+// terms to the product, so the matrix kernel's 16-byte loaders can then run
+// on operands that were not aligned.  One thread writes one 16-byte group of
+// a row; blockIdx.y strides over the rows.
+__global__ __launch_bounds__(256)
+void pack_kernel(const float* __restrict__ src, int64_t ld, int32_t rows, int32_t cols,
+                 float* __restrict__ dst, int32_t rows_p, int32_t cols_p) {
+    const int32_t c4 = (int32_t)blockIdx.x * 256 + (int32_t)threadIdx.x;
+    if (4 * c4 >= cols_p) return;
+    for (int32_t r = blockIdx.y; r < rows_p; r += gridDim.y) {
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < rows) {
+            const float* s = src + (int64_t)r * ld + 4 * c4;
+            const int32_t left = cols - 4 * c4;
+            if (left > 0) v.x = s[0];
+            if (left > 1) v.y = s[1];
+            if (left > 2) v.z = s[2];
+            if (left > 3) v.w = s[3];
+        }
+        *reinterpret_cast<float4*>(dst + (int64_t)r * cols_p + 4 * c4) = v;
+    }
+}
+
+// Stream-K fix-up (see the stream-K decomposition of the MFMA kernel):
+// workgroup (j, part) handles elements [part * kFixupChunk, (part + 1) *
+// kFixupChunk) of stream-K tile j, four 16-byte groups per thread so that
+// every thread has its loads in flight at once.  A tile whose K-steps fall in
+// one workgroup's range was written whole; otherwise its partial slots, from
+// workgroups w0..w1 in that order, are summed and the tile is written to C.
+constexpr int kFixupChunk = 4096;
+
+constexpr bool fixup_chunks_fit() {
+    for (const TileShape& t : kMfmaTiles)
+        if ((t.bm * t.bn) % kFixupChunk != 0) return false;
+    return true;
+}
+static_assert(fixup_chunks_fit(), "every MFMA tile splits into whole fix-up chunks");
+
 __global__ __launch_bounds__(256)
 void streamk_fixup_kernel(GemmArgs g, int bm, int bn) {
     const int j = blockIdx.x;
@@ -88,20 +127,34 @@ void streamk_fixup_kernel(GemmArgs g, int bm, int bn) {
     const int m0 = tm * bm;
     const int n0 = tn * bn;
     const int64_t slot = (int64_t)bm * bn;
-    for (int e = 4 * threadIdx.x; e < bm * bn; e += 4 * blockDim.x) {
-        const int i = e / bn;
-        const int c = e - i * bn;
+    const bool vec_c = (g.ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(g.C) % 16 == 0);
+    f32x4 s[4];
+    int es[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        es[u] = (int)blockIdx.y * kFixupChunk + 4 * ((int)threadIdx.x + 256 * u);
+        s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int w = w0; w <= w1; ++w) {
+        const int which = (int64_t)w * g.sk_ipw >= first ? 0 : 1;
+        const float* src = g.ws + (int64_t)(2 * w + which) * slot;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s[u] += *reinterpret_cast<const f32x4*>(src + es[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = es[u] / bn;
+        const int c = es[u] - i * bn;
         if (m0 + i >= g.M || n0 + c >= g.N) continue;
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-        for (int w = w0; w <= w1; ++w) {
-            const int which = (int64_t)w * g.sk_ipw >= first ? 0 : 1;
-            s += *reinterpret_cast<const f32x4*>(g.ws + (int64_t)(2 * w + which) * slot + e);
-        }
         float* crow = g.C + (int64_t)(m0 + i) * g.ldc + n0 + c;
-        crow[0] = s[0];
-        if (n0 + c + 1 < g.N) crow[1] = s[1];
-        if (n0 + c + 2 < g.N) crow[2] = s[2];
-        if (n0 + c + 3 < g.N) crow[3] = s[3];
+        if (vec_c && n0 + c + 3 < g.N) {
+            *reinterpret_cast<f32x4*>(crow) = s[u];
+        } else {
+            crow[0] = s[u][0];
+            if (n0 + c + 1 < g.N) crow[1] = s[u][1];
+            if (n0 + c + 2 < g.N) crow[2] = s[u][2];
+            if (n0 + c + 3 < g.N) crow[3] = s[u][3];
+        }
     }
 }
 
@@ -130,7 +183,18 @@ hipError_t launch_splitk_reduce(const float* W, int64_t ldw, int64_t w_slice, in
 }
 
 hipError_t launch_streamk_fixup(const GemmArgs& g, int bm, int bn, int sk_tiles, hipStream_t stream) {
-    hipLaunchKernelGGL(streamk_fixup_kernel, dim3((unsigned)sk_tiles), dim3(256), 0, stream, g, bm, bn);
+    // every tile shape holds a whole number of chunks
+    if ((bm * bn) % kFixupChunk != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(streamk_fixup_kernel, dim3((unsigned)sk_tiles, (unsigned)(bm * bn / kFixupChunk)), dim3(256),
+                       0, stream, g, bm, bn);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(const float* src, int64_t ld, int32_t rows, int32_t cols, float* dst, int32_t rows_p,
+                       int32_t cols_p, hipStream_t stream) {
+    const unsigned gx = (unsigned)((cols_p / 4 + 255) / 256);
+    const unsigned gy = (unsigned)std::min<int32_t>(rows_p, 65535);
+    hipLaunchKernelGGL(pack_kernel, dim3(gx, gy), dim3(256), 0, stream, src, ld, rows, cols, dst, rows_p, cols_p);
     return hipGetLastError();
 }
 

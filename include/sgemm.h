@@ -29,8 +29,9 @@
  * the device that is current when the call is made.  The library keeps no
  * reference to them after the call returns.  All work is enqueued on
  * `stream` (0 = the null stream) and the call returns without waiting;
- * the caller synchronises.  Calls on one stream run in order.  When split-K
- * needs scratch memory, `sgemm` allocates it stream-ordered on `stream`
+ * the caller synchronises.  Calls on one stream run in order.  When a plan
+ * needs scratch memory (packed operand copies, split-K or stream-K
+ * partials), `sgemm` allocates it stream-ordered on `stream`
  * (hipMallocAsync / hipFreeAsync); `sgemm_ex` can take a caller buffer.
  *
  * Errors: every argument check below runs on the host before any HIP call;
@@ -101,9 +102,17 @@ typedef enum sgemm_decomposition {
  *   vector        : 0 = choose (16-byte loads when the operands allow them),
  *                   1 = force 4-byte loads.
  *   decomposition : an sgemm_decomposition.
- *   workspace     : 256-byte aligned device buffer of workspace_bytes for split-K or
- *                   stream-K partials, or NULL to let the library allocate it
- *                   stream-ordered.  The caller keeps it alive until the work completes.
+ *   pack          : operands whose rows are not 16-byte aligned (or K, N not multiples
+ *                   of 4) can first be copied into zero-padded, aligned workspace
+ *                   copies (the "packing" of blocked GEMMs) so that the 16-byte
+ *                   loaders apply: 0 = when the time model favours it, 1 = never,
+ *                   2 = whenever an operand is misaligned.  Ignored when vector = 1.
+ *                   Packing copies values exactly, so results are those of the
+ *                   16-byte path on the same values.
+ *   workspace     : 256-byte aligned device buffer of workspace_bytes for packed
+ *                   operands and split-K or stream-K partials, or NULL to let the
+ *                   library allocate it stream-ordered.  The caller keeps it alive
+ *                   until the work completes.
  */
 typedef struct sgemm_options {
     int32_t path;
@@ -111,7 +120,7 @@ typedef struct sgemm_options {
     int32_t split_k;
     int32_t vector;
     int32_t decomposition;
-    int32_t reserved;
+    int32_t pack;
     void* workspace;
     size_t workspace_bytes;
 } sgemm_options;
@@ -141,6 +150,9 @@ typedef struct sgemm_plan {
     int64_t dp_tiles;        /* stream-K: tiles computed whole first */
     int64_t sk_tiles;        /* stream-K: tiles whose K-steps are shared out */
     int64_t sk_units_per_wg; /* stream-K: (tile, K-step) units per workgroup */
+    int32_t packed;          /* bit 0: A, bit 1: B copied to aligned workspace first */
+    int32_t k_padded;        /* K as the matrix kernel sees it (a multiple of 4 when
+                                packed; K otherwise) */
 } sgemm_plan;
 
 sgemm_status sgemm_plan_query(int64_t M, int64_t N, int64_t K,
@@ -149,8 +161,9 @@ sgemm_status sgemm_plan_query(int64_t M, int64_t N, int64_t K,
                               const float* C, int64_t ldc,
                               const sgemm_options* opts, sgemm_plan* plan);
 
-/* Scratch bytes the default plan of sgemm would need (0 when it does not
- * split K).  Host only. */
+/* Scratch bytes the default plan of sgemm would need for 16-byte aligned
+ * base pointers and these leading dimensions (0 when it neither packs nor
+ * splits K).  Host only. */
 size_t sgemm_workspace_size(int64_t M, int64_t N, int64_t K,
                             int64_t lda, int64_t ldb, int64_t ldc);
 

@@ -83,6 +83,7 @@ def test_bad_options_rejected():
     assert lib.sgemm_raw(*base, opts=lib._options(path="skinny")) == 1          # M > 16
     assert lib.sgemm_raw(*base, opts=lib._options(path="naive", split_k=2)) == 1
     assert lib.sgemm_raw(*base, opts=lib._options(workspace=A + 16, workspace_bytes=1 << 20)) == 1
+    assert lib.sgemm_raw(*base, opts=lib._options(pack=-1)) == 1
 
 
 def test_empty_problems_plan_no_launch():
@@ -120,14 +121,42 @@ def test_boundary_worked_example():
 
 
 def test_vector_loader_selection():
-    # 16-byte aligned, ld and widths multiples of 4 -> 16-byte loaders
-    assert lib.sgemm_plan_query(512, 512, 512)["vector"] == 1
-    # odd leading dimensions (the ragged workload) -> 4-byte loaders
-    assert lib.sgemm_plan_query(4097, 3001, 2049, lda=2049, ldb=3001, ldc=3001)["vector"] == 0
+    # 16-byte aligned, ld and widths multiples of 4 -> 16-byte loaders, nothing packed
+    p = lib.sgemm_plan_query(512, 512, 512)
+    assert p["vector"] == 1 and p["packed"] == 0 and p["k_padded"] == 512
+    # odd leading dimensions (the ragged workload) without packing -> 4-byte loaders
+    p = lib.sgemm_plan_query(4097, 3001, 2049, lda=2049, ldb=3001, ldc=3001, pack="never")
+    assert p["vector"] == 0 and p["packed"] == 0
     # a base pointer offset by one float
-    assert lib.sgemm_plan_query(512, 512, 512, A=0x100004)["vector"] == 0
-    # forced off
-    assert lib.sgemm_plan_query(512, 512, 512, vector=1)["vector"] == 0
+    assert lib.sgemm_plan_query(512, 512, 512, A=0x100004, pack="never")["vector"] == 0
+    # forced off: no packing either
+    p = lib.sgemm_plan_query(512, 512, 512, A=0x100004, vector=1, pack="always")
+    assert p["vector"] == 0 and p["packed"] == 0
+
+
+def test_packing_plans():
+    """Packed operands: which ones, K padded to a multiple of 4, the copies
+    at the front of the workspace, one launch per packed operand."""
+    M, N, K = 4097, 3001, 2049
+    p = lib.sgemm_plan_query(M, N, K, lda=K, ldb=N, ldc=N, path="mfma", tile=8, decomposition="tiles",
+                             split_k=1, pack="always")
+    assert p["packed"] == 3 and p["vector"] == 1 and p["k_padded"] == 2052
+    r256 = lambda b: (b + 255) // 256 * 256
+    assert p["workspace_bytes"] == r256(M * 2052 * 4) + r256(2052 * 3004 * 4)
+    assert p["launches"] == 3
+    # only B misaligned (N odd, K a multiple of 4): A is read in place
+    q = lib.sgemm_plan_query(512, 509, 512, path="mfma", tile=8, decomposition="tiles", split_k=1,
+                             pack="always")
+    assert q["packed"] == 2 and q["k_padded"] == 512 and q["workspace_bytes"] == 512 * 512 * 4
+    # only A misaligned (odd lda)
+    q = lib.sgemm_plan_query(512, 512, 512, lda=513, path="mfma", tile=8, decomposition="tiles", split_k=1,
+                             pack="always")
+    assert q["packed"] == 1 and q["workspace_bytes"] == 512 * 512 * 4 and q["launches"] == 2
+    # aligned operands are never packed; other paths never pack
+    assert lib.sgemm_plan_query(512, 512, 512, pack="always")["packed"] == 0
+    assert lib.sgemm_plan_query(512, 509, 512, path="valu", pack="always")["packed"] == 0
+    with pytest.raises(lib.SgemmError):
+        lib.sgemm_plan_query(512, 512, 512, pack=3)
 
 
 def test_default_plans_fill_the_chip():
@@ -140,11 +169,13 @@ def test_default_plans_fill_the_chip():
         p = lib.sgemm_plan_query(M, N, K, lda=K, ldb=N, ldc=N)
         waves = p["workgroups"] * p["threads"] // 64
         assert p["workgroups"] >= 256 or waves >= 1024, (M, N, K, p)
-        assert p["k_chunk"] * p["split_k"] >= K
-        assert p["k_chunk"] * (p["split_k"] - 1) < K
+        Kg = p["k_padded"]
+        assert Kg in (K, (K + 3) // 4 * 4)
+        assert p["k_chunk"] * p["split_k"] >= Kg
+        assert p["k_chunk"] * (p["split_k"] - 1) < Kg
         if p["split_k"] > 1:
             assert p["workspace_bytes"] >= p["split_k"] * M * N * 4
-            assert p["launches"] == 2
+            assert p["launches"] == 2 + bin(p["packed"]).count("1")
         assert lib.sgemm_workspace_size(M, N, K) == p["workspace_bytes"]
     assert lib.sgemm_plan_query(16, 11008, 4096)["path_name"] == "skinny"
     p = lib.sgemm_plan_query(512, 512, 65536)

@@ -159,12 +159,13 @@ def test_padded_leading_dimensions(oracle_mod, path):
     assert_bit_exact(Cbuf.numpy(), ref, what=f"{path} padded")
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma", "skinny"])
-def test_misaligned_base_pointers(oracle_mod, path):
+@pytest.mark.parametrize("path,pack", [("valu", "never"), ("mfma", "never"), ("mfma", "always"),
+                                       ("skinny", "never")])
+def test_misaligned_base_pointers(oracle_mod, path, pack):
     """Views starting one float into their buffers: 4-byte aligned only."""
     M = 12 if path == "skinny" else 97
     N, K = 132, 76
-    say(f"misaligned path={path}")
+    say(f"misaligned path={path} pack={pack}")
     A, B = inputs(M, N, K, "integer", 9)
     Abuf = torch.zeros((M * K + 1,), dtype=torch.float32, device=DEV)
     Bbuf = torch.zeros((K * N + 1,), dtype=torch.float32, device=DEV)
@@ -174,14 +175,58 @@ def test_misaligned_base_pointers(oracle_mod, path):
     Cd = Cbuf[1:M * N + 1].view(M, N)
     Ad.copy_(A.to(DEV))
     Bd.copy_(B.to(DEV))
-    plan = lib.sgemm_plan_query(M, N, K, Ad.data_ptr(), K, Bd.data_ptr(), N, Cd.data_ptr(), N, path=path)
-    assert plan["vector"] == 0
-    lib.sgemm_ex(Ad, Bd, Cd, path=path)
+    plan = lib.sgemm_plan_query(M, N, K, Ad.data_ptr(), K, Bd.data_ptr(), N, Cd.data_ptr(), N, path=path,
+                                pack=pack)
+    if pack == "always":
+        assert plan["vector"] == 1 and plan["packed"] == 3
+    else:
+        assert plan["vector"] == 0 and plan["packed"] == 0
+    lib.sgemm_ex(Ad, Bd, Cd, path=path, pack=pack)
     torch.cuda.synchronize()
     c = Cbuf.cpu().numpy()
     assert np.isnan(c[0]) and np.isnan(c[-1]), "wrote outside C"
     ref = oracle_mod.round_to_f32(oracle_mod.sgemm(A.numpy(), B.numpy()))
     assert_bit_exact(c[1:M * N + 1].reshape(M, N), ref, what=f"{path} misaligned")
+
+
+# --- packed operands: misaligned operands copied to aligned, zero-padded workspace -------------
+
+PACK_CASES = [
+    # (M, N, K, lda, ldb, packed bits expected)
+    (300, 200, 21, None, None, 3),      # K not a multiple of 4: both operands padded along K
+    (130, 261, 100, None, None, 2),     # N odd: B only
+    (130, 260, 100, 101, None, 1),      # lda odd: A only
+    (513, 385, 272, 273, 387, 3),       # both leading dimensions odd, NaN in the gaps
+    (1, 1, 1, None, None, 3),
+    (600, 517, 333, 335, None, 3),      # several 256 x 256 tiles, ragged in every dimension
+]
+
+
+@pytest.mark.parametrize("decomposition", ["tiles", "stream_k"])
+@pytest.mark.parametrize("case", PACK_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"_lda{c[3]}_ldb{c[4]}")
+def test_packed_operands(oracle_mod, case, decomposition):
+    M, N, K, lda, ldb, bits = case
+    plan = lib.sgemm_plan_query(M, N, K, lda=lda or K, ldb=ldb or N, path="mfma", tile=8, pack="always",
+                                decomposition=decomposition)
+    assert plan["packed"] == bits and plan["vector"] == 1
+    assert plan["k_padded"] == (K + 3) // 4 * 4
+    check_case(oracle_mod, M, N, K, f"packed/{decomposition}", lda=lda, ldb=ldb, path="mfma", tile=8,
+               pack="always", decomposition=decomposition)
+
+
+def test_packed_matches_unpacked_bits():
+    """Packing copies values exactly and pads with zeros: the 16-byte kernel
+    on packed copies returns the bits of the 16-byte kernel run on an
+    aligned copy of the same operands made on the host."""
+    M, N, K = 700, 301, 517
+    say("packed vs aligned copy")
+    A, B = inputs(M, N, K, "uniform", 77)
+    Kp, Np = 520, 304
+    Ap = torch.zeros((M, Kp)); Ap[:, :K] = A
+    Bp = torch.zeros((Kp, Np)); Bp[:K, :N] = B
+    C1 = run(A, B, path="mfma", tile=8, pack="always", decomposition="tiles")
+    C2 = run(Ap, Bp[:, :N], path="mfma", tile=8, decomposition="tiles")
+    assert torch.equal(C1.cpu(), C2.cpu())
 
 
 # --- degenerate sizes ------------------------------------------------------------------------
