@@ -172,7 +172,7 @@ def main():
     src = {1: "simple.hip", 2: "valu.hip", 3: "mfma.hip", 4: "skinny.hip"}.get(plan["path"], "mfma.hip")
     digest = source_digest([f"dense_fp32_matrix_amd/csrc/{src}", "dense_fp32_matrix_amd/csrc/kernels.hpp"])
     key = (f"{main_kernel}:{w.name}:tile{plan['tile']}:{plan['decomposition_name']}:split{plan['split_k']}"
-           f":vec{plan['vector']}")
+           f":vec{plan['vector']}:pack{plan['packed']}")
     hbm_bound = w.M <= 16
     if hbm_bound:
         achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
