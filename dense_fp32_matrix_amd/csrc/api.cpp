@@ -84,7 +84,9 @@ int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 // add their partial-product traffic and one more launch.
 // ---------------------------------------------------------------------------
 constexpr double kMacRate = 128.0 * 2.4e9;   // FP32 MACs per second per CU at peak
-constexpr double kPartialBw = 4e12;          // bytes/s for partial tiles (mostly cache resident)
+constexpr double kPartialBw = 4e12;          // bytes/s for split-K partial slices (mostly cache resident)
+constexpr double kStreamKBw = 1e13;          // bytes/s for stream-K partial tiles (written and read back
+                                             // by neighbouring workgroups, cache resident)
 constexpr double kLaunch = 4e-6;             // one more dependent kernel launch
 
 // Share of the CU's peak one tile shape sustains when its CU is full, with
@@ -94,7 +96,7 @@ constexpr double kLaunch = 4e-6;             // one more dependent kernel launch
 double mfma_efficiency(int tile, bool vec) {
     if (!vec) {
         switch (tile) {
-            case 8: case 9: return 0.66;
+            case 8: case 9: case 11: case 12: return 0.66;
             case 10: return 0.58;
             case 2: return 0.62;
             case 4: return 0.60;
@@ -102,6 +104,7 @@ double mfma_efficiency(int tile, bool vec) {
         }
     }
     switch (tile) {
+        case 11: case 12: return 0.92;
         case 8: return 0.91;
         case 9: return 0.905;
         case 3: case 6: return 0.89;
@@ -176,7 +179,7 @@ Candidate streamk_candidate(int tile, bool vec, int64_t M, int64_t N, int64_t K)
             it += ks1 - ks0;
         }
     }
-    if (partial > 0) c.time += 2.0 * partial * t.bm * t.bn * 4 / kPartialBw + kLaunch;
+    if (partial > 0) c.time += 2.0 * partial * t.bm * t.bn * 4 / kStreamKBw + kLaunch;
     return c;
 }
 
@@ -212,7 +215,7 @@ void choose_split(int64_t tiles, int64_t K, int bk, int64_t target_wgs, int64_t 
 Candidate mfma_best(const sgemm_options& o, bool vec, int64_t M, int64_t N, int64_t K) {
     std::vector<int> cands;
     if (o.tile >= 0) cands.push_back(o.tile);
-    else cands = {8, 3, 10, 0, 1, 2, 5, 4};
+    else cands = {11, 8, 3, 10, 0, 1, 2, 5, 4};
     Candidate best;
     bool have = false;
     for (int tile : cands) {

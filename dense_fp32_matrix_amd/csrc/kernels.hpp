@@ -75,6 +75,8 @@ constexpr TileShape kMfmaTiles[] = {
     {256, 256, 16, 2, 2, 1, 1, 3},   // 8: as 3, direct-to-LDS loads, three stages
     {256, 256, 16, 2, 2, 1, 1, 4},   // 9: as 3, direct-to-LDS loads, four stages
     {256, 128, 16, 2, 2, 2, 0, 3},   // 10: as 0, direct-to-LDS loads, three stages
+    {256, 256, 16, 2, 4, 2, 1, 3},   // 11: as 8 with 8 waves (two per SIMD), 128x64 per wave
+    {256, 256, 16, 2, 4, 2, 1, 4},   // 12: as 11, four stages
 };
 constexpr int kNumMfmaTiles = sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]);
 

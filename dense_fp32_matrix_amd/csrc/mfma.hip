@@ -720,11 +720,13 @@ hipError_t launch_mfma(int tile, bool vec, const GemmArgs& g, int splits, hipStr
         SGEMM_MFMA_CASE(8)
         SGEMM_MFMA_CASE(9)
         SGEMM_MFMA_CASE(10)
+        SGEMM_MFMA_CASE(11)
+        SGEMM_MFMA_CASE(12)
         default:
             return hipErrorInvalidValue;
     }
 #undef SGEMM_MFMA_CASE
 }
-static_assert(kNumMfmaTiles == 11, "launch_mfma covers every MFMA tile");
+static_assert(kNumMfmaTiles == 13, "launch_mfma covers every MFMA tile");
 
 }  // namespace sgemm_impl
