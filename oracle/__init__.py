@@ -7,7 +7,9 @@ input generators, which hold none of the product's arithmetic).
 
 Every function follows the plain definition C[i][j] = sum_k A[i][k] B[k][j]
 ("CUDA 算子优化：GEMM", section "矩阵乘法"; "GEMM from naive to tiled",
-section 一.2) with fp64 accumulation in ascending k.  Parity status: every
+section 一.2) with fp64 accumulation in ascending k; ``gemm`` adds the
+library-call form alpha * op(A) op(B) + beta * C ("GEMM from naive to
+tiled", section 二.2).  Parity status: every
 function here is pinned by ``tests/test_oracle_pins.py`` (integer brute
 force, identity and permutation, transpose law, associativity, closed
 forms, exact-sum and library cross-checks).
@@ -38,6 +40,9 @@ def _load():
         lib.oracle_sgemm_entries.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64,
                                              _i64, _p, _p, _p, _p]
         lib.oracle_sgemm_entries.restype = ctypes.c_int
+        lib.oracle_gemm.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, ctypes.c_double, _p, _i64,
+                                    _p, _i64, ctypes.c_double, _p, _i64, _p, _i64, _p, _i64]
+        lib.oracle_gemm.restype = ctypes.c_int
         lib.oracle_gemv.argtypes = [_i64, _i64, _p, _i64, _p, _p, ctypes.c_int]
         lib.oracle_gemv.restype = ctypes.c_int
         lib.oracle_round_to_f32.argtypes = [_i64, _p, _p]
@@ -90,6 +95,41 @@ def sgemm(A, B, with_denominator: bool = False):
     if rc != 0:
         raise RuntimeError(f"oracle_sgemm failed ({rc})")
     return (C, D) if with_denominator else C
+
+
+def gemm(A, B, C=None, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, with_denominator=False):
+    """alpha * op(A) . op(B) + beta * C in fp64, and optionally its error scale.
+
+    A is stored (M, K), or (K, M) when trans_a; B is stored (K, N), or (N, K)
+    when trans_b (float32, unit column stride).  C (M, N) float32 is read
+    only when beta != 0; A and B only when alpha != 0 and K > 0.  alpha and
+    beta are taken as the float32 values a GPU call would receive.
+    """
+    A, lda = _as_matrix(A, "A")
+    B, ldb = _as_matrix(B, "B")
+    M, K = (A.shape[1], A.shape[0]) if trans_a else A.shape
+    K2, N = (B.shape[1], B.shape[0]) if trans_b else B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    alpha = float(np.float32(alpha))
+    beta = float(np.float32(beta))
+    if beta != 0.0:
+        if C is None:
+            raise ValueError("beta != 0 needs C")
+        C, ldcin = _as_matrix(C, "C")
+        if C.shape != (M, N):
+            raise ValueError(f"C must be {(M, N)}, got {C.shape}")
+    else:
+        C, ldcin = None, max(N, 1)
+    out = np.empty((M, N), dtype=np.float64)
+    D = np.empty((M, N), dtype=np.float64) if with_denominator else None
+    rc = _load().oracle_gemm(int(bool(trans_a)), int(bool(trans_b)), M, N, K, alpha,
+                             _ptr(A), max(lda, A.shape[1], 1), _ptr(B), max(ldb, B.shape[1], 1), beta,
+                             _ptr(C) if C is not None else None, max(ldcin, N, 1),
+                             _ptr(out), max(N, 1), _ptr(D) if D is not None else None, max(N, 1))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm failed ({rc})")
+    return (out, D) if with_denominator else out
 
 
 def sgemm_entries(A, B, rows, cols):

@@ -91,6 +91,78 @@ int oracle_sgemm(int64_t M, int64_t N, int64_t K,
 }
 
 /*
+ * The library-call form: C = alpha * op(A) * op(B) + beta * Cin, row-major,
+ * with op(X) = X or its transpose.  This is the operation behind the BLAS
+ * call that "GEMM from naive to tiled" (arganzheng.life), section 二.2,
+ * follows from torch.matmul down to (transa, transb, m, n, k, alpha, A, lda,
+ * B, ldb, beta, C, ldc), with the row-major reading of section 一.2:
+ *   op(A)[i][k] = trans_a ? A[k * lda + i] : A[i * lda + k]   (A stored K x M or M x K)
+ *   op(B)[k][j] = trans_b ? B[j * ldb + k] : B[k * ldb + j]   (B stored N x K or K x N)
+ *   C[i][j] = alpha * sum_{k<K} op(A)[i][k] op(B)[k][j] + beta * Cin[i][j]
+ * The sum is taken in fp64 in ascending k, as in oracle_sgemm.  The BLAS
+ * conventions for the scalars are kept: with beta == 0, Cin is not read (so
+ * NaN there does not propagate); with alpha == 0 or K == 0, A and B are not
+ * read and C = beta * Cin.
+ * D (when not NULL) receives the error scale
+ *   |alpha| * sum_k |op(A)[i][k]| |op(B)[k][j]| + |beta| * |Cin[i][j]|
+ * (each term only where it is computed).
+ * Returns 0 on success, -1 on bad arguments, -2 if scratch allocation fails.
+ */
+int oracle_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, double alpha,
+                const float* A, int64_t lda, const float* B, int64_t ldb, double beta,
+                const float* Cin, int64_t ldcin, double* C, int64_t ldc, double* D, int64_t ldd) {
+    if (M < 0 || N < 0 || K < 0) return -1;
+    if (M == 0 || N == 0) return 0;
+    if (C == NULL || ldc < N) return -1;
+    if (D != NULL && ldd < N) return -1;
+    const int use_ab = alpha != 0.0 && K > 0;
+    if (use_ab) {
+        if (A == NULL || B == NULL) return -1;
+        if (lda < (trans_a ? M : K) || ldb < (trans_b ? K : N)) return -1;
+    }
+    if (beta != 0.0 && (Cin == NULL || ldcin < N)) return -1;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* acc = (double*)malloc((size_t)N * sizeof(double));
+        double* aacc = (double*)malloc((size_t)N * sizeof(double));
+        if (acc == NULL || aacc == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < M; ++i) {
+            if (acc == NULL || aacc == NULL) continue;
+            for (int64_t j = 0; j < N; ++j) acc[j] = aacc[j] = 0.0;
+            if (use_ab) {
+                for (int64_t k = 0; k < K; ++k) {
+                    const double a = (double)(trans_a ? A[k * lda + i] : A[i * lda + k]);
+                    for (int64_t j = 0; j < N; ++j) {
+                        const double b = (double)(trans_b ? B[j * ldb + k] : B[k * ldb + j]);
+                        acc[j] += a * b;
+                        aacc[j] += fabs(a) * fabs(b);
+                    }
+                }
+            }
+            for (int64_t j = 0; j < N; ++j) {
+                double c = use_ab ? alpha * acc[j] : 0.0;
+                double d = use_ab ? fabs(alpha) * aacc[j] : 0.0;
+                if (beta != 0.0) {
+                    const double cin = (double)Cin[i * ldcin + j];
+                    c += beta * cin;
+                    d += fabs(beta) * fabs(cin);
+                }
+                C[i * ldc + j] = c;
+                if (D != NULL) D[i * ldd + j] = d;
+            }
+        }
+        free(acc);
+        free(aacc);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
  * Selected entries only: for each t < count, c_out[t] = C[rows[t]][cols[t]]
  * and (when d_out is not NULL) d_out[t] = D[rows[t]][cols[t]], each a dot
  * product summed in ascending k.  Lets a full-size product be checked on

@@ -224,6 +224,80 @@ def test_threads_do_not_change_results(oracle_mod):
         assert np.array_equal(oracle_mod.sgemm(A[i:i + 1], B)[0], C[i])
 
 
+# --- the library-call form: alpha * op(A) op(B) + beta * C ------------------------------
+
+GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden")
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (True, False), (False, True), (True, True)])
+def test_gemm_worked_example(oracle_mod, ta, tb):
+    """The hand-computed example of tests/golden/gemm_alpha_beta.json, with
+    each operand stored as given or transposed."""
+    import json
+    g = json.load(open(__import__("os").path.join(GOLDEN, "gemm_alpha_beta.json")))
+    A = np.array(g["A"], np.float32)
+    B = np.array(g["B"], np.float32)
+    C = np.array(g["C"], np.float32)
+    As = np.ascontiguousarray(A.T) if ta else A
+    Bs = np.ascontiguousarray(B.T) if tb else B
+    got = oracle_mod.gemm(As, Bs, C, trans_a=ta, trans_b=tb, alpha=g["alpha"], beta=g["beta"])
+    assert np.array_equal(got, np.array(g["expected"], np.float64))
+    assert np.array_equal(oracle_mod.gemm(As, Bs, trans_a=ta, trans_b=tb), np.array(g["AB"], np.float64))
+
+
+@pytest.mark.parametrize("M,N,K", [(7, 11, 13), (33, 1, 70), (1, 45, 9), (64, 40, 17)])
+def test_gemm_integer_exact_all_layouts(oracle_mod, M, N, K):
+    """Integer operands, every storage layout, alpha = 2 and beta = -0.5: the
+    result is exact, so it must equal the int64 product scaled by hand."""
+    A = ints(M, K, 41)
+    B = ints(K, N, 42)
+    C = ints(M, N, 43)
+    ref = 2.0 * (A.astype(np.int64) @ B.astype(np.int64)).astype(np.float64) - 0.5 * C.astype(np.float64)
+    for ta in (False, True):
+        for tb in (False, True):
+            As = np.ascontiguousarray(A.T) if ta else A
+            Bs = np.ascontiguousarray(B.T) if tb else B
+            got = oracle_mod.gemm(As, Bs, C, trans_a=ta, trans_b=tb, alpha=2.0, beta=-0.5)
+            assert np.array_equal(got, ref), (ta, tb)
+
+
+def test_gemm_row_column_major_law(oracle_mod):
+    """Section 二.2 of "GEMM from naive to tiled": row-major C = AB is C^T = B^T A^T.
+    gemm with both operands transposed, fed B as the first and A as the second
+    stored matrix, returns C^T with the same sums in the same order."""
+    A = unif(37, 29, 44)
+    B = unif(29, 23, 45)
+    C = oracle_mod.sgemm(A, B)
+    Ct = oracle_mod.gemm(B, A, trans_a=True, trans_b=True)
+    assert Ct.shape == (23, 37)
+    assert np.array_equal(Ct, C.T)
+
+
+def test_gemm_scalars_skip_reads(oracle_mod):
+    """beta == 0 does not read C; alpha == 0 does not read A or B (NaN there
+    must not reach the result)."""
+    A = unif(9, 12, 46)
+    B = unif(12, 5, 47)
+    Cnan = np.full((9, 5), np.nan, np.float32)
+    got = oracle_mod.gemm(A, B, Cnan, alpha=3.0, beta=0.0)
+    assert np.all(np.isfinite(got)) and np.array_equal(got, 3.0 * oracle_mod.sgemm(A, B))
+    C = unif(9, 5, 48)
+    got = oracle_mod.gemm(np.full_like(A, np.nan), np.full_like(B, np.nan), C, alpha=0.0, beta=-2.0)
+    assert np.array_equal(got, -2.0 * C.astype(np.float64))
+    got, D = oracle_mod.gemm(A, B, C, alpha=0.0, beta=0.0, with_denominator=True)
+    assert np.all(got == 0) and np.all(D == 0)
+
+
+def test_gemm_denominator(oracle_mod):
+    """D = |alpha| |op(A)| |op(B)| + |beta| |C| on a case computed by hand."""
+    A = np.array([[1, -2]], np.float32)
+    B = np.array([[3], [4]], np.float32)
+    C = np.array([[-5]], np.float32)
+    val, D = oracle_mod.gemm(A, B, C, alpha=-2.0, beta=3.0, with_denominator=True)
+    assert val[0, 0] == -2.0 * (3 - 8) + 3.0 * -5      # = -5
+    assert D[0, 0] == 2.0 * (3 + 8) + 3.0 * 5           # = 37
+
+
 # --- planted mistakes: each pin above must catch a plausible oracle bug ----------------
 
 def _mutants(oracle_mod):
@@ -262,3 +336,30 @@ def test_planted_mistakes_are_caught(oracle_mod):
     for mutant in _mutants(oracle_mod):
         got = mutant(A, B)
         assert not np.array_equal(got, exact), mutant.__name__
+
+
+def test_planted_gemm_mistakes_are_caught(oracle_mod):
+    """Plausible mistakes in the library-call form (an operand read with the
+    wrong orientation, a scalar ignored or misapplied) fail the exact pin."""
+    M, N, K = 6, 5, 7
+    A = ints(M, K, 51)
+    B = ints(K, N, 52)
+    C = ints(M, N, 53)
+    exact = 2.0 * (A.astype(np.int64) @ B.astype(np.int64)).astype(np.float64) - 0.5 * C.astype(np.float64)
+    Bsq = ints(K, K, 54)
+    mutants = {
+        "trans flag ignored on A": lambda: oracle_mod.gemm(np.ascontiguousarray(A.T).reshape(M, K), B, C,
+                                                            alpha=2.0, beta=-0.5),
+        "alpha dropped": lambda: oracle_mod.gemm(A, B, C, alpha=1.0, beta=-0.5),
+        "beta sign": lambda: oracle_mod.gemm(A, B, C, alpha=2.0, beta=0.5),
+        "beta term dropped": lambda: oracle_mod.gemm(A, B, C, alpha=2.0, beta=0.0),
+        "C read transposed-ish": lambda: oracle_mod.gemm(A, B, np.ascontiguousarray(np.roll(C, 1, axis=1)),
+                                                          alpha=2.0, beta=-0.5),
+    }
+    for name, f in mutants.items():
+        assert not np.array_equal(f(), exact), name
+    # a square case where reading B with the wrong orientation still runs
+    Asq = ints(K, K, 55)
+    ref = (Asq.astype(np.int64) @ Bsq.astype(np.int64)).astype(np.float64)
+    assert not np.array_equal(oracle_mod.gemm(Asq, Bsq, trans_b=True), ref)
+    assert np.array_equal(oracle_mod.gemm(Asq, np.ascontiguousarray(Bsq.T), trans_b=True), ref)
