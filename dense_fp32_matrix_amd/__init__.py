@@ -1,4 +1,5 @@
-"""Python binding of ``libsgemm.so``: row-major FP32 C = A.B on an MI355X.
+"""Python binding of ``libsgemm.so``: row-major FP32 C = A.B, and the
+library-call form C = alpha * op(A) op(B) + beta * C, on an MI355X.
 
 Argument marshalling only -- every step of the product runs in the library's
 gfx950 kernels.  The functions carry the C interface's names
@@ -13,7 +14,9 @@ import os
 from typing import Optional
 
 __all__ = [
-    "SgemmError", "PATHS", "DECOMPOSITIONS", "PACK", "sgemm", "sgemm_ex", "sgemm_raw", "sgemm_plan_query", "sgemm_workspace_size",
+    "SgemmError", "PATHS", "DECOMPOSITIONS", "PACK",
+    "sgemm", "sgemm_ex", "sgemm_raw", "sgemm_plan_query", "sgemm_workspace_size",
+    "gemm", "gemm_raw", "gemm_plan_query", "gemm_workspace_size",
     "sgemm_tile_info", "sgemm_status_string", "sgemm_version", "library_path", "load_library",
 ]
 
@@ -77,6 +80,16 @@ def load_library():
     lib.sgemm_plan_query.restype = ctypes.c_int
     lib.sgemm_workspace_size.argtypes = [i64] * 6
     lib.sgemm_workspace_size.restype = ctypes.c_size_t
+    f = ctypes.c_float
+    gm = [i32, i32, i64, i64, i64, f, p, i64, p, i64, f, p, i64]
+    lib.sgemm_gemm.argtypes = gm + [p]
+    lib.sgemm_gemm.restype = ctypes.c_int
+    lib.sgemm_gemm_ex.argtypes = gm + [p, ctypes.POINTER(_Options)]
+    lib.sgemm_gemm_ex.restype = ctypes.c_int
+    lib.sgemm_gemm_plan_query.argtypes = gm + [ctypes.POINTER(_Options), ctypes.POINTER(_Plan)]
+    lib.sgemm_gemm_plan_query.restype = ctypes.c_int
+    lib.sgemm_gemm_workspace_size.argtypes = [i32, i32] + [i64] * 6
+    lib.sgemm_gemm_workspace_size.restype = ctypes.c_size_t
     ip = ctypes.POINTER(i32)
     lib.sgemm_tile_info.argtypes = [i32, i32, ip, ip, ip, ip, ip]
     lib.sgemm_tile_info.restype = ctypes.c_int
@@ -174,6 +187,99 @@ def sgemm_ex(A, B, C=None, stream=None, *, path="auto", tile=-1, split_k=0, vect
     ``pack`` in PACK (aligned copies of misaligned operands), optional ``workspace``
     tensor."""
     return _call(A, B, C, stream, _options(path, tile, split_k, vector, decomposition, workspace, pack=pack))
+
+
+def gemm_raw(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0,
+             opts: Optional[_Options] = None) -> int:
+    """sgemm_gemm / sgemm_gemm_ex with integer device addresses; returns the status code."""
+    lib = load_library()
+    if opts is None:
+        return lib.sgemm_gemm(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    return lib.sgemm_gemm_ex(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, ctypes.byref(opts))
+
+
+def _operand(t, name):
+    """(pointer, op, rows, cols, ld) of the logical 2-D operand t: a row-major
+    tensor is passed as stored (op N); a column-major one (a transposed view of
+    a row-major matrix) as the stored matrix with op T."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D torch tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be on a GPU")
+    rows, cols = t.shape
+    if cols <= 1 or t.stride(1) == 1:
+        ld = t.stride(0) if rows > 1 else max(cols, 1)
+        return (t.data_ptr() if t.numel() else None), 0, rows, cols, max(ld, cols, 1)
+    if rows <= 1 or t.stride(0) == 1:
+        ld = t.stride(1) if cols > 1 else max(rows, 1)
+        return (t.data_ptr() if t.numel() else None), 1, rows, cols, max(ld, rows, 1)
+    raise ValueError(f"{name} must be row-major or column-major (one unit stride)")
+
+
+def gemm(A, B, C=None, stream=None, *, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, **options):
+    """C = alpha * op(A) @ op(B) + beta * C with op(X) = X.T when trans_x.
+
+    A and B may be row-major tensors or column-major views (such as W.t());
+    each is handed to the library as stored, with the matching operation
+    flag, so nothing is copied.  C (row-major) is read only when beta != 0
+    and is allocated when None (then beta must be 0).  ``options`` are those
+    of ``sgemm_ex``.  Returns C."""
+    import torch
+    a_log = A.t() if trans_a else A
+    b_log = B.t() if trans_b else B
+    a, op_a, M, K, lda = _operand(a_log, "A")
+    b, op_b, K2, N, ldb = _operand(b_log, "B")
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: op(A) is {M}x{K}, op(B) is {K2}x{N}")
+    if C is None:
+        if beta != 0:
+            raise ValueError("beta != 0 needs C")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    c, Mc, Nc, ldc = _matrix(C, "C")
+    if (Mc, Nc) != (M, N):
+        raise ValueError(f"C must be {M}x{N}, got {Mc}x{Nc}")
+    if not (A.device == B.device == C.device):
+        raise ValueError("A, B and C must be on the same device")
+    opts = _options(**options) if options else None
+    with torch.cuda.device(A.device):
+        st = gemm_raw(op_a, op_b, M, N, K, float(alpha), a, lda, b, ldb, float(beta), c, ldc,
+                      _stream_handle(stream, A.device), opts)
+    if st != SGEMM_OK:
+        raise SgemmError(st, "sgemm_gemm")
+    return C
+
+
+def gemm_plan_query(op_a, op_b, M, N, K, alpha=1.0, A=0x100000, lda=None, B=0x200000000, ldb=None, beta=0.0,
+                    C=0x400000000, ldc=None, **options) -> dict:
+    """The plan sgemm_gemm_ex would use (host only); ops are "N"/"T" or 0/1."""
+    lib = load_library()
+    oa = {"N": 0, "T": 1}.get(op_a, op_a)
+    ob = {"N": 0, "T": 1}.get(op_b, op_b)
+    lda = max(M if oa == 1 else K, 1) if lda is None else lda
+    ldb = max(K if ob == 1 else N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    o = _options(**options)
+    pl = _Plan()
+    st = lib.sgemm_gemm_plan_query(oa, ob, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ctypes.byref(o),
+                                   ctypes.byref(pl))
+    if st != SGEMM_OK:
+        raise SgemmError(st, "sgemm_gemm_plan_query")
+    out = {name: getattr(pl, name) for name, _ in _Plan._fields_}
+    out["path_name"] = _PATH_NAMES.get(out["path"], "?")
+    out["decomposition_name"] = _DECOMP_NAMES.get(out["decomposition"], "?")
+    return out
+
+
+def gemm_workspace_size(op_a, op_b, M, N, K, lda=None, ldb=None, ldc=None) -> int:
+    lib = load_library()
+    oa = {"N": 0, "T": 1}.get(op_a, op_a)
+    ob = {"N": 0, "T": 1}.get(op_b, op_b)
+    return int(lib.sgemm_gemm_workspace_size(oa, ob, M, N, K, max(M if oa == 1 else K, 1) if lda is None else lda,
+                                             max(K if ob == 1 else N, 1) if ldb is None else ldb,
+                                             max(N, 1) if ldc is None else ldc))
 
 
 def sgemm_plan_query(M, N, K, A=0x100000, lda=None, B=0x200000000, ldb=None, C=0x400000000, ldc=None,

@@ -49,9 +49,10 @@ struct Plan {
     int64_t ldw = 0;       // split-K workspace leading dimension (floats)
     int64_t k_steps = 0;   // stream-K: K-steps per tile
     bool second = false;   // a split-K reduce or stream-K fix-up follows the matrix kernel
-    // packing: the matrix kernel reads A' (M x kp, leading dimension kp) and
-    // B' (kp x np, leading dimension np) from the workspace at these offsets
-    int64_t kp = 0, np = 0;
+    // packing: the matrix kernel reads the packed copies of A and B (their
+    // stored orientation, K padded to kp) from the workspace at these offsets
+    int64_t kp = 0;
+    int64_t a_rows = 0, a_cols = 0, b_rows = 0, b_cols = 0;   // packed stored shapes (leading dimension = cols)
     size_t pack_a_off = 0, pack_b_off = 0, gemm_ws_off = 0;
 };
 
@@ -183,19 +184,43 @@ Candidate streamk_candidate(int tile, bool vec, int64_t M, int64_t N, int64_t K)
     return c;
 }
 
-sgemm_status validate(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
-                      int64_t ldb, const float* C, int64_t ldc) {
-    if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_INVALID_ARG;
-    if (lda < std::max<int64_t>(1, K) || ldb < std::max<int64_t>(1, N) || ldc < std::max<int64_t>(1, N))
+// One call of the library-call form C = alpha * op(A) op(B) + beta * C.
+struct Call {
+    bool ta = false, tb = false;      // A stored K x M / B stored N x K
+    int64_t M = 0, N = 0, K = 0;
+    float alpha = 1.f, beta = 0.f;
+    const float* A = nullptr;
+    int64_t lda = 0;
+    const float* B = nullptr;
+    int64_t ldb = 0;
+    const float* C = nullptr;
+    int64_t ldc = 0;
+    // stored shapes of A and B
+    int64_t a_rows() const { return ta ? K : M; }
+    int64_t a_cols() const { return ta ? M : K; }
+    int64_t b_rows() const { return tb ? N : K; }
+    int64_t b_cols() const { return tb ? K : N; }
+    bool reads_ab() const { return alpha != 0.f && K > 0 && M > 0 && N > 0; }
+};
+
+sgemm_status validate(const Call& c) {
+    if (c.M < 0 || c.N < 0 || c.K < 0) return SGEMM_ERR_INVALID_ARG;
+    if (c.lda < std::max<int64_t>(1, c.a_cols()) || c.ldb < std::max<int64_t>(1, c.b_cols()) ||
+        c.ldc < std::max<int64_t>(1, c.N))
         return SGEMM_ERR_INVALID_ARG;
-    if (M > 0 && K > 0 && A == nullptr) return SGEMM_ERR_INVALID_ARG;
-    if (K > 0 && N > 0 && B == nullptr) return SGEMM_ERR_INVALID_ARG;
-    if (M > 0 && N > 0 && C == nullptr) return SGEMM_ERR_INVALID_ARG;
-    if (!aligned(A, 4) || !aligned(B, 4) || !aligned(C, 4)) return SGEMM_ERR_INVALID_ARG;
-    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return SGEMM_ERR_UNSUPPORTED;
-    if (!extent_ok(M, K, lda) || !extent_ok(K, N, ldb) || !extent_ok(M, N, ldc)) return SGEMM_ERR_UNSUPPORTED;
-    const Range rc = span(C, M, N, ldc);
-    if (overlap(rc, span(A, M, K, lda)) || overlap(rc, span(B, K, N, ldb))) return SGEMM_ERR_INVALID_ARG;
+    const bool ab = c.reads_ab();
+    if (ab && (c.A == nullptr || c.B == nullptr)) return SGEMM_ERR_INVALID_ARG;
+    if (c.M > 0 && c.N > 0 && c.C == nullptr) return SGEMM_ERR_INVALID_ARG;
+    if (!aligned(c.A, 4) || !aligned(c.B, 4) || !aligned(c.C, 4)) return SGEMM_ERR_INVALID_ARG;
+    if (c.M > kMaxDim || c.N > kMaxDim || c.K > kMaxDim) return SGEMM_ERR_UNSUPPORTED;
+    if (!extent_ok(c.a_rows(), c.a_cols(), c.lda) || !extent_ok(c.b_rows(), c.b_cols(), c.ldb) ||
+        !extent_ok(c.M, c.N, c.ldc))
+        return SGEMM_ERR_UNSUPPORTED;
+    if (ab) {
+        const Range rc = span(c.C, c.M, c.N, c.ldc);
+        if (overlap(rc, span(c.A, c.a_rows(), c.a_cols(), c.lda)) || overlap(rc, span(c.B, c.b_rows(), c.b_cols(), c.ldb)))
+            return SGEMM_ERR_INVALID_ARG;
+    }
     return SGEMM_OK;
 }
 
@@ -211,14 +236,15 @@ void choose_split(int64_t tiles, int64_t K, int bk, int64_t target_wgs, int64_t 
     *k_chunk = kc;
 }
 
-// Best MFMA plan for the given operand alignment (vec) and K.
-Candidate mfma_best(const sgemm_options& o, bool vec, int64_t M, int64_t N, int64_t K) {
+// Best MFMA plan for the given operand alignment (vec), operand layouts (trans) and K.
+Candidate mfma_best(const sgemm_options& o, bool vec, bool trans, int64_t M, int64_t N, int64_t K) {
     std::vector<int> cands;
     if (o.tile >= 0) cands.push_back(o.tile);
     else cands = {11, 8, 3, 10, 0, 1, 2, 5, 4};
     Candidate best;
     bool have = false;
     for (int tile : cands) {
+        if (trans && !kMfmaTiles[tile].trans) continue;   // operands stored transposed
         std::vector<Candidate> cs;
         if (o.decomposition != SGEMM_DECOMP_STREAM_K) {
             if (o.split_k > 0) {
@@ -249,9 +275,8 @@ Candidate mfma_best(const sgemm_options& o, bool vec, int64_t M, int64_t N, int6
 
 constexpr double kPackBw = 3e12;   // bytes/s read + written by the pack kernel
 
-sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
-                       int64_t ldb, const float* C, int64_t ldc, const sgemm_options* opts, Plan* out) {
-    sgemm_status st = validate(M, N, K, A, lda, B, ldb, C, ldc);
+sgemm_status make_plan(const Call& c, const sgemm_options* opts, Plan* out) {
+    sgemm_status st = validate(c);
     if (st != SGEMM_OK) return st;
     sgemm_options o{};
     if (opts) o = *opts;
@@ -260,13 +285,19 @@ sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
     if (o.decomposition < SGEMM_DECOMP_AUTO || o.decomposition > SGEMM_DECOMP_STREAM_K) return SGEMM_ERR_INVALID_ARG;
     if (o.pack < 0 || o.pack > 2) return SGEMM_ERR_INVALID_ARG;
     if (o.workspace != nullptr && !aligned(o.workspace, 256)) return SGEMM_ERR_INVALID_ARG;
+    const int64_t M = c.M, N = c.N, K = c.K;
+    const bool trans = c.ta || c.tb;
 
     Plan p;
     std::memset(&p.pub, 0, sizeof(p.pub));
     sgemm_plan& q = p.pub;
     q.split_k = 1;
     q.decomposition = SGEMM_DECOMP_TILES;
-    if (M == 0 || N == 0 || K == 0) {   // nothing to write, or the empty sum (C = 0)
+    if (o.path == SGEMM_PATH_VALU || o.path == SGEMM_PATH_SKINNY) {
+        if (trans) return SGEMM_ERR_INVALID_ARG;      // those kernels read row-major A and B only
+    }
+    if (M == 0 || N == 0 || !c.reads_ab()) {
+        // nothing to write, or C = beta * C (the empty sum, or alpha == 0)
         q.path = o.path == SGEMM_PATH_AUTO ? SGEMM_PATH_MFMA : o.path;
         q.launches = (M == 0 || N == 0) ? 0 : 1;
         q.k_padded = (int32_t)K;
@@ -274,18 +305,25 @@ sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
         return SGEMM_OK;
     }
 
-    const bool vec_ok = aligned(A, 16) && aligned(B, 16) && lda % 4 == 0 && ldb % 4 == 0 &&
-                        K % 4 == 0 && N % 4 == 0;
+    // 16-byte loaders: the operand's contiguous dimension (K for the KC
+    // layout of A and of B stored transposed, M or N for the KM layout) must
+    // come in whole 16-byte groups on 16-byte aligned rows.
+    const bool kc_a = !c.ta, kc_b = c.tb;
+    const bool a_rows_ok = aligned(c.A, 16) && c.lda % 4 == 0 && (kc_a || M % 4 == 0);
+    const bool b_rows_ok = aligned(c.B, 16) && c.ldb % 4 == 0 && (kc_b || N % 4 == 0);
+    const bool k_ok = (!kc_a && !kc_b) || K % 4 == 0;
+    const bool vec_ok = a_rows_ok && b_rows_ok && k_ok;
     q.vector = (vec_ok && o.vector == 0) ? 1 : 0;
 
     int path = o.path;
     if (path == SGEMM_PATH_AUTO) {
-        path = (M <= 16) ? SGEMM_PATH_SKINNY : SGEMM_PATH_MFMA;
+        path = (M <= 16 && !trans) ? SGEMM_PATH_SKINNY : SGEMM_PATH_MFMA;
         o.tile = -1;                 // the tile index belongs to an explicit path
     }
     if (path == SGEMM_PATH_SKINNY && M > 16) return SGEMM_ERR_INVALID_ARG;
     const int ntiles = tile_count(path);
     if (o.tile < -1 || o.tile >= ntiles) return SGEMM_ERR_INVALID_ARG;
+    if (path == SGEMM_PATH_MFMA && trans && o.tile >= 0 && !kMfmaTiles[o.tile].trans) return SGEMM_ERR_INVALID_ARG;
     if (path == SGEMM_PATH_NAIVE && o.split_k > 1) return SGEMM_ERR_INVALID_ARG;
     if (o.decomposition == SGEMM_DECOMP_STREAM_K && (path != SGEMM_PATH_MFMA || o.split_k > 1))
         return SGEMM_ERR_INVALID_ARG;
@@ -313,28 +351,32 @@ sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
         best.splits = cdiv(K, k_chunk);
         best.k_chunk = k_chunk;
     } else if (path == SGEMM_PATH_MFMA) {
-        best = mfma_best(o, q.vector != 0, M, N, K);
-        // Alternative: copy the misaligned operand(s) into aligned, zero-padded
-        // workspace first and run the 16-byte loaders.  K not a multiple of 4
-        // pads K, which both operands must then carry.
+        best = mfma_best(o, q.vector != 0, trans, M, N, K);
+        // Alternative: copy the misaligned operand(s), in their stored
+        // orientation, into aligned, zero-padded workspace first and run the
+        // 16-byte loaders.  A K that the KC layout would cut mid-chunk is
+        // padded to a multiple of 4, which both operands must then carry.
         if (!vec_ok && o.vector == 0 && o.pack != 1) {
-            const bool a_ok = aligned(A, 16) && lda % 4 == 0;
-            const bool b_ok = aligned(B, 16) && ldb % 4 == 0 && N % 4 == 0;
-            const int64_t kp = round_up(K, 4);
-            const bool pack_a = !a_ok || kp != K;
-            const bool pack_b = !b_ok || kp != K;
-            const int64_t np = pack_b ? round_up(N, 4) : N;
+            const int64_t kp = k_ok ? K : round_up(K, 4);
+            const bool pack_a = !a_rows_ok || kp != K;
+            const bool pack_b = !b_rows_ok || kp != K;
+            // packed stored shapes: the K dimension padded to kp, the contiguous one to a multiple of 4
+            const int64_t ar = c.ta ? kp : M, ac = c.ta ? round_up(M, 4) : kp;
+            const int64_t br = c.tb ? N : kp, bc = c.tb ? kp : round_up(N, 4);
             double bytes = 0;
-            if (pack_a) bytes += 4.0 * (M * K + M * kp);
-            if (pack_b) bytes += 4.0 * (K * N + kp * np);
-            Candidate c = mfma_best(o, true, M, N, kp);
-            c.time += bytes / kPackBw + (pack_a + pack_b) * kLaunch;
-            if (o.pack == 2 || c.time < best.time) {
-                best = c;
+            if (pack_a) bytes += 4.0 * (c.a_rows() * c.a_cols() + ar * ac);
+            if (pack_b) bytes += 4.0 * (c.b_rows() * c.b_cols() + br * bc);
+            Candidate cand = mfma_best(o, true, trans, M, N, kp);
+            cand.time += bytes / kPackBw + (pack_a + pack_b) * kLaunch;
+            if (o.pack == 2 || cand.time < best.time) {
+                best = cand;
                 q.vector = 1;
                 q.packed = (pack_a ? 1 : 0) | (pack_b ? 2 : 0);
                 p.kp = kp;
-                p.np = np;
+                p.a_rows = ar;
+                p.a_cols = ac;
+                p.b_rows = br;
+                p.b_cols = bc;
             }
         }
     } else {   // VALU
@@ -394,11 +436,11 @@ sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
     size_t off = 0;
     if (q.packed & 1) {
         p.pack_a_off = off;
-        off += align256((size_t)(M * p.kp) * sizeof(float));
+        off += align256((size_t)(p.a_rows * p.a_cols) * sizeof(float));
     }
     if (q.packed & 2) {
         p.pack_b_off = off;
-        off += align256((size_t)(p.kp * p.np) * sizeof(float));
+        off += align256((size_t)(p.b_rows * p.b_cols) * sizeof(float));
     }
     p.gemm_ws_off = off;
     q.workspace_bytes = gemm_ws > 0 ? off + gemm_ws : off;
@@ -407,16 +449,16 @@ sgemm_status make_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
     return SGEMM_OK;
 }
 
-sgemm_status run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb,
-                 float* C, int64_t ldc, hipStream_t stream, const sgemm_options* opts) {
+sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_options* opts) {
     Plan p;
-    sgemm_status st = make_plan(M, N, K, A, lda, B, ldb, C, ldc, opts, &p);
+    sgemm_status st = make_plan(c, opts, &p);
     if (st != SGEMM_OK) return st;
     const sgemm_plan& q = p.pub;
     if (q.launches == 0) return SGEMM_OK;
-    if (K == 0) {
-        return launch_fill_zero(C, ldc, (int32_t)M, (int32_t)N, stream) == hipSuccess ? SGEMM_OK
-                                                                                     : SGEMM_ERR_HIP;
+    const int64_t M = c.M, N = c.N;
+    if (!c.reads_ab()) {
+        return launch_scale(C, c.ldc, (int32_t)M, (int32_t)N, c.beta, stream) == hipSuccess ? SGEMM_OK
+                                                                                             : SGEMM_ERR_HIP;
     }
 
     void* ws = nullptr;
@@ -434,19 +476,24 @@ sgemm_status run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, c
         }
     }
 
+    const float* A = c.A;
+    const float* B = c.B;
+    int64_t lda = c.lda, ldb = c.ldb;
     char* const wsb = static_cast<char*>(ws);
     hipError_t e = hipSuccess;
     if (q.packed & 1) {
         float* Ap = reinterpret_cast<float*>(wsb + p.pack_a_off);
-        e = launch_pack(A, lda, (int32_t)M, (int32_t)K, Ap, (int32_t)M, (int32_t)p.kp, stream);
+        e = launch_pack(A, lda, (int32_t)c.a_rows(), (int32_t)c.a_cols(), Ap, (int32_t)p.a_rows, (int32_t)p.a_cols,
+                        stream);
         A = Ap;
-        lda = p.kp;
+        lda = p.a_cols;
     }
     if (e == hipSuccess && (q.packed & 2)) {
         float* Bp = reinterpret_cast<float*>(wsb + p.pack_b_off);
-        e = launch_pack(B, ldb, (int32_t)K, (int32_t)N, Bp, (int32_t)p.kp, (int32_t)p.np, stream);
+        e = launch_pack(B, ldb, (int32_t)c.b_rows(), (int32_t)c.b_cols(), Bp, (int32_t)p.b_rows, (int32_t)p.b_cols,
+                        stream);
         B = Bp;
-        ldb = p.np;
+        ldb = p.b_cols;
     }
     void* const gws = q.workspace_bytes > p.gemm_ws_off ? static_cast<void*>(wsb + p.gemm_ws_off) : nullptr;
 
@@ -457,6 +504,10 @@ sgemm_status run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, c
     g.M = (int32_t)M;
     g.N = (int32_t)N;
     g.K = q.k_padded;
+    g.alpha = c.alpha;
+    g.beta = c.beta;
+    g.trans_a = c.ta ? 1 : 0;
+    g.trans_b = c.tb ? 1 : 0;
     g.k_chunk = (int32_t)q.k_chunk;
     g.lda = lda;
     g.ldb = ldb;
@@ -466,7 +517,7 @@ sgemm_status run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, c
     // then cover a roughly square block of tiles
     g.group_m = (int32_t)std::min<int64_t>(q.tiles_m, 8);
     g.C = C;
-    g.ldc = ldc;
+    g.ldc = c.ldc;
     if (q.decomposition == SGEMM_DECOMP_STREAM_K) {
         g.sk_grid = (int32_t)q.workgroups;
         g.dp_tiles = (int32_t)q.dp_tiles;
@@ -481,24 +532,56 @@ sgemm_status run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, c
     }
 
     if (e == hipSuccess) {
+        const int ops = (c.ta ? 1 : 0) | (c.tb ? 2 : 0);
         switch (q.path) {
             case SGEMM_PATH_NAIVE: e = launch_naive(g, stream); break;
             case SGEMM_PATH_VALU: e = launch_valu(q.tile, q.vector != 0, g, q.split_k, stream); break;
             case SGEMM_PATH_SKINNY: e = launch_skinny(q.tile, q.vector != 0, g, q.split_k, stream); break;
-            default: e = launch_mfma(q.tile, q.vector != 0, g, q.split_k, stream); break;
+            default: e = launch_mfma(q.tile, q.vector != 0, ops, g, q.split_k, stream); break;
         }
     }
     if (e == hipSuccess && p.second) {
         if (q.decomposition == SGEMM_DECOMP_STREAM_K)
             e = launch_streamk_fixup(g, q.bm, q.bn, (int)q.sk_tiles, stream);
         else
-            e = launch_splitk_reduce(static_cast<const float*>(gws), p.ldw, M * p.ldw, q.split_k, C, ldc,
-                                     (int32_t)M, (int32_t)N, stream);
+            e = launch_splitk_reduce(static_cast<const float*>(gws), p.ldw, M * p.ldw, q.split_k, C, c.ldc,
+                                     (int32_t)M, (int32_t)N, c.alpha, c.beta, stream);
     }
     if (owned) {
         if (hipFreeAsync(ws, stream) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
     }
     return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
+}
+
+Call nn_call(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb,
+             const float* C, int64_t ldc) {
+    Call c;
+    c.M = M;
+    c.N = N;
+    c.K = K;
+    c.A = A;
+    c.lda = lda;
+    c.B = B;
+    c.ldb = ldb;
+    c.C = C;
+    c.ldc = ldc;
+    return c;
+}
+
+bool op_of(int32_t op, bool* t) {
+    if (op != SGEMM_OP_N && op != SGEMM_OP_T) return false;
+    *t = op == SGEMM_OP_T;
+    return true;
+}
+
+Call gemm_call(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
+               const float* B, int64_t ldb, float beta, const float* C, int64_t ldc) {
+    Call c = nn_call(M, N, K, A, lda, B, ldb, C, ldc);
+    c.ta = ta;
+    c.tb = tb;
+    c.alpha = alpha;
+    c.beta = beta;
+    return c;
 }
 
 }  // namespace
@@ -507,12 +590,12 @@ extern "C" {
 
 sgemm_status sgemm(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb,
                    float* C, int64_t ldc, hipStream_t stream) {
-    return run(M, N, K, A, lda, B, ldb, C, ldc, stream, nullptr);
+    return run(nn_call(M, N, K, A, lda, B, ldb, C, ldc), C, stream, nullptr);
 }
 
 sgemm_status sgemm_ex(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
                       int64_t ldb, float* C, int64_t ldc, hipStream_t stream, const sgemm_options* opts) {
-    return run(M, N, K, A, lda, B, ldb, C, ldc, stream, opts);
+    return run(nn_call(M, N, K, A, lda, B, ldb, C, ldc), C, stream, opts);
 }
 
 sgemm_status sgemm_plan_query(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
@@ -520,18 +603,51 @@ sgemm_status sgemm_plan_query(int64_t M, int64_t N, int64_t K, const float* A, i
                               sgemm_plan* plan) {
     if (plan == nullptr) return SGEMM_ERR_INVALID_ARG;
     Plan p;
-    sgemm_status st = make_plan(M, N, K, A, lda, B, ldb, C, ldc, opts, &p);
+    sgemm_status st = make_plan(nn_call(M, N, K, A, lda, B, ldb, C, ldc), opts, &p);
+    if (st == SGEMM_OK) *plan = p.pub;
+    return st;
+}
+
+sgemm_status sgemm_gemm(int32_t op_a, int32_t op_b, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                        int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
+                        hipStream_t stream) {
+    return sgemm_gemm_ex(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, nullptr);
+}
+
+sgemm_status sgemm_gemm_ex(int32_t op_a, int32_t op_b, int64_t M, int64_t N, int64_t K, float alpha,
+                           const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                           int64_t ldc, hipStream_t stream, const sgemm_options* opts) {
+    bool ta, tb;
+    if (!op_of(op_a, &ta) || !op_of(op_b, &tb)) return SGEMM_ERR_INVALID_ARG;
+    return run(gemm_call(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), C, stream, opts);
+}
+
+sgemm_status sgemm_gemm_plan_query(int32_t op_a, int32_t op_b, int64_t M, int64_t N, int64_t K, float alpha,
+                                   const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                                   const float* C, int64_t ldc, const sgemm_options* opts, sgemm_plan* plan) {
+    if (plan == nullptr) return SGEMM_ERR_INVALID_ARG;
+    bool ta, tb;
+    if (!op_of(op_a, &ta) || !op_of(op_b, &tb)) return SGEMM_ERR_INVALID_ARG;
+    Plan p;
+    sgemm_status st = make_plan(gemm_call(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), opts, &p);
     if (st == SGEMM_OK) *plan = p.pub;
     return st;
 }
 
 size_t sgemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc) {
+    return sgemm_gemm_workspace_size(SGEMM_OP_N, SGEMM_OP_N, M, N, K, lda, ldb, ldc);
+}
+
+size_t sgemm_gemm_workspace_size(int32_t op_a, int32_t op_b, int64_t M, int64_t N, int64_t K, int64_t lda,
+                                 int64_t ldb, int64_t ldc) {
     // A plan for 16-byte aligned stand-in pointers far apart; only shapes matter.
     const float* A = reinterpret_cast<const float*>(uintptr_t(1) << 44);
     const float* B = reinterpret_cast<const float*>(uintptr_t(2) << 44);
     const float* C = reinterpret_cast<const float*>(uintptr_t(3) << 44);
+    bool ta, tb;
+    if (!op_of(op_a, &ta) || !op_of(op_b, &tb)) return 0;
     Plan p;
-    if (make_plan(M, N, K, A, lda, B, ldb, C, ldc, nullptr, &p) != SGEMM_OK) return 0;
+    if (make_plan(gemm_call(ta, tb, M, N, K, 1.f, A, lda, B, ldb, 0.f, C, ldc), nullptr, &p) != SGEMM_OK) return 0;
     return p.pub.workspace_bytes;
 }
 

@@ -9,13 +9,19 @@ namespace sgemm_impl {
 
 // One launch of a tiled product kernel.  The kernel computes, for every
 // output tile (tm, tn) and slice z < gridDim.z,
-//   Cz[i][j] = sum_{k in [z*k_chunk, min(K, (z+1)*k_chunk))} A[i][k] B[k][j]
-// with Cz = C + z * c_slice, and writes it (overwrite) where i < M, j < N.
+//   Sz[i][j] = sum_{k in [z*k_chunk, min(K, (z+1)*k_chunk))} op(A)[i][k] op(B)[k][j]
+// with op(A)[i][k] = A[i*lda + k] (or A[k*lda + i] when A is stored
+// transposed) and op(B)[k][j] = B[k*ldb + j] (or B[j*ldb + k]).  With one
+// slice (c_slice == 0) it writes C[i][j] = alpha * S[i][j] + beta * C[i][j]
+// where i < M, j < N (C read only when beta != 0); with several, the raw
+// partial Sz goes to C + z * c_slice and the reduction applies alpha, beta.
 struct GemmArgs {
     const float* A;
     const float* B;
     float* C;
     int32_t M, N, K;
+    float alpha, beta;
+    int32_t trans_a, trans_b;   // the naive kernel reads these; the tiled ones are instantiated per layout
     int32_t k_chunk;    // K elements per slice (a multiple of the tile's BK)
     int64_t lda, ldb, ldc;
     int64_t c_slice;    // elements between consecutive slices' outputs
@@ -29,6 +35,15 @@ struct GemmArgs {
     int64_t sk_ipw;     // units per workgroup
     float* ws;          // partial-tile slots, 2 per workgroup, BM * BN floats each
 };
+
+// The final write of one output element: alpha * v + beta * (*p), one
+// rounding for alpha * v and one for the fused add; *p is read only when
+// beta != 0 (so whatever C held, NaN included, does not matter then).
+__device__ __forceinline__ void store_scaled(float* p, float v, float alpha, float beta) {
+    v = alpha * v;
+    if (beta != 0.f) v = __builtin_fmaf(beta, *p, v);
+    *p = v;
+}
 
 // Workgroup -> output tile.  Consecutive workgroup ids are dispatched
 // round-robin over the chip's 8 XCDs (each with its own L2), so id b is first
@@ -61,6 +76,7 @@ struct TileShape {
     int sched = 1;          // >= 1: interleave LDS and global memory instructions between MFMAs,
                             // with 8 * (sched - 1) MFMAs after the last LDS write of a K-step
     int dtl = 0;            // > 0: stages of the direct-to-LDS loader (16-byte aligned operands)
+    bool trans = false;     // also instantiated for operands stored transposed (direct-to-LDS tiles only)
 };
 
 constexpr TileShape kMfmaTiles[] = {
@@ -72,10 +88,10 @@ constexpr TileShape kMfmaTiles[] = {
     {128, 128, 32, 2, 2, 2, 0},   // 5: medium, deeper K-step
     {256, 256, 32, 2, 2, 1, 1},   // 6: as 3 with a deeper K-step (half the barriers)
     {128, 256, 16, 2, 2, 2, 1},   // 7: as 1, interleaved schedule
-    {256, 256, 16, 2, 2, 1, 1, 3},   // 8: as 3, direct-to-LDS loads, three stages
+    {256, 256, 16, 2, 2, 1, 1, 3, true},   // 8: as 3, direct-to-LDS loads, three stages
     {256, 256, 16, 2, 2, 1, 1, 4},   // 9: as 3, direct-to-LDS loads, four stages
     {256, 128, 16, 2, 2, 2, 0, 3},   // 10: as 0, direct-to-LDS loads, three stages
-    {256, 256, 16, 2, 4, 2, 1, 3},   // 11: as 8 with 8 waves (two per SIMD), 128x64 per wave
+    {256, 256, 16, 2, 4, 2, 1, 3, true},   // 11: as 8 with 8 waves (two per SIMD), 128x64 per wave
     {256, 256, 16, 2, 4, 2, 1, 4},   // 12: as 11, four stages
 };
 constexpr int kNumMfmaTiles = sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]);
@@ -99,20 +115,23 @@ constexpr TileShape kSkinnyTiles[] = {
 constexpr int kNumSkinnyTiles = sizeof(kSkinnyTiles) / sizeof(kSkinnyTiles[0]);
 
 hipError_t launch_naive(const GemmArgs& g, hipStream_t stream);
-hipError_t launch_mfma(int tile, bool vec, const GemmArgs& g, int splits, hipStream_t stream);
+// ops: bit 0 = A stored transposed, bit 1 = B stored transposed (tiles with `trans` only).
+hipError_t launch_mfma(int tile, bool vec, int ops, const GemmArgs& g, int splits, hipStream_t stream);
 hipError_t launch_valu(int tile, bool vec, const GemmArgs& g, int splits, hipStream_t stream);
 hipError_t launch_skinny(int tile, bool vec, const GemmArgs& g, int splits, hipStream_t stream);
 
 // C[i][j] = sum_{z=0}^{splits-1} W[z*w_slice + i*ldw + j], summed in order z = 0, 1, ...
 hipError_t launch_splitk_reduce(const float* W, int64_t ldw, int64_t w_slice, int splits,
-                                float* C, int64_t ldc, int32_t M, int32_t N, hipStream_t stream);
+                                float* C, int64_t ldc, int32_t M, int32_t N, float alpha, float beta,
+                                hipStream_t stream);
 
 // Stream-K fix-up: for each stream-K tile split over several workgroups, sum
 // its partial slots in workgroup order and write the tile to C.
 hipError_t launch_streamk_fixup(const GemmArgs& g, int bm, int bn, int sk_tiles, hipStream_t stream);
 
 // C[i][j] = +0.0 for i < M, j < N (the empty sum, K == 0).
-hipError_t launch_fill_zero(float* C, int64_t ldc, int32_t M, int32_t N, hipStream_t stream);
+// C = beta * C (C not read when beta == 0): the whole product when alpha == 0 or K == 0.
+hipError_t launch_scale(float* C, int64_t ldc, int32_t M, int32_t N, float beta, hipStream_t stream);
 
 // dst (rows_p x cols_p, leading dimension cols_p % 4 == 0, 16-byte aligned) =
 // src (rows x cols, leading dimension ld) zero-padded.

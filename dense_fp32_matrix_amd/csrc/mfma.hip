@@ -46,6 +46,8 @@
 //     latency after the barrier is covered by matrix-core work.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace sgemm_impl {
@@ -141,7 +143,43 @@ struct TileOut {
     float* out;
     int64_t ldo;
     int row0, col0, row_lim, col_lim;
+    float alpha = 1.f, beta = 0.f;   // out = alpha * sum + beta * out (partial sums: 1, 0)
 };
+
+// The epilogue: each wave writes its MB x NB blocks of 32 x 32 (lane l,
+// register r of a block holds row 8 (r / 4) + 4 (l / 32) + r % 4, column
+// l % 32), masked at the tile's limits, as alpha * sum + beta * out.  With
+// beta != 0 the old values are read one block at a time (the fence keeps the
+// scheduler from hoisting all of them next to the live accumulators).
+template <int MB, int NB, int WM, int WN>
+__device__ __forceinline__ void write_tile(const TileOut& o, const f32x16 (&acc)[MB][NB], int wm, int wn, int l32,
+                                           int lh) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int j = o.col0 + wn * WN + nb * 32 + l32;
+            const int ib = o.row0 + wm * WM + mb * 32 + 4 * lh;
+            if (o.beta == 0.f) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = ib + 8 * (r >> 2) + (r & 3);
+                    if (i < o.row_lim && j < o.col_lim) o.out[(int64_t)i * o.ldo + j] = o.alpha * acc[mb][nb][r];
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = ib + 8 * (r >> 2) + (r & 3);
+                    if (i < o.row_lim && j < o.col_lim) {
+                        float* p = o.out + (int64_t)i * o.ldo + j;
+                        *p = __builtin_fmaf(o.beta, *p, o.alpha * acc[mb][nb][r]);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
 
 // One output tile (tm, tn) over k in [kb, ke): load, contract, write.  All
 // threads of the workgroup call it together; smem is the workgroup's LDS.
@@ -324,19 +362,7 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& g, float* smem, int tm
     }
 
     // ---- epilogue: overwrite the destination (masked at its edges) ----
-#pragma unroll
-    for (int mb = 0; mb < P::MB; ++mb) {
-#pragma unroll
-        for (int nb = 0; nb < P::NB; ++nb) {
-            const int j = o.col0 + wn * P::WN + nb * 32 + l32;
-            const int ib = o.row0 + wm * P::WM + mb * 32 + 4 * lh;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = ib + 8 * (r >> 2) + (r & 3);
-                if (i < o.row_lim && j < o.col_lim) o.out[(int64_t)i * o.ldo + j] = acc[mb][nb][r];
-            }
-        }
-    }
+    write_tile<P::MB, P::NB, P::WM, P::WN>(o, acc, wm, wn, l32, lh);
 }
 
 
@@ -370,39 +396,94 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs& g, float* smem, int tm
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void glb_void_t;
 
-template <int BM, int BN, int BK, int WGM, int WGN, int W>
-struct DtlCfg {
-    static_assert(W == 4 || W == 1, "16-byte or 4-byte lanes");
-    static constexpr int WAVES = WGM * WGN;
+// Stage layouts of one operand.
+//  KC: R rows of BK floats (k contiguous within a row), the 16-byte chunks of
+//      row r at XOR-swizzled positions; fragments are read as 16-byte
+//      chunks.  A stored M x K and B stored N x K (transposed) use it.
+//  KM: BK rows of R floats (k-major), in blocks of 256 / R rows whose starts
+//      are GS floats apart; fragments are read one float per k row.  B
+//      stored K x N and A stored K x M (transposed) use it.
+// elem() gives, for instruction `ins` and a lane, the non-K index r and the
+// K index k of the element(s) that lane fetches; dst() the stage offset the
+// instruction writes (lane l at dst + W * l).
+template <int R, int BK, int W>
+struct KcLayout {
+    static constexpr bool KC = true;
     static constexpr int SEG = 64 * W;                    // floats one instruction writes
-    static constexpr int A_INSTR = BM * BK / SEG;
-    static constexpr int A_PER_WAVE = A_INSTR / WAVES;
-    static constexpr int B_ROWS = 256 / BN;               // B rows per 1 KB block (R)
-    static constexpr int B_GS = B_ROWS == 1 ? BN + 8 : B_ROWS * BN + 16;   // floats between blocks
-    static constexpr int B_SEGS = 256 / SEG;              // instructions per block
-    static constexpr int B_INSTR = BK / B_ROWS * B_SEGS;
-    static constexpr int B_PER_WAVE = B_INSTR / WAVES;
-    static constexpr int A_STAGE = BM * BK;
-    static constexpr int B_STAGE = BK / B_ROWS * B_GS;
-    static constexpr int STAGE = A_STAGE + B_STAGE;
-    static constexpr int LOADS = A_PER_WAVE + B_PER_WAVE;  // per lane per K-step
-    static_assert(BN == 128 || BN == 256, "B blocks hold one or two rows");
-    static_assert(SEG % BK == 0, "an A instruction fills whole rows");
-    static_assert(A_PER_WAVE * WAVES == A_INSTR && B_PER_WAVE * WAVES == B_INSTR, "instructions per wave");
-    static_assert((4 / B_ROWS) * B_GS % 64 == 32, "lane halves of a B fragment read 32 banks apart");
-    // B row k of a stage starts at this float offset
-    static __device__ __forceinline__ int b_row(int k) { return A_STAGE + (k / B_ROWS) * B_GS + (k % B_ROWS) * BN; }
+    static constexpr int FLOATS = R * BK;
+    static constexpr int INSTR = FLOATS / SEG;
+    static_assert(SEG % BK == 0, "an instruction fills whole rows");
+    static __device__ __forceinline__ void elem(int ins, int lane, int& r, int& k) {
+        const int p = ins * SEG + W * lane;
+        r = p / BK;
+        k = 4 * (((p % BK) / 4) ^ a_swizzle<BK>(r)) + p % 4;
+    }
+    static __device__ __forceinline__ int dst(int ins) { return ins * SEG; }
+    // 16-byte chunk c (k = 4c .. 4c + 3) of row r
+    static __device__ __forceinline__ int chunk(int r, int c) { return r * BK + 4 * (c ^ a_swizzle<BK>(r)); }
 };
 
-// Floats per stage of the direct-to-LDS layout (the same for both lane
-// widths; only instantiated when used).
-template <bool ON, int BM, int BN, int BK, int WGM, int WGN>
+template <int R, int BK, int W>
+struct KmLayout {
+    static constexpr bool KC = false;
+    static constexpr int SEG = 64 * W;
+    static constexpr int ROWS = 256 / R;                  // k rows per 1 KB block
+    static constexpr int GS = ROWS == 1 ? R + 8 : ROWS * R + 16;   // floats between blocks
+    static constexpr int SEGS = 256 / SEG;                // instructions per block
+    static constexpr int INSTR = BK / ROWS * SEGS;
+    static constexpr int FLOATS = BK / ROWS * GS;
+    static_assert(R == 128 || R == 256, "blocks hold one or two rows");
+    static_assert((4 / ROWS) * GS % 64 == 32, "lane halves of a fragment read 32 banks apart");
+    static __device__ __forceinline__ void elem(int ins, int lane, int& r, int& k) {
+        const int f = (ins % SEGS) * SEG + W * lane;       // float within the block
+        k = ins / SEGS * ROWS + f / R;
+        r = f % R;
+    }
+    static __device__ __forceinline__ int dst(int ins) { return ins / SEGS * GS + ins % SEGS * SEG; }
+    // k row k starts at this offset
+    static __device__ __forceinline__ int krow(int k) { return (k / ROWS) * GS + (k % ROWS) * R; }
+};
+
+template <bool TA, int BM, int BK, int W>
+using ALayout = std::conditional_t<TA, KmLayout<BM, BK, W>, KcLayout<BM, BK, W>>;
+template <bool TB, int BN, int BK, int W>
+using BLayout = std::conditional_t<TB, KcLayout<BN, BK, W>, KmLayout<BN, BK, W>>;
+
+// Floats per stage of the direct-to-LDS layout: A region, then B region (the
+// same for both lane widths; only instantiated when used).
+template <bool ON, int OPS, int BM, int BN, int BK>
 struct DtlStageFloats {
     static constexpr int value = 4;
 };
-template <int BM, int BN, int BK, int WGM, int WGN>
-struct DtlStageFloats<true, BM, BN, BK, WGM, WGN> {
-    static constexpr int value = DtlCfg<BM, BN, BK, WGM, WGN, 4>::STAGE;
+template <int OPS, int BM, int BN, int BK>
+struct DtlStageFloats<true, OPS, BM, BN, BK> {
+    static constexpr int value = ALayout<(OPS & 1) != 0, BM, BK, 4>::FLOATS + BLayout<(OPS & 2) != 0, BN, BK, 4>::FLOATS;
+};
+
+// The direct loads of one operand that one wave issues per K-step: PER
+// instructions, ins = i * waves + wave, with per-lane sources fixed over the
+// K loop.  r0 is the tile's first non-K index and lim its bound (M or N);
+// lanes past the bound, or past the K range, read the zero block.
+template <class L, int PER>
+struct DtlLoads {
+    int64_t off[PER];
+    int kk[PER];
+    bool ok[PER];
+    __device__ __forceinline__ void init(int wave, int waves, int lane, int64_t ld, int r0, int lim) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            int r, k;
+            L::elem(i * waves + wave, lane, r, k);
+            ok[i] = r0 + r < lim;
+            const int rr = ok[i] ? r0 + r : 0;
+            off[i] = L::KC ? (int64_t)rr * ld + k : (int64_t)k * ld + rr;
+            kk[i] = k;
+        }
+    }
+    // base_k0: the operand advanced to K-step start k0 (k0 columns for KC, k0 rows for KM)
+    __device__ __forceinline__ const float* src(const float* base_k0, int i, int k0, int ke) const {
+        return ok[i] && (k0 + kk[i] < ke) ? base_k0 + off[i] : kZeroMfma;
+    }
 };
 
 // s_waitcnt that waits for vmcnt <= N and nothing else (gfx9 encoding).
@@ -438,14 +519,20 @@ __device__ __forceinline__ void dma_lanes(const float* src, const float* lds) {
         asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(base));
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int SCHED, int DS, int W>
+template <int BM, int BN, int BK, int WGM, int WGN, int SCHED, int DS, int W, int OPS>
 __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, float* st1, float* st2, float* st3,
                                               int tm, int tn, int kb, int ke, const TileOut& o) {
     float* const stg[4] = {st0, st1, st2, st3};
     using P = MfmaCfg<BM, BN, BK, WGM, WGN, true>;
-    using Q = DtlCfg<BM, BN, BK, WGM, WGN, W>;
+    using LA = ALayout<(OPS & 1) != 0, BM, BK, W>;
+    using LB = BLayout<(OPS & 2) != 0, BN, BK, W>;
+    constexpr int WAVES = WGM * WGN;
+    constexpr int A_PER = LA::INSTR / WAVES;
+    constexpr int B_PER = LB::INSTR / WAVES;
+    constexpr int LOADS = A_PER + B_PER;                 // per lane per K-step
+    static_assert(A_PER * WAVES == LA::INSTR && B_PER * WAVES == LB::INSTR, "instructions per wave");
     static_assert(DS == 3 || DS == 4, "three or four stages");
-    static_assert((DS - 2) * Q::LOADS < 64, "loads in flight fit the vmcnt counter");
+    static_assert((DS - 2) * LOADS < 64, "loads in flight fit the vmcnt counter");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -455,66 +542,21 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
     const int n0 = tn * BN;
     const int steps = (ke - kb + BK - 1) / BK;
 
-    // Per-lane sources, fixed over the K loop.  Instruction `ins` fills the
-    // stage floats [ins * SEG, (ins + 1) * SEG) of A, or SEG floats of one B
-    // block, W floats per lane in lane order; each lane fetches the
-    // element(s) that belong at its position.
-    int64_t a_off[Q::A_PER_WAVE];
-    int a_kc[Q::A_PER_WAVE];
-    bool a_rok[Q::A_PER_WAVE];
-#pragma unroll
-    for (int i = 0; i < Q::A_PER_WAVE; ++i) {
-        const int p = (i * Q::WAVES + wave) * Q::SEG + W * lane;
-        const int row = p / BK;
-        const int k = 4 * (((p % BK) / 4) ^ a_swizzle<BK>(row)) + p % 4;
-        a_rok[i] = m0 + row < g.M;
-        a_off[i] = (int64_t)(a_rok[i] ? m0 + row : 0) * g.lda + k;
-        a_kc[i] = k;
-    }
-    int64_t b_off[Q::B_PER_WAVE];
-    int b_kr[Q::B_PER_WAVE];
-    bool b_cok[Q::B_PER_WAVE];
-#pragma unroll
-    for (int i = 0; i < Q::B_PER_WAVE; ++i) {
-        const int ins = i * Q::WAVES + wave;
-        const int f = (ins % Q::B_SEGS) * Q::SEG + W * lane;    // float within the block
-        const int row = ins / Q::B_SEGS * Q::B_ROWS + f / BN;
-        const int col = f % BN;
-        b_cok[i] = n0 + col < g.N;
-        b_off[i] = (int64_t)row * g.ldb + (b_cok[i] ? n0 + col : 0);
-        b_kr[i] = row;
-    }
+    DtlLoads<LA, A_PER> la;
+    DtlLoads<LB, B_PER> lb;
+    la.init(wave, WAVES, lane, g.lda, m0, g.M);
+    lb.init(wave, WAVES, lane, g.ldb, n0, g.N);
 
-    // direct load d (A loads first, then B) of K-step `step` into stage `st`
-    auto issue_one = [&](int step, float* st, int d) {
-        const int k0 = kb + step * BK;
-        if (d < Q::A_PER_WAVE) {
-            const bool ok = a_rok[d] && (k0 + a_kc[d] < ke);
-            dma_lanes<W>(ok ? g.A + k0 + a_off[d] : kZeroMfma, st + (d * Q::WAVES + wave) * Q::SEG);
-        } else {
-            const int i = d - Q::A_PER_WAVE;
-            const int ins = i * Q::WAVES + wave;
-            const bool ok = b_cok[i] && (k0 + b_kr[i] < ke);
-            dma_lanes<W>(ok ? g.B + (int64_t)k0 * g.ldb + b_off[i] : kZeroMfma,
-                         st + Q::A_STAGE + ins / Q::B_SEGS * Q::B_GS + ins % Q::B_SEGS * Q::SEG);
-        }
-    };
+    // issue the direct loads of K-step `step` into stage `st`
     auto issue = [&](int step, float* st) {
         const int k0 = kb + step * BK;
-        const float* abase = g.A + k0;
-        const float* bbase = g.B + (int64_t)k0 * g.ldb;
+        const float* abase = g.A + (LA::KC ? (int64_t)k0 : (int64_t)k0 * g.lda);
+        const float* bbase = g.B + (LB::KC ? (int64_t)k0 : (int64_t)k0 * g.ldb);
 #pragma unroll
-        for (int i = 0; i < Q::A_PER_WAVE; ++i) {
-            const bool ok = a_rok[i] && (k0 + a_kc[i] < ke);
-            dma_lanes<W>(ok ? abase + a_off[i] : kZeroMfma, st + (i * Q::WAVES + wave) * Q::SEG);
-        }
+        for (int i = 0; i < A_PER; ++i) dma_lanes<W>(la.src(abase, i, k0, ke), st + LA::dst(i * WAVES + wave));
 #pragma unroll
-        for (int i = 0; i < Q::B_PER_WAVE; ++i) {
-            const int ins = i * Q::WAVES + wave;
-            const bool ok = b_cok[i] && (k0 + b_kr[i] < ke);
-            dma_lanes<W>(ok ? bbase + b_off[i] : kZeroMfma,
-                         st + Q::A_STAGE + ins / Q::B_SEGS * Q::B_GS + ins % Q::B_SEGS * Q::SEG);
-        }
+        for (int i = 0; i < B_PER; ++i)
+            dma_lanes<W>(lb.src(bbase, i, k0, ke), st + LA::FLOATS + LB::dst(i * WAVES + wave));
     };
 
     f32x16 acc[P::MB][P::NB];
@@ -527,25 +569,52 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
 
     const int l32 = lane & 31;
     const int lh = lane >> 5;
+    // Fragments: lane l holds op(A)[m = l % 32][k] and op(B)[k][n = l % 32] for
+    // k = 8 kg + 4 (l / 32) + q, q < 4 (the MFMA's two k of step q are 4
+    // apart; A and B agree on that order).  A KC operand reads its four k as
+    // one 16-byte chunk, a KM operand one float per k row.
     int a_frag[P::KG][P::MB];
+    int b_frag[P::KG][P::NB];
 #pragma unroll
-    for (int mb = 0; mb < P::MB; ++mb) {
-        const int row = wm * P::WM + mb * 32 + l32;
-        const int sw = a_swizzle<BK>(row);
+    for (int kg = 0; kg < P::KG; ++kg) {
 #pragma unroll
-        for (int kg = 0; kg < P::KG; ++kg) a_frag[kg][mb] = row * BK + 4 * ((2 * kg + lh) ^ sw);
+        for (int mb = 0; mb < P::MB; ++mb) {
+            if constexpr (LA::KC) a_frag[kg][mb] = LA::chunk(wm * P::WM + mb * 32 + l32, 2 * kg + lh);
+            else a_frag[kg][mb] = 0;
+        }
+#pragma unroll
+        for (int nb = 0; nb < P::NB; ++nb) {
+            if constexpr (LB::KC) b_frag[kg][nb] = LA::FLOATS + LB::chunk(wn * P::WN + nb * 32 + l32, 2 * kg + lh);
+            else b_frag[kg][nb] = 0;
+        }
     }
+    const int a_col = wm * P::WM + l32;
     const int b_col = wn * P::WN + l32;
 
     f32x4 fa[2][P::MB];
     float fb[2][P::NB][4];
     auto read_frags = [&](const float* st, int kg, int set) {
 #pragma unroll
-        for (int mb = 0; mb < P::MB; ++mb) fa[set][mb] = *reinterpret_cast<const f32x4*>(st + a_frag[kg][mb]);
+        for (int mb = 0; mb < P::MB; ++mb) {
+            if constexpr (LA::KC) {
+                fa[set][mb] = *reinterpret_cast<const f32x4*>(st + a_frag[kg][mb]);
+            } else {
 #pragma unroll
-        for (int nb = 0; nb < P::NB; ++nb)
+                for (int q = 0; q < 4; ++q) fa[set][mb][q] = st[LA::krow(8 * kg + 4 * lh + q) + a_col + mb * 32];
+            }
+        }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) fb[set][nb][q] = st[Q::b_row(8 * kg + 4 * lh + q) + b_col + nb * 32];
+        for (int nb = 0; nb < P::NB; ++nb) {
+            if constexpr (LB::KC) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(st + b_frag[kg][nb]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) fb[set][nb][q] = v[q];
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    fb[set][nb][q] = st[LA::FLOATS + LB::krow(8 * kg + 4 * lh + q) + b_col + nb * 32];
+            }
+        }
     };
     auto mfmas = [&](int set) {
 #pragma unroll
@@ -560,7 +629,7 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
     if (steps > 0) {
 #pragma unroll
         for (int j = 0; j + 1 < DS; ++j) issue(j, stg[j]);
-        dtl_barrier<(DS - 2) * Q::LOADS>();
+        dtl_barrier<(DS - 2) * LOADS>();
         read_frags(stg[0], 0, 0);
         issue(DS - 1, stg[DS - 1]);
 #pragma unroll
@@ -571,7 +640,7 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
         // iteration s uses stage s % DS and refills stage (s - 1) % DS
         auto iter = [&](int s, auto j_tag) {
             constexpr int J = decltype(j_tag)::value;
-            dtl_barrier<(DS - 2) * Q::LOADS>();
+            dtl_barrier<(DS - 2) * LOADS>();
             read_frags(stg[J], 0, 0);
             mfmas(1);
             issue(s + DS - 1, stg[(J + DS - 1) % DS]);
@@ -600,19 +669,7 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
         wait_vmcnt<0>();                     // loads issued past the end land before the LDS is reused
     }
 
-#pragma unroll
-    for (int mb = 0; mb < P::MB; ++mb) {
-#pragma unroll
-        for (int nb = 0; nb < P::NB; ++nb) {
-            const int j = o.col0 + wn * P::WN + nb * 32 + l32;
-            const int ib = o.row0 + wm * P::WM + mb * 32 + 4 * lh;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = ib + 8 * (r >> 2) + (r & 3);
-                if (i < o.row_lim && j < o.col_lim) o.out[(int64_t)i * o.ldo + j] = acc[mb][nb][r];
-            }
-        }
-    }
+    write_tile<P::MB, P::NB, P::WM, P::WN>(o, acc, wm, wn, l32, lh);
 }
 
 // The kernel has two work decompositions.
@@ -628,11 +685,12 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
 //    and the stream-K fix-up kernel sums the slots of each tile in range
 //    order.  The cut depends only on the shapes, so the sums always happen in
 //    the same order (the work-splitting of "GEMM from naive to tiled", 十.1).
-template <int BM, int BN, int BK, int WGM, int WGN, bool VEC, int WPE, int SCHED, int DS>
+template <int BM, int BN, int BK, int WGM, int WGN, bool VEC, int WPE, int SCHED, int DS, int OPS>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void mfma_gemm_kernel(GemmArgs g) {
     using P = MfmaCfg<BM, BN, BK, WGM, WGN, VEC>;
+    static_assert(DS > 0 || OPS == 0, "operands stored transposed need the direct-to-LDS loader");
     // LDS: two stages for the register-staged loader, or DSE separate stage
     // arrays for the direct-to-LDS loader (16-byte lanes when the operands
     // are 16-byte aligned, else 4-byte lanes, which keep three stages so
@@ -640,7 +698,7 @@ void mfma_gemm_kernel(GemmArgs g) {
     constexpr bool DTL = DS > 0;
     constexpr int DSE = VEC ? DS : 3;
     constexpr int W = VEC ? 4 : 1;
-    constexpr int QS = DtlStageFloats<DTL, BM, BN, BK, WGM, WGN>::value;
+    constexpr int QS = DtlStageFloats<DTL, OPS, BM, BN, BK>::value;
     __shared__ __attribute__((aligned(16))) float lds0[DTL ? QS : 2 * P::STAGE];
     __shared__ __attribute__((aligned(16))) float lds1[DTL ? QS : 4];
     __shared__ __attribute__((aligned(16))) float lds2[DTL ? QS : 4];
@@ -650,15 +708,17 @@ void mfma_gemm_kernel(GemmArgs g) {
         tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
         const int kb = blockIdx.z * g.k_chunk;
         const int ke = min(g.K, kb + g.k_chunk);
-        const TileOut o{g.C + (int64_t)blockIdx.z * g.c_slice, g.ldc, tm * BM, tn * BN, g.M, g.N};
-        if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W>(g, lds0, lds1, lds2, lds3, tm, tn, kb, ke, o);
+        // one slice writes alpha * sum + beta * C; several write raw partial sums
+        const TileOut o{g.C + (int64_t)blockIdx.z * g.c_slice, g.ldc, tm * BM, tn * BN, g.M, g.N,
+                        g.c_slice ? 1.f : g.alpha, g.c_slice ? 0.f : g.beta};
+        if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W, OPS>(g, lds0, lds1, lds2, lds3, tm, tn, kb, ke, o);
         else mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, lds0, tm, tn, kb, ke, o);
         return;
     }
     for (int t = blockIdx.x; t < g.dp_tiles; t += gridDim.x) {
         tile_coords(t, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
-        const TileOut o{g.C, g.ldc, tm * BM, tn * BN, g.M, g.N};
-        if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W>(g, lds0, lds1, lds2, lds3, tm, tn, 0, g.K, o);
+        const TileOut o{g.C, g.ldc, tm * BM, tn * BN, g.M, g.N, g.alpha, g.beta};
+        if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W, OPS>(g, lds0, lds1, lds2, lds3, tm, tn, 0, g.K, o);
         else mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, lds0, tm, tn, 0, g.K, o);
         __syncthreads();                 // the next tile's prologue overwrites LDS
     }
@@ -673,13 +733,13 @@ void mfma_gemm_kernel(GemmArgs g) {
         const int kb = ks0 * BK;
         const int ke = min(g.K, ks1 * BK);
         if (ks0 == 0 && ks1 == g.k_steps) {
-            const TileOut o{g.C, g.ldc, tm * BM, tn * BN, g.M, g.N};
-            if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W>(g, lds0, lds1, lds2, lds3, tm, tn, kb, ke, o);
+            const TileOut o{g.C, g.ldc, tm * BM, tn * BN, g.M, g.N, g.alpha, g.beta};
+            if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W, OPS>(g, lds0, lds1, lds2, lds3, tm, tn, kb, ke, o);
         else mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, lds0, tm, tn, kb, ke, o);
         } else {
             float* slot = g.ws + (int64_t)(2 * blockIdx.x + which) * (BM * BN);
             const TileOut o{slot, BN, 0, 0, BM, BN};
-            if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W>(g, lds0, lds1, lds2, lds3, tm, tn, kb, ke, o);
+            if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W, OPS>(g, lds0, lds1, lds2, lds3, tm, tn, kb, ke, o);
         else mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, lds0, tm, tn, kb, ke, o);
         }
         __syncthreads();
@@ -688,26 +748,47 @@ void mfma_gemm_kernel(GemmArgs g) {
     }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int WPE, int SCHED, int DS>
-hipError_t launch_one(bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
+template <int BM, int BN, int BK, int WGM, int WGN, int WPE, int SCHED, int DS, int OPS>
+hipError_t launch_ops(bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
     dim3 grid(g.sk_iters > 0 ? (unsigned)g.sk_grid : (unsigned)((int64_t)g.tiles_m * g.tiles_n), 1,
               g.sk_iters > 0 ? 1u : (unsigned)splits);
     dim3 block(64 * WGM * WGN);
     if (vec)
-        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, true, WPE, SCHED, DS>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, true, WPE, SCHED, DS, OPS>), grid, block, 0, stream,
+                           g);
     else
-        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, false, WPE, SCHED, DS>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, false, WPE, SCHED, DS, OPS>), grid, block, 0,
+                           stream, g);
     return hipGetLastError();
+}
+
+// ops: bit 0 = A stored transposed, bit 1 = B stored transposed; only the
+// tiles whose table entry says so are instantiated for the transposed layouts.
+template <int BM, int BN, int BK, int WGM, int WGN, int WPE, int SCHED, int DS, bool TRANS>
+hipError_t launch_one(bool vec, int ops, const GemmArgs& g, int splits, hipStream_t stream) {
+    if constexpr (TRANS) {
+        switch (ops) {
+            case 0: return launch_ops<BM, BN, BK, WGM, WGN, WPE, SCHED, DS, 0>(vec, g, splits, stream);
+            case 1: return launch_ops<BM, BN, BK, WGM, WGN, WPE, SCHED, DS, 1>(vec, g, splits, stream);
+            case 2: return launch_ops<BM, BN, BK, WGM, WGN, WPE, SCHED, DS, 2>(vec, g, splits, stream);
+            case 3: return launch_ops<BM, BN, BK, WGM, WGN, WPE, SCHED, DS, 3>(vec, g, splits, stream);
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        if (ops != 0) return hipErrorInvalidValue;
+        return launch_ops<BM, BN, BK, WGM, WGN, WPE, SCHED, DS, 0>(vec, g, splits, stream);
+    }
 }
 
 }  // namespace
 
-hipError_t launch_mfma(int tile, bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
+hipError_t launch_mfma(int tile, bool vec, int ops, const GemmArgs& g, int splits, hipStream_t stream) {
 #define SGEMM_MFMA_CASE(ID)                                                                     \
     case ID:                                                                                    \
         return launch_one<kMfmaTiles[ID].bm, kMfmaTiles[ID].bn, kMfmaTiles[ID].bk,             \
                           kMfmaTiles[ID].waves_m, kMfmaTiles[ID].waves_n,                      \
-                          kMfmaTiles[ID].waves_per_simd, kMfmaTiles[ID].sched, kMfmaTiles[ID].dtl>(vec, g, splits, stream);
+                          kMfmaTiles[ID].waves_per_simd, kMfmaTiles[ID].sched, kMfmaTiles[ID].dtl, \
+                          kMfmaTiles[ID].trans>(vec, ops, g, splits, stream);
     switch (tile) {
         SGEMM_MFMA_CASE(0)
         SGEMM_MFMA_CASE(1)

@@ -1,5 +1,6 @@
-// Small kernels: the one-thread-per-output product, the split-K reduction and
-// the zero fill for K == 0.
+// Small kernels: the one-thread-per-output product, the split-K reduction,
+// the stream-K fix-up, operand packing and the C = beta * C scaling used
+// when alpha == 0 or K == 0.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -15,7 +16,9 @@ namespace {
 // 优化总结").  threadIdx.x runs along N so a wave reads 64 consecutive B
 // floats and one broadcast A float per k.  The sum runs in ascending k with
 // one rounding per fused multiply-add.  Kept as the bring-up and
-// cross-check kernel, not a performance path.
+// cross-check kernel, not a performance path.  Operands stored transposed
+// only change the strides: op(A)[i][k] steps by 1 in k (lda when
+// transposed), op(B)[k][j] by ldb in k (1 when transposed).
 constexpr int kNaiveX = 64;
 constexpr int kNaiveY = 4;
 
@@ -26,11 +29,13 @@ void naive_gemm_kernel(GemmArgs g) {
     const int64_t i = (t / tiles_n) * kNaiveY + threadIdx.y;
     const int64_t j = (t % tiles_n) * kNaiveX + threadIdx.x;
     if (i >= g.M || j >= g.N) return;
-    const float* a = g.A + i * g.lda;
-    const float* b = g.B + j;
+    const float* a = g.trans_a ? g.A + i : g.A + i * g.lda;
+    const int64_t sa = g.trans_a ? g.lda : 1;
+    const float* b = g.trans_b ? g.B + j * g.ldb : g.B + j;
+    const int64_t sb = g.trans_b ? 1 : g.ldb;
     float acc = 0.f;
-    for (int k = 0; k < g.K; ++k) acc = __builtin_fmaf(a[k], b[(int64_t)k * g.ldb], acc);
-    g.C[i * g.ldc + j] = acc;
+    for (int k = 0; k < g.K; ++k) acc = __builtin_fmaf(a[k * sa], b[k * sb], acc);
+    store_scaled(g.C + i * g.ldc + j, acc, g.alpha, g.beta);
 }
 
 // Deterministic split-K reduction: each output is the sum of the slices'
@@ -43,7 +48,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256)
 void splitk_reduce_kernel(const float* __restrict__ W, int64_t ldw, int64_t w_slice, int splits,
-                          float* __restrict__ C, int64_t ldc, int32_t M, int32_t N) {
+                          float* __restrict__ C, int64_t ldc, int32_t M, int32_t N, float alpha, float beta) {
     const int64_t groups_per_row = ldw / 4;
     const int64_t total = (int64_t)M * groups_per_row;
     for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total;
@@ -55,21 +60,22 @@ void splitk_reduce_kernel(const float* __restrict__ W, int64_t ldw, int64_t w_sl
         f32x4 s = *reinterpret_cast<const f32x4*>(w);
         for (int z = 1; z < splits; ++z) s += *reinterpret_cast<const f32x4*>(w + z * w_slice);
         float* c = C + i * ldc + j;
-        c[0] = s[0];
-        if (j + 1 < N) c[1] = s[1];
-        if (j + 2 < N) c[2] = s[2];
-        if (j + 3 < N) c[3] = s[3];
+        store_scaled(c, s[0], alpha, beta);
+        if (j + 1 < N) store_scaled(c + 1, s[1], alpha, beta);
+        if (j + 2 < N) store_scaled(c + 2, s[2], alpha, beta);
+        if (j + 3 < N) store_scaled(c + 3, s[3], alpha, beta);
     }
 }
 
 __global__ __launch_bounds__(256)
-void fill_zero_kernel(float* __restrict__ C, int64_t ldc, int32_t M, int32_t N) {
+void scale_kernel(float* __restrict__ C, int64_t ldc, int32_t M, int32_t N, float beta) {
     const int64_t total = (int64_t)M * N;
     for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total;
          v += (int64_t)gridDim.x * blockDim.x) {
         const int64_t i = v / N;
         const int64_t j = v - i * N;
-        C[i * ldc + j] = 0.f;
+        float* p = C + i * ldc + j;
+        *p = beta != 0.f ? beta * *p : 0.f;
     }
 }
 
@@ -148,12 +154,18 @@ void streamk_fixup_kernel(GemmArgs g, int bm, int bn) {
         if (m0 + i >= g.M || n0 + c >= g.N) continue;
         float* crow = g.C + (int64_t)(m0 + i) * g.ldc + n0 + c;
         if (vec_c && n0 + c + 3 < g.N) {
-            *reinterpret_cast<f32x4*>(crow) = s[u];
+            f32x4 v = g.alpha * s[u];
+            if (g.beta != 0.f) {
+                const f32x4 old = *reinterpret_cast<const f32x4*>(crow);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(g.beta, old[q], v[q]);
+            }
+            *reinterpret_cast<f32x4*>(crow) = v;
         } else {
-            crow[0] = s[u][0];
-            if (n0 + c + 1 < g.N) crow[1] = s[u][1];
-            if (n0 + c + 2 < g.N) crow[2] = s[u][2];
-            if (n0 + c + 3 < g.N) crow[3] = s[u][3];
+            store_scaled(crow, s[u][0], g.alpha, g.beta);
+            if (n0 + c + 1 < g.N) store_scaled(crow + 1, s[u][1], g.alpha, g.beta);
+            if (n0 + c + 2 < g.N) store_scaled(crow + 2, s[u][2], g.alpha, g.beta);
+            if (n0 + c + 3 < g.N) store_scaled(crow + 3, s[u][3], g.alpha, g.beta);
         }
     }
 }
@@ -175,10 +187,11 @@ hipError_t launch_naive(const GemmArgs& g, hipStream_t stream) {
 }
 
 hipError_t launch_splitk_reduce(const float* W, int64_t ldw, int64_t w_slice, int splits,
-                                float* C, int64_t ldc, int32_t M, int32_t N, hipStream_t stream) {
+                                float* C, int64_t ldc, int32_t M, int32_t N, float alpha, float beta,
+                                hipStream_t stream) {
     const int64_t items = (int64_t)M * (ldw / 4);
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for(items, 256)), dim3(256), 0, stream,
-                       W, ldw, w_slice, splits, C, ldc, M, N);
+                       W, ldw, w_slice, splits, C, ldc, M, N, alpha, beta);
     return hipGetLastError();
 }
 
@@ -198,9 +211,8 @@ hipError_t launch_pack(const float* src, int64_t ld, int32_t rows, int32_t cols,
     return hipGetLastError();
 }
 
-hipError_t launch_fill_zero(float* C, int64_t ldc, int32_t M, int32_t N, hipStream_t stream) {
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for((int64_t)M * N, 256)), dim3(256), 0, stream,
-                       C, ldc, M, N);
+hipError_t launch_scale(float* C, int64_t ldc, int32_t M, int32_t N, float beta, hipStream_t stream) {
+    hipLaunchKernelGGL(scale_kernel, dim3(grid_for((int64_t)M * N, 256)), dim3(256), 0, stream, C, ldc, M, N, beta);
     return hipGetLastError();
 }
 

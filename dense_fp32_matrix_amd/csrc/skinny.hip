@@ -140,9 +140,11 @@ void skinny_gemm_kernel(GemmArgs g) {
     for (int w = 1; w < WAVES; ++w) s4 += *reinterpret_cast<const f32x4*>(&red[w][i][c4]);
     if (i < g.M) {
         float* crow = g.C + (int64_t)blockIdx.z * g.c_slice + (int64_t)i * g.ldc;
+        const float alpha = g.c_slice ? 1.f : g.alpha;    // slices are raw partial sums
+        const float beta = g.c_slice ? 0.f : g.beta;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            if (n_w + c4 + c < g.N) crow[n_w + c4 + c] = s4[c];
+            if (n_w + c4 + c < g.N) store_scaled(crow + n_w + c4 + c, s4[c], alpha, beta);
     }
 }
 

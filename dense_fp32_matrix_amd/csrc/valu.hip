@@ -183,6 +183,8 @@ void valu_gemm_kernel(GemmArgs g) {
     }
 
     float* C = g.C + (int64_t)blockIdx.z * g.c_slice;
+    const float alpha = g.c_slice ? 1.f : g.alpha;    // slices are raw partial sums
+    const float beta = g.c_slice ? 0.f : g.beta;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int gi = m0 + wm * 64 + (i < 4 ? 4 * lr + i : 32 + 4 * lr + (i - 4));
@@ -191,7 +193,7 @@ void valu_gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int gj = n0 + wn * 64 + (j < 4 ? 4 * lc + j : 32 + 4 * lc + (j - 4));
-            if (gj < g.N) crow[gj] = acc[i][j];
+            if (gj < g.N) store_scaled(crow + gj, acc[i][j], alpha, beta);
         }
     }
 }

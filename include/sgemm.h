@@ -161,6 +161,54 @@ sgemm_status sgemm_plan_query(int64_t M, int64_t N, int64_t K,
                               const float* C, int64_t ldc,
                               const sgemm_options* opts, sgemm_plan* plan);
 
+/*
+ * The library-call form ("GEMM from naive to tiled", section 二.2, which
+ * follows torch.matmul down to the BLAS call with operation flags, alpha
+ * and beta; the epilogue of section 九.2 applies alpha and beta):
+ *
+ *     C = alpha * op(A) * op(B) + beta * C,     op(X) = X or X^T,
+ *
+ * all matrices row-major, op(A) M x K, op(B) K x N, C M x N:
+ *   op_a = SGEMM_OP_N: A stored M x K, op(A)[i][k] = A[i*lda + k], lda >= max(1, K)
+ *   op_a = SGEMM_OP_T: A stored K x M, op(A)[i][k] = A[k*lda + i], lda >= max(1, M)
+ *   op_b = SGEMM_OP_N: B stored K x N, op(B)[k][j] = B[k*ldb + j], ldb >= max(1, N)
+ *   op_b = SGEMM_OP_T: B stored N x K, op(B)[k][j] = B[j*ldb + k], ldb >= max(1, K)
+ * (so nn.Linear's X . W^T is op_a = N, op_b = T with W stored N x K).
+ * Scalars follow BLAS: with beta == 0, C is not read (whatever it holds,
+ * NaN included, is overwritten); with alpha == 0 or K == 0, A and B are not
+ * read (they may be NULL) and C = beta * C.  The arithmetic is that of
+ * sgemm for the sum, then one rounding for alpha * sum and one for the
+ * fused beta * C + (alpha * sum).  sgemm(...) is sgemm_gemm(N, N, ..., 1,
+ * ..., 0, ...).  C may not overlap A or B when they are read; errors,
+ * streams and workspace as for sgemm / sgemm_ex.  Operands stored
+ * transposed are read by the matrix-core path (or the naive path when
+ * forced); forcing the VALU or skinny path with them is SGEMM_ERR_INVALID_ARG.
+ */
+typedef enum sgemm_op {
+    SGEMM_OP_N = 0,   /* the operand as stored */
+    SGEMM_OP_T = 1    /* the transpose of the stored operand */
+} sgemm_op;
+
+sgemm_status sgemm_gemm(int32_t op_a, int32_t op_b, int64_t M, int64_t N, int64_t K, float alpha,
+                        const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                        float* C, int64_t ldc, hipStream_t stream);
+
+/* sgemm_gemm with explicit options (opts may be NULL). */
+sgemm_status sgemm_gemm_ex(int32_t op_a, int32_t op_b, int64_t M, int64_t N, int64_t K, float alpha,
+                           const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                           float* C, int64_t ldc, hipStream_t stream, const sgemm_options* opts);
+
+/* The plan sgemm_gemm_ex would use.  Host only, no HIP call. */
+sgemm_status sgemm_gemm_plan_query(int32_t op_a, int32_t op_b, int64_t M, int64_t N, int64_t K, float alpha,
+                                   const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                                   const float* C, int64_t ldc, const sgemm_options* opts,
+                                   sgemm_plan* plan);
+
+/* Scratch bytes the default plan of sgemm_gemm would need for 16-byte
+ * aligned base pointers and these leading dimensions.  Host only. */
+size_t sgemm_gemm_workspace_size(int32_t op_a, int32_t op_b, int64_t M, int64_t N, int64_t K,
+                                 int64_t lda, int64_t ldb, int64_t ldc);
+
 /* Scratch bytes the default plan of sgemm would need for 16-byte aligned
  * base pointers and these leading dimensions (0 when it neither packs nor
  * splits K).  Host only. */

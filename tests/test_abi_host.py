@@ -75,6 +75,50 @@ def test_invalid_arguments_rejected_before_hip(args, status):
     assert lib.sgemm_raw(*args, stream=0, opts=lib._options()) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    ((2, 0, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4), 1),       # op_a not N or T
+    ((0, -1, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4), 1),      # op_b not N or T
+    ((1, 0, 8, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4), 1),       # A stored K x M needs lda >= M
+    ((0, 1, 4, 4, 8, 1.0, A, 8, B, 4, 0.0, C, 4), 1),       # B stored N x K needs ldb >= K
+    ((0, 1, 4, 4, 8, 1.0, A, 8, B, 8, 0.0, C + 2, 4), 1),   # C misaligned
+    ((1, 1, 4, 4, 4, 1.0, 0, 4, B, 4, 0.0, C, 4), 1),       # A NULL while read
+    ((0, 0, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, A + 8, 4), 1),   # C overlaps A
+])
+def test_gemm_invalid_arguments(args, status):
+    assert lib.gemm_raw(*args, stream=0) == status
+
+
+def test_gemm_plans():
+    """Operand layouts and scalars in the plan: transposed operands run on the
+    direct-to-LDS tiles; alpha == 0 or K == 0 is one scaling launch that
+    reads neither A nor B (NULL allowed); the alignment rule follows each
+    operand's contiguous dimension."""
+    M, N, K = 8192, 11008, 4096
+    p = lib.gemm_plan_query("N", "T", M, N, K)                   # nn.Linear: X . W^T
+    assert p["path_name"] == "mfma" and p["tile"] in (8, 11) and p["vector"] == 1 and p["packed"] == 0
+    for ops in [("T", "N"), ("T", "T"), ("N", "T")]:
+        q = lib.gemm_plan_query(*ops, 4096, 4096, 4096)
+        assert q["tile"] in (8, 11) and q["vector"] == 1
+    # alpha == 0: C = beta * C only, A and B may be NULL
+    q = lib.gemm_plan_query("N", "N", 64, 64, 64, alpha=0.0, A=0, B=0, beta=2.0)
+    assert q["launches"] == 1 and q["workspace_bytes"] == 0
+    # k-major operands (A stored K x M, B stored K x N) need no K padding for odd K
+    q = lib.gemm_plan_query("T", "N", 512, 512, 511, path="mfma", tile=11, split_k=1, decomposition="tiles")
+    assert q["vector"] == 1 and q["packed"] == 0 and q["k_padded"] == 511
+    # odd K with a k-contiguous operand: pads K, packs both
+    q = lib.gemm_plan_query("N", "T", 512, 512, 511, path="mfma", tile=11, split_k=1, decomposition="tiles",
+                            pack="always")
+    assert q["packed"] == 3 and q["k_padded"] == 512
+    # the paths that read row-major operands only, and tiles without transposed variants
+    for kw in ({"path": "valu"}, {"path": "skinny"}, {"path": "mfma", "tile": 3}):
+        with pytest.raises(lib.SgemmError):
+            lib.gemm_plan_query("N", "T", 16, 512, 512, **kw)
+    assert lib.gemm_plan_query("T", "T", 300, 200, 20, path="naive")["path_name"] == "naive"
+    # M <= 16 with a transposed operand: the MFMA path, not the skinny one
+    assert lib.gemm_plan_query("N", "T", 16, 11008, 4096)["path_name"] == "mfma"
+    assert lib.gemm_workspace_size("N", "T", M, N, K) == p["workspace_bytes"]
+
+
 def test_bad_options_rejected():
     base = (64, 64, 64, A, 64, B, 64, C, 64)
     assert lib.sgemm_raw(*base, opts=lib._options(path=7)) == 1
