@@ -59,6 +59,11 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+template <bool V>
+struct BoolC {
+    static constexpr bool value = V;
+};
+
 template <int V>
 struct IntC {
     static constexpr int value = V;
@@ -461,28 +466,37 @@ struct DtlStageFloats<true, OPS, BM, BN, BK> {
 };
 
 // The direct loads of one operand that one wave issues per K-step: PER
-// instructions, ins = i * waves + wave, with per-lane sources fixed over the
-// K loop.  r0 is the tile's first non-K index and lim its bound (M or N);
-// lanes past the bound, or past the K range, read the zero block.
+// instructions, ins = i * waves + wave.  Each keeps a running per-lane
+// source pointer that one issue advances by one K-step (steps are issued in
+// order), so a step inside the K range costs one 64-bit add per load.
+// r0 is the tile's first non-K index and lim its bound (M or N): lanes past
+// it read the last valid row or column instead, which only reaches outputs
+// outside C that are never written.  Only the K range needs the zero block,
+// on the steps that cross its end (checked()).
 template <class L, int PER>
 struct DtlLoads {
-    int64_t off[PER];
+    const float* ptr[PER];
     int kk[PER];
-    bool ok[PER];
-    __device__ __forceinline__ void init(int wave, int waves, int lane, int64_t ld, int r0, int lim) {
+    int64_t step;
+    __device__ __forceinline__ void init(const float* X, int64_t ld, int wave, int waves, int lane, int r0, int lim,
+                                         int kb, int bk) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             int r, k;
             L::elem(i * waves + wave, lane, r, k);
-            ok[i] = r0 + r < lim;
-            const int rr = ok[i] ? r0 + r : 0;
-            off[i] = L::KC ? (int64_t)rr * ld + k : (int64_t)k * ld + rr;
+            const int rr = min(r0 + r, lim - 1);
+            ptr[i] = X + (L::KC ? (int64_t)rr * ld + kb + k : (int64_t)(kb + k) * ld + rr);
             kk[i] = k;
         }
+        step = L::KC ? (int64_t)bk : (int64_t)bk * ld;
     }
-    // base_k0: the operand advanced to K-step start k0 (k0 columns for KC, k0 rows for KM)
-    __device__ __forceinline__ const float* src(const float* base_k0, int i, int k0, int ke) const {
-        return ok[i] && (k0 + kk[i] < ke) ? base_k0 + off[i] : kZeroMfma;
+    // source of load i for the step starting at k0, zero block past ke
+    __device__ __forceinline__ const float* checked(int i, int k0, int ke) const {
+        return k0 + kk[i] < ke ? ptr[i] : kZeroMfma;
+    }
+    __device__ __forceinline__ void advance() {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) ptr[i] += step;
     }
 };
 
@@ -531,7 +545,7 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
     constexpr int B_PER = LB::INSTR / WAVES;
     constexpr int LOADS = A_PER + B_PER;                 // per lane per K-step
     static_assert(A_PER * WAVES == LA::INSTR && B_PER * WAVES == LB::INSTR, "instructions per wave");
-    static_assert(DS == 3 || DS == 4, "three or four stages");
+    static_assert(DS >= 2 && DS <= 4, "two to four stages");
     static_assert((DS - 2) * LOADS < 64, "loads in flight fit the vmcnt counter");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -544,19 +558,22 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
 
     DtlLoads<LA, A_PER> la;
     DtlLoads<LB, B_PER> lb;
-    la.init(wave, WAVES, lane, g.lda, m0, g.M);
-    lb.init(wave, WAVES, lane, g.ldb, n0, g.N);
+    la.init(g.A, g.lda, wave, WAVES, lane, m0, g.M, kb, BK);
+    lb.init(g.B, g.ldb, wave, WAVES, lane, n0, g.N, kb, BK);
 
-    // issue the direct loads of K-step `step` into stage `st`
-    auto issue = [&](int step, float* st) {
+    // issue the direct loads of the next K-step (`step`) into stage `st`;
+    // FULL: the whole step lies inside [kb, ke), so no lane needs the check
+    auto issue = [&](int step, float* st, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
         const int k0 = kb + step * BK;
-        const float* abase = g.A + (LA::KC ? (int64_t)k0 : (int64_t)k0 * g.lda);
-        const float* bbase = g.B + (LB::KC ? (int64_t)k0 : (int64_t)k0 * g.ldb);
 #pragma unroll
-        for (int i = 0; i < A_PER; ++i) dma_lanes<W>(la.src(abase, i, k0, ke), st + LA::dst(i * WAVES + wave));
+        for (int i = 0; i < A_PER; ++i)
+            dma_lanes<W>(FULL ? la.ptr[i] : la.checked(i, k0, ke), st + LA::dst(i * WAVES + wave));
 #pragma unroll
         for (int i = 0; i < B_PER; ++i)
-            dma_lanes<W>(lb.src(bbase, i, k0, ke), st + LA::FLOATS + LB::dst(i * WAVES + wave));
+            dma_lanes<W>(FULL ? lb.ptr[i] : lb.checked(i, k0, ke), st + LA::FLOATS + LB::dst(i * WAVES + wave));
+        la.advance();
+        lb.advance();
     };
 
     f32x16 acc[P::MB][P::NB];
@@ -628,22 +645,22 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
     };
     if (steps > 0) {
 #pragma unroll
-        for (int j = 0; j + 1 < DS; ++j) issue(j, stg[j]);
+        for (int j = 0; j + 1 < DS; ++j) issue(j, stg[j], BoolC<false>{});
         dtl_barrier<(DS - 2) * LOADS>();
         read_frags(stg[0], 0, 0);
-        issue(DS - 1, stg[DS - 1]);
+        issue(DS - 1, stg[DS - 1], BoolC<false>{});
 #pragma unroll
         for (int kg = 0; kg + 1 < P::KG; ++kg) {
             read_frags(stg[0], kg + 1, (kg + 1) & 1);
             mfmas(kg & 1);
         }
-        // iteration s uses stage s % DS and refills stage (s - 1) % DS
-        auto iter = [&](int s, auto j_tag) {
+        // iteration s uses stage s % DS and refills stage (s - 1) % DS with step s + DS - 1
+        auto iter = [&](int s, auto j_tag, auto full_tag) {
             constexpr int J = decltype(j_tag)::value;
             dtl_barrier<(DS - 2) * LOADS>();
             read_frags(stg[J], 0, 0);
             mfmas(1);
-            issue(s + DS - 1, stg[(J + DS - 1) % DS]);
+            issue(s + DS - 1, stg[(J + DS - 1) % DS], full_tag);
 #pragma unroll
             for (int kg = 0; kg + 1 < P::KG; ++kg) {
                 read_frags(stg[J], kg + 1, (kg + 1) & 1);
@@ -652,18 +669,36 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
             if constexpr (SCHED)
                 interleave_hints<P::MB * P::NB * 4, P::MB + 2 * P::NB, 0, P::KG, 8 * (SCHED - 1)>();
         };
+        // Unrolled by DS so that every iteration names its stages statically.
+        // The first loop runs whole trips of iterations whose refill step lies
+        // inside the K range (s + DS - 1 < full_steps); the second finishes
+        // with the checked loads (and the loads past the end, which read zeros).
+        // (4-byte lanes, with 8x the loads, keep one checked loop: a second
+        // copy of the loop would not fit their registers.)
         int s = 1;
+        if constexpr (W == 4) {
+            const int full_steps = (ke - kb) / BK;
+            const int fast_trips = full_steps > DS ? (full_steps - DS) / DS : 0;
+            for (int t = 0; t < fast_trips; ++t) {
+                iter(s++, IntC<1>{}, BoolC<true>{});
+                if constexpr (DS > 2) iter(s++, IntC<2>{}, BoolC<true>{});
+                if constexpr (DS > 3) iter(s++, IntC<3>{}, BoolC<true>{});
+                iter(s++, IntC<0>{}, BoolC<true>{});
+            }
+        }
         while (true) {
             if (s >= steps) break;
-            iter(s++, IntC<1 % DS>{});
-            if (s >= steps) break;
-            iter(s++, IntC<2 % DS>{});
-            if (s >= steps) break;
-            iter(s++, IntC<3 % DS>{});
-            if constexpr (DS == 4) {
+            iter(s++, IntC<1>{}, BoolC<false>{});
+            if constexpr (DS > 2) {
                 if (s >= steps) break;
-                iter(s++, IntC<0>{});
+                iter(s++, IntC<2>{}, BoolC<false>{});
             }
+            if constexpr (DS > 3) {
+                if (s >= steps) break;
+                iter(s++, IntC<3>{}, BoolC<false>{});
+            }
+            if (s >= steps) break;
+            iter(s++, IntC<0>{}, BoolC<false>{});
         }
         mfmas(1);
         wait_vmcnt<0>();                     // loads issued past the end land before the LDS is reused
@@ -696,55 +731,71 @@ void mfma_gemm_kernel(GemmArgs g) {
     // are 16-byte aligned, else 4-byte lanes, which keep three stages so
     // that the loads in flight fit the vmcnt counter)
     constexpr bool DTL = DS > 0;
-    constexpr int DSE = VEC ? DS : 3;
+    constexpr int DSE = VEC || DS < 3 ? DS : 3;
     constexpr int W = VEC ? 4 : 1;
     constexpr int QS = DtlStageFloats<DTL, OPS, BM, BN, BK>::value;
     __shared__ __attribute__((aligned(16))) float lds0[DTL ? QS : 2 * P::STAGE];
     __shared__ __attribute__((aligned(16))) float lds1[DTL ? QS : 4];
-    __shared__ __attribute__((aligned(16))) float lds2[DTL ? QS : 4];
+    __shared__ __attribute__((aligned(16))) float lds2[DTL && DSE > 2 ? QS : 4];
     __shared__ __attribute__((aligned(16))) float lds3[DTL && DSE > 3 ? QS : 4];
-    int tm, tn;
-    if (g.sk_iters == 0) {
-        tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
-        const int kb = blockIdx.z * g.k_chunk;
-        const int ke = min(g.K, kb + g.k_chunk);
-        // one slice writes alpha * sum + beta * C; several write raw partial sums
-        const TileOut o{g.C + (int64_t)blockIdx.z * g.c_slice, g.ldc, tm * BM, tn * BN, g.M, g.N,
+    // One call site for every work item, so that a single copy of the tile
+    // code serves all decompositions: (tile, slice) in the one-tile mode;
+    // the data-parallel tiles, then the K-step ranges, in stream-K mode.
+    int64_t it = (int64_t)blockIdx.x * g.sk_ipw;                // stream-K: next (tile, K-step) unit
+    const int64_t it_end = min(it + g.sk_ipw, g.sk_iters);
+    int t = blockIdx.x;                                          // stream-K: next data-parallel tile
+    int which = 0;                                               // stream-K: partial slot 0, then 1
+    bool first = true;
+    while (true) {
+        int tile, kb, ke;
+        TileOut o;
+        int64_t step = 0;                                        // K-steps this item covers (stream-K ranges)
+        bool slot = false;                                       // a partial tile, written to its slot
+        if (g.sk_iters == 0) {
+            if (!first) break;
+            tile = blockIdx.x;
+            kb = blockIdx.z * g.k_chunk;
+            ke = min(g.K, kb + g.k_chunk);
+            // one slice writes alpha * sum + beta * C; several write raw partial sums
+            o = TileOut{g.C + (int64_t)blockIdx.z * g.c_slice, g.ldc, 0, 0, g.M, g.N,
                         g.c_slice ? 1.f : g.alpha, g.c_slice ? 0.f : g.beta};
+        } else if (t < g.dp_tiles) {
+            tile = t;
+            t += gridDim.x;
+            kb = 0;
+            ke = g.K;
+            o = TileOut{g.C, g.ldc, 0, 0, g.M, g.N, g.alpha, g.beta};
+        } else if (it < it_end) {
+            const int j = (int)(it / g.k_steps);
+            const int ks0 = (int)(it - (int64_t)j * g.k_steps);
+            const int ks1 = (int)min((int64_t)g.k_steps, ks0 + (it_end - it));
+            tile = g.dp_tiles + j;
+            kb = ks0 * BK;
+            ke = min(g.K, ks1 * BK);
+            if (ks0 == 0 && ks1 == g.k_steps) {
+                o = TileOut{g.C, g.ldc, 0, 0, g.M, g.N, g.alpha, g.beta};
+            } else {
+                // slot 0 for the range's first tile, 1 for its last (the
+                // fix-up picks the slot the same way)
+                o = TileOut{g.ws + (int64_t)(2 * blockIdx.x + which) * (BM * BN), BN, 0, 0, BM, BN};
+                slot = true;
+            }
+            which = 1;
+            step = ks1 - ks0;
+        } else {
+            break;
+        }
+        int tm, tn;
+        tile_coords(tile, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
+        if (!slot) {
+            o.row0 = tm * BM;                                    // C (or a split-K slice): the tile's place
+            o.col0 = tn * BN;
+        }
+        if (!first) __syncthreads();                             // the next tile's prologue overwrites LDS
+        first = false;
         if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W, OPS>(g, lds0, lds1, lds2, lds3, tm, tn, kb, ke, o);
         else mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, lds0, tm, tn, kb, ke, o);
-        return;
-    }
-    for (int t = blockIdx.x; t < g.dp_tiles; t += gridDim.x) {
-        tile_coords(t, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
-        const TileOut o{g.C, g.ldc, tm * BM, tn * BN, g.M, g.N, g.alpha, g.beta};
-        if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W, OPS>(g, lds0, lds1, lds2, lds3, tm, tn, 0, g.K, o);
-        else mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, lds0, tm, tn, 0, g.K, o);
-        __syncthreads();                 // the next tile's prologue overwrites LDS
-    }
-    int64_t it = (int64_t)blockIdx.x * g.sk_ipw;
-    const int64_t it_end = min(it + g.sk_ipw, g.sk_iters);
-    int which = 0;
-    while (it < it_end) {
-        const int j = (int)(it / g.k_steps);
-        const int ks0 = (int)(it - (int64_t)j * g.k_steps);
-        const int ks1 = (int)min((int64_t)g.k_steps, ks0 + (it_end - it));
-        tile_coords(g.dp_tiles + j, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
-        const int kb = ks0 * BK;
-        const int ke = min(g.K, ks1 * BK);
-        if (ks0 == 0 && ks1 == g.k_steps) {
-            const TileOut o{g.C, g.ldc, tm * BM, tn * BN, g.M, g.N, g.alpha, g.beta};
-            if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W, OPS>(g, lds0, lds1, lds2, lds3, tm, tn, kb, ke, o);
-        else mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, lds0, tm, tn, kb, ke, o);
-        } else {
-            float* slot = g.ws + (int64_t)(2 * blockIdx.x + which) * (BM * BN);
-            const TileOut o{slot, BN, 0, 0, BM, BN};
-            if constexpr (DTL) mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W, OPS>(g, lds0, lds1, lds2, lds3, tm, tn, kb, ke, o);
-        else mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, lds0, tm, tn, kb, ke, o);
-        }
-        __syncthreads();
-        which = 1;
-        it += ks1 - ks0;
+        it += step;
     }
 }
 
