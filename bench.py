@@ -209,7 +209,7 @@ def main():
                    "inputs": f"A~{w.a_kind}, B~{w.b_kind}", "path": plan["path_name"], "tile": plan["tile"],
                    "bm": plan["bm"], "bn": plan["bn"], "bk": plan["bk"], "split_k": plan["split_k"],
                    "decomposition": plan["decomposition_name"],
-                   "vector_loads": bool(plan["vector"]), "workgroups": plan["workgroups"]},
+                   "vector_loads": bool(plan["vector"]), "packed": plan["packed"], "workgroups": plan["workgroups"]},
         "roofline": roof,
         "cpu_baseline": cpu,
         "flushed_launch_ms_median": statistics.median(fl),
