@@ -52,7 +52,9 @@ struct Plan {
     // packing: the matrix kernel reads the packed copies of A and B (their
     // stored orientation, K padded to kp) from the workspace at these offsets
     int64_t kp = 0;
-    int64_t a_rows = 0, a_cols = 0, b_rows = 0, b_cols = 0;   // packed stored shapes (leading dimension = cols)
+    int64_t a_rows = 0, a_cols = 0, b_rows = 0, b_cols = 0;   // packed stored shapes
+    int64_t a_ld = 0, b_ld = 0;   // their leading dimensions: cols rounded up to 128 bytes, so that
+                                  // every row starts on a cache line
     size_t pack_a_off = 0, pack_b_off = 0, gemm_ws_off = 0;
 };
 
@@ -375,8 +377,10 @@ sgemm_status make_plan(const Call& c, const sgemm_options* opts, Plan* out) {
                 p.kp = kp;
                 p.a_rows = ar;
                 p.a_cols = ac;
+                p.a_ld = round_up(ac, 32);
                 p.b_rows = br;
                 p.b_cols = bc;
+                p.b_ld = round_up(bc, 32);
             }
         }
     } else {   // VALU
@@ -436,11 +440,11 @@ sgemm_status make_plan(const Call& c, const sgemm_options* opts, Plan* out) {
     size_t off = 0;
     if (q.packed & 1) {
         p.pack_a_off = off;
-        off += align256((size_t)(p.a_rows * p.a_cols) * sizeof(float));
+        off += align256((size_t)(p.a_rows * p.a_ld) * sizeof(float));
     }
     if (q.packed & 2) {
         p.pack_b_off = off;
-        off += align256((size_t)(p.b_rows * p.b_cols) * sizeof(float));
+        off += align256((size_t)(p.b_rows * p.b_ld) * sizeof(float));
     }
     p.gemm_ws_off = off;
     q.workspace_bytes = gemm_ws > 0 ? off + gemm_ws : off;
@@ -483,17 +487,17 @@ sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_option
     hipError_t e = hipSuccess;
     if (q.packed & 1) {
         float* Ap = reinterpret_cast<float*>(wsb + p.pack_a_off);
-        e = launch_pack(A, lda, (int32_t)c.a_rows(), (int32_t)c.a_cols(), Ap, (int32_t)p.a_rows, (int32_t)p.a_cols,
-                        stream);
+        e = launch_pack(A, lda, (int32_t)c.a_rows(), (int32_t)c.a_cols(), Ap, p.a_ld, (int32_t)p.a_rows,
+                        (int32_t)p.a_cols, stream);
         A = Ap;
-        lda = p.a_cols;
+        lda = p.a_ld;
     }
     if (e == hipSuccess && (q.packed & 2)) {
         float* Bp = reinterpret_cast<float*>(wsb + p.pack_b_off);
-        e = launch_pack(B, ldb, (int32_t)c.b_rows(), (int32_t)c.b_cols(), Bp, (int32_t)p.b_rows, (int32_t)p.b_cols,
-                        stream);
+        e = launch_pack(B, ldb, (int32_t)c.b_rows(), (int32_t)c.b_cols(), Bp, p.b_ld, (int32_t)p.b_rows,
+                        (int32_t)p.b_cols, stream);
         B = Bp;
-        ldb = p.b_cols;
+        ldb = p.b_ld;
     }
     void* const gws = q.workspace_bytes > p.gemm_ws_off ? static_cast<void*>(wsb + p.gemm_ws_off) : nullptr;
 

@@ -133,10 +133,10 @@ hipError_t launch_streamk_fixup(const GemmArgs& g, int bm, int bn, int sk_tiles,
 // C = beta * C (C not read when beta == 0): the whole product when alpha == 0 or K == 0.
 hipError_t launch_scale(float* C, int64_t ldc, int32_t M, int32_t N, float beta, hipStream_t stream);
 
-// dst (rows_p x cols_p, leading dimension cols_p % 4 == 0, 16-byte aligned) =
-// src (rows x cols, leading dimension ld) zero-padded.
-hipError_t launch_pack(const float* src, int64_t ld, int32_t rows, int32_t cols, float* dst, int32_t rows_p,
-                       int32_t cols_p, hipStream_t stream);
+// dst (rows_p x cols_p, leading dimension ldd >= cols_p, both multiples of 4,
+// 16-byte aligned) = src (rows x cols, leading dimension ld) zero-padded.
+hipError_t launch_pack(const float* src, int64_t ld, int32_t rows, int32_t cols, float* dst, int64_t ldd,
+                       int32_t rows_p, int32_t cols_p, hipStream_t stream);
 
 // Sixteen zero bytes in device memory, defined once per kernel source.  A
 // masked-off load (outside the matrix, or past the end of a K slice) reads

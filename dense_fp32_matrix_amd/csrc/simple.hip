@@ -81,14 +81,15 @@ void scale_kernel(float* __restrict__ C, int64_t ldc, int32_t M, int32_t N, floa
 
 // Packing: the rows x cols matrix src (leading dimension ld, any 4-byte
 // alignment) is copied into the rows_p x cols_p row-major dst (leading
-// dimension cols_p, a multiple of 4; dst 16-byte aligned), with zeros in the
+// dimension ldd >= cols_p, both multiples of 4; dst 16-byte aligned; columns
+// from cols_p to ldd are left alone, nothing reads them), with zeros in the
 // padding rows and columns.  The copy is exact, and the zeros only add +0
 // terms to the product, so the matrix kernel's 16-byte loaders can then run
 // on operands that were not aligned.  One thread writes one 16-byte group of
 // a row; blockIdx.y strides over the rows.
 __global__ __launch_bounds__(256)
 void pack_kernel(const float* __restrict__ src, int64_t ld, int32_t rows, int32_t cols,
-                 float* __restrict__ dst, int32_t rows_p, int32_t cols_p) {
+                 float* __restrict__ dst, int64_t ldd, int32_t rows_p, int32_t cols_p) {
     const int32_t c4 = (int32_t)blockIdx.x * 256 + (int32_t)threadIdx.x;
     if (4 * c4 >= cols_p) return;
     for (int32_t r = blockIdx.y; r < rows_p; r += gridDim.y) {
@@ -101,7 +102,7 @@ void pack_kernel(const float* __restrict__ src, int64_t ld, int32_t rows, int32_
             if (left > 2) v.z = s[2];
             if (left > 3) v.w = s[3];
         }
-        *reinterpret_cast<float4*>(dst + (int64_t)r * cols_p + 4 * c4) = v;
+        *reinterpret_cast<float4*>(dst + (int64_t)r * ldd + 4 * c4) = v;
     }
 }
 
@@ -203,11 +204,12 @@ hipError_t launch_streamk_fixup(const GemmArgs& g, int bm, int bn, int sk_tiles,
     return hipGetLastError();
 }
 
-hipError_t launch_pack(const float* src, int64_t ld, int32_t rows, int32_t cols, float* dst, int32_t rows_p,
-                       int32_t cols_p, hipStream_t stream) {
+hipError_t launch_pack(const float* src, int64_t ld, int32_t rows, int32_t cols, float* dst, int64_t ldd,
+                       int32_t rows_p, int32_t cols_p, hipStream_t stream) {
+    if (ldd < cols_p || ldd % 4 != 0 || cols_p % 4 != 0) return hipErrorInvalidValue;
     const unsigned gx = (unsigned)((cols_p / 4 + 255) / 256);
     const unsigned gy = (unsigned)std::min<int32_t>(rows_p, 65535);
-    hipLaunchKernelGGL(pack_kernel, dim3(gx, gy), dim3(256), 0, stream, src, ld, rows, cols, dst, rows_p, cols_p);
+    hipLaunchKernelGGL(pack_kernel, dim3(gx, gy), dim3(256), 0, stream, src, ld, rows, cols, dst, ldd, rows_p, cols_p);
     return hipGetLastError();
 }
 
