@@ -75,7 +75,7 @@ struct TileShape {
     int waves_per_simd;     // occupancy the register budget is sized for
     int sched = 1;          // >= 1: interleave LDS and global memory instructions between MFMAs,
                             // with 8 * (sched - 1) MFMAs after the last LDS write of a K-step
-    int dtl = 0;            // > 0: stages of the direct-to-LDS loader (16-byte aligned operands)
+    int dtl = 0;            // > 0: stages of the direct-to-LDS loader (3 at most with 4-byte lanes)
     bool trans = false;     // also instantiated for operands stored transposed (direct-to-LDS tiles only)
 };
 

@@ -5,13 +5,16 @@
 //   * Each workgroup owns one BM x BN tile of C (output-stationary, as in the
 //     throughput-matching page "如何让计算受限问题真正达到计算受限", section 1.2)
 //     and walks K in steps of BK.
-//   * Per K-step, the A tile (BM x BK) and B tile (BK x BN) go global -> VGPR
-//     -> LDS with coalesced loads; 16-byte loads when rows are 16-byte
-//     aligned, 4-byte loads otherwise; out-of-range elements are zero-filled
-//     (the padding argument of section 七: a zero term leaves the sum alone).
-//   * Two LDS stages: the loads of step t+1 are issued before step t is
-//     computed and land in the other stage afterwards, so one barrier per
-//     K-step suffices (section 六.1; "SGEMM 纯 CUDA 优化总结", ex9).
+//   * Per K-step, the A tile (BM x BK) and B tile (BK x BN) reach LDS either
+//     straight from global memory (the direct-to-LDS tiles, the default; see
+//     mfma_tile_dtl) or through registers with coalesced loads (the
+//     register-staged tiles described here); out-of-range elements are
+//     zero-filled (the padding argument of section 七: a zero term leaves the
+//     sum alone).
+//   * Register-staged: two LDS stages; the loads of step t+1 are issued
+//     before step t is computed and land in the other stage afterwards, so
+//     one barrier per K-step suffices (section 六.1; "SGEMM 纯 CUDA 优化总结",
+//     ex9).
 //   * Each wave owns a WM x WN sub-tile as (WM/32) x (WN/32) blocks of
 //     v_mfma_f32_32x32x2_f32: true FP32 products, FP32 accumulation.
 //
@@ -25,7 +28,7 @@
 // is used once, and the A fragment of a lane is 4 consecutive k of one row,
 // read from LDS with a single 16-byte read.
 //
-// LDS layout, per stage:
+// LDS layout of the register-staged tiles, per stage:
 //   As[BM][BK]      row-major like A, no padding; the 16-byte chunk c of row
 //                   r is stored at chunk position c ^ swz(r).  The XOR
 //                   swizzle (one of the three bank-conflict fixes of "SGEMM
@@ -36,7 +39,8 @@
 //   Bs[BK][BN + 8]  row-major like B; the two lane halves read rows 4 apart,
 //                   offset by 4 * (BN + 8) = 32 (mod 64) banks.
 //
-// Schedule of one K-step t (stages alternate between two LDS buffers):
+// Schedule of one register-staged K-step t (stages alternate between two
+// LDS buffers):
 //   issue the global loads of step t+1;
 //   for each k-group but the last: read the next group's fragments from
 //     LDS, then issue this group's MFMAs;
