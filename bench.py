@@ -14,8 +14,11 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +75,22 @@ def load_traffic(kernel_key, digest):
     if not rec or rec.get("source_digest") != digest:
         return None
     return rec.get("bytes_per_launch")
+
+
+def sample_clocks(stop, out):
+    """rocm-smi readings (shader clock in MHz, package power in W) until stop is set."""
+    while not stop.is_set():
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--showpower"], capture_output=True, text=True,
+                               timeout=5)
+        except (OSError, subprocess.SubprocessError):
+            return
+        m = re.search(r"sclk clock level: \d+: \((\d+)Mhz\)", r.stdout)
+        if m:
+            out["sclk_mhz"].append(int(m.group(1)))
+        m = re.search(r"Package Power \(W\): ([0-9.]+)", r.stdout)
+        if m:
+            out["power_w"].append(float(m.group(1)))
 
 
 def cpu_baseline(w, A, B, target_s):
@@ -134,6 +153,28 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    # Clock and power while the workload runs: an untimed probe phase of
+    # about 1.5 s after the warmup steps, which also brings the clocks to
+    # their steady state before the timed region.
+    samples = {"sclk_mhz": [], "power_w": []}
+    stop = threading.Event()
+    th = threading.Thread(target=sample_clocks, args=(stop, samples))
+    th.start()
+    t_end = time.perf_counter() + 1.5
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    clocks = None
+    if samples["sclk_mhz"]:
+        tail = samples["sclk_mhz"][len(samples["sclk_mhz"]) // 2:]
+        clocks = {"sclk_mhz_median_2nd_half": statistics.median(tail), "sclk_mhz_min": min(samples["sclk_mhz"]),
+                  "sclk_mhz_max": max(samples["sclk_mhz"]), "samples": len(samples["sclk_mhz"]),
+                  "power_w_median": statistics.median(samples["power_w"]) if samples["power_w"] else None,
+                  "source": "rocm-smi during ~1.5 s of untimed steps before the timed region"}
 
     # timed region: K back-to-back steps, plus events around every step on the launch stream
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -212,6 +253,7 @@ def main():
                    "vector_loads": bool(plan["vector"]), "packed": plan["packed"], "workgroups": plan["workgroups"]},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "clocks": clocks,
         "flushed_launch_ms_median": statistics.median(fl),
         "flushed_tflops": flops / (statistics.median(fl) * 1e-3) / 1e12,
         "step_ms_min": min(per_step_ms),
