@@ -107,20 +107,22 @@ void pack_kernel(const float* __restrict__ src, int64_t ld, int32_t rows, int32_
 }
 
 // Stream-K fix-up (see the stream-K decomposition of the MFMA kernel):
-// workgroup (j, part) handles elements [part * kFixupChunk, (part + 1) *
-// kFixupChunk) of stream-K tile j, four 16-byte groups per thread so that
-// every thread has its loads in flight at once.  A tile whose K-steps fall in
-// one workgroup's range was written whole; otherwise its partial slots, from
-// workgroups w0..w1 in that order, are summed and the tile is written to C.
-constexpr int kFixupChunk = 4096;
-
+// workgroup (j, part) handles elements [part * 1024 U, (part + 1) * 1024 U)
+// of stream-K tile j, U 16-byte groups per thread; the loop over the
+// contributing slots is unrolled so that several loads per thread are in
+// flight (the sum itself stays in slot order).  U = 4 when a tile has few
+// contributors, U = 1 (four times the workgroups) when it has many.  A tile
+// whose K-steps fall in one workgroup's range was written whole; otherwise
+// its partial slots, from workgroups w0..w1 in that order, are summed and the
+// tile is written to C.
 constexpr bool fixup_chunks_fit() {
     for (const TileShape& t : kMfmaTiles)
-        if ((t.bm * t.bn) % kFixupChunk != 0) return false;
+        if ((t.bm * t.bn) % 4096 != 0) return false;
     return true;
 }
 static_assert(fixup_chunks_fit(), "every MFMA tile splits into whole fix-up chunks");
 
+template <int U>
 __global__ __launch_bounds__(256)
 void streamk_fixup_kernel(GemmArgs g, int bm, int bn) {
     const int j = blockIdx.x;
@@ -135,21 +137,22 @@ void streamk_fixup_kernel(GemmArgs g, int bm, int bn) {
     const int n0 = tn * bn;
     const int64_t slot = (int64_t)bm * bn;
     const bool vec_c = (g.ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(g.C) % 16 == 0);
-    f32x4 s[4];
-    int es[4];
+    f32x4 s[U];
+    int es[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        es[u] = (int)blockIdx.y * kFixupChunk + 4 * ((int)threadIdx.x + 256 * u);
+    for (int u = 0; u < U; ++u) {
+        es[u] = (int)blockIdx.y * (1024 * U) + 4 * ((int)threadIdx.x + 256 * u);
         s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll 4
     for (int w = w0; w <= w1; ++w) {
         const int which = (int64_t)w * g.sk_ipw >= first ? 0 : 1;
         const float* src = g.ws + (int64_t)(2 * w + which) * slot;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) s[u] += *reinterpret_cast<const f32x4*>(src + es[u]);
+        for (int u = 0; u < U; ++u) s[u] += *reinterpret_cast<const f32x4*>(src + es[u]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
         const int i = es[u] / bn;
         const int c = es[u] - i * bn;
         if (m0 + i >= g.M || n0 + c >= g.N) continue;
@@ -198,9 +201,15 @@ hipError_t launch_splitk_reduce(const float* W, int64_t ldw, int64_t w_slice, in
 
 hipError_t launch_streamk_fixup(const GemmArgs& g, int bm, int bn, int sk_tiles, hipStream_t stream) {
     // every tile shape holds a whole number of chunks
-    if ((bm * bn) % kFixupChunk != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(streamk_fixup_kernel, dim3((unsigned)sk_tiles, (unsigned)(bm * bn / kFixupChunk)), dim3(256),
-                       0, stream, g, bm, bn);
+    if ((bm * bn) % 4096 != 0) return hipErrorInvalidValue;
+    // workgroups contributing to one tile (at most): many -> smaller chunks, more workgroups
+    const int64_t contributors = (g.k_steps + g.sk_ipw - 1) / g.sk_ipw + 1;
+    if (contributors > 8)
+        hipLaunchKernelGGL(streamk_fixup_kernel<1>, dim3((unsigned)sk_tiles, (unsigned)(bm * bn / 1024)), dim3(256),
+                           0, stream, g, bm, bn);
+    else
+        hipLaunchKernelGGL(streamk_fixup_kernel<4>, dim3((unsigned)sk_tiles, (unsigned)(bm * bn / 4096)), dim3(256),
+                           0, stream, g, bm, bn);
     return hipGetLastError();
 }
 
