@@ -90,7 +90,7 @@ constexpr double kMacRate = 128.0 * 2.4e9;   // FP32 MACs per second per CU at p
 constexpr double kPartialBw = 4e12;          // bytes/s for split-K partial slices (mostly cache resident)
 constexpr double kStreamKBw = 1e13;          // bytes/s for stream-K partial tiles (written and read back
                                              // by neighbouring workgroups, cache resident)
-constexpr double kLaunch = 4e-6;             // one more dependent kernel launch
+constexpr double kLaunch = 6e-6;             // one more dependent kernel launch
 
 // Share of the CU's peak one tile shape sustains when its CU is full, with
 // 16-byte (vec) or 4-byte loaders.  The register-staged 4-byte loaders need
@@ -100,7 +100,7 @@ double mfma_efficiency(int tile, bool vec) {
     if (!vec) {
         switch (tile) {
             case 8: case 9: case 11: case 12: return 0.66;
-            case 10: return 0.58;
+            case 10: case 13: case 14: return 0.58;
             case 2: return 0.62;
             case 4: return 0.60;
             default: return 0.55;
@@ -110,11 +110,26 @@ double mfma_efficiency(int tile, bool vec) {
         case 11: case 12: return 0.92;
         case 8: return 0.91;
         case 9: return 0.905;
+        case 13: return 0.89;
+        case 14: return 0.885;
         case 3: case 6: return 0.89;
         case 10: return 0.87;
         case 0: case 1: case 7: return 0.85;
         case 2: case 5: return 0.83;
         default: return 0.70;
+    }
+}
+
+// Share of the CU's peak when the CU holds a single workgroup of a tile
+// built for two or more per CU (a tail shorter than one wave of
+// workgroups).  Direct-to-LDS tiles keep most of their rate alone;
+// register-staged ones depend on a second workgroup to hide their loads.
+double mfma_alone_efficiency(int tile, bool vec) {
+    const double e = mfma_efficiency(tile, vec);
+    switch (tile) {
+        case 13: return 0.79 * e;
+        case 2: return 0.75 * e;
+        default: return e;
     }
 }
 
@@ -143,9 +158,12 @@ Candidate tiles_candidate(int tile, bool vec, int64_t M, int64_t N, int64_t K, i
     const int64_t full_waves = wgs / (kNumCUs * per_cu);
     const int64_t tail = wgs - full_waves * kNumCUs * per_cu;
     const double wg_time = (double)t.bm * t.bn * c.k_chunk * per_cu / (kMacRate * mfma_efficiency(tile, vec));
-    // a tail of at most one workgroup per CU runs alone on its CU (about 0.8 of the shared time)
+    // a tail of at most one workgroup per CU runs alone on its CU
     double tail_time = 0;
-    if (tail > 0) tail_time = (tail <= kNumCUs && per_cu > 1) ? wg_time * 0.8 / per_cu * 1.25 : wg_time;
+    if (tail > 0)
+        tail_time = (tail <= kNumCUs && per_cu > 1)
+                        ? (double)t.bm * t.bn * c.k_chunk / (kMacRate * mfma_alone_efficiency(tile, vec))
+                        : wg_time;
     c.time = full_waves * wg_time + tail_time;
     if (c.splits > 1) c.time += (2.0 * c.splits + 1) * M * N * 4 / kPartialBw + kLaunch;
     return c;
@@ -242,7 +260,7 @@ void choose_split(int64_t tiles, int64_t K, int bk, int64_t target_wgs, int64_t 
 Candidate mfma_best(const sgemm_options& o, bool vec, bool trans, int64_t M, int64_t N, int64_t K) {
     std::vector<int> cands;
     if (o.tile >= 0) cands.push_back(o.tile);
-    else cands = {11, 8, 3, 10, 0, 1, 2, 5, 4};
+    else cands = {11, 14, 13, 8, 3, 10, 0, 1, 2, 5, 4};
     Candidate best;
     bool have = false;
     for (int tile : cands) {

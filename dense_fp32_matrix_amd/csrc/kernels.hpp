@@ -93,6 +93,8 @@ constexpr TileShape kMfmaTiles[] = {
     {256, 128, 16, 2, 2, 2, 0, 3},   // 10: as 0, direct-to-LDS loads, three stages
     {256, 256, 16, 2, 4, 2, 1, 3, true},   // 11: as 8 with 8 waves (two per SIMD), 128x64 per wave
     {256, 256, 16, 2, 4, 2, 1, 4},   // 12: as 11, four stages
+    {128, 128, 16, 2, 2, 2, 1, 3, true},   // 13: direct-to-LDS, 4 waves of 64x64, up to two workgroups per CU
+    {128, 128, 32, 2, 2, 1, 1, 3, true},   // 14: as 13 with a 32-deep K-step (half the barriers), one per CU
 };
 constexpr int kNumMfmaTiles = sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]);
 

@@ -858,11 +858,13 @@ hipError_t launch_mfma(int tile, bool vec, int ops, const GemmArgs& g, int split
         SGEMM_MFMA_CASE(10)
         SGEMM_MFMA_CASE(11)
         SGEMM_MFMA_CASE(12)
+        SGEMM_MFMA_CASE(13)
+        SGEMM_MFMA_CASE(14)
         default:
             return hipErrorInvalidValue;
     }
 #undef SGEMM_MFMA_CASE
 }
-static_assert(kNumMfmaTiles == 13, "launch_mfma covers every MFMA tile");
+static_assert(kNumMfmaTiles == 15, "launch_mfma covers every MFMA tile");
 
 }  // namespace sgemm_impl

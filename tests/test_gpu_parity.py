@@ -112,7 +112,7 @@ def test_skinny(oracle_mod, shape, vector, split_k):
     check_case(oracle_mod, *shape, f"skinny/v{vector}/s{split_k}", path="skinny", vector=vector, split_k=split_k)
 
 
-@pytest.mark.parametrize("path,tile", [("mfma", 0), ("mfma", 2), ("mfma", 4), ("mfma", 8), ("valu", 0)])
+@pytest.mark.parametrize("path,tile", [("mfma", 0), ("mfma", 2), ("mfma", 4), ("mfma", 8), ("mfma", 13), ("mfma", 14), ("valu", 0)])
 @pytest.mark.parametrize("split_k", [2, 5, 16])
 def test_split_k(oracle_mod, path, tile, split_k):
     check_case(oracle_mod, 200, 136, 2000, f"{path}/{tile}/split{split_k}", path=path, tile=tile,
@@ -128,7 +128,7 @@ STREAMK_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("tile", [3, 0, 2, 8, 10, 11, 12])
+@pytest.mark.parametrize("tile", [3, 0, 2, 8, 10, 11, 12, 13, 14])
 @pytest.mark.parametrize("vector", [0, 1])
 @pytest.mark.parametrize("shape", STREAMK_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_stream_k(oracle_mod, shape, tile, vector):
