@@ -7,6 +7,10 @@
 #include <cstdint>
 #include <cstring>
 #include <limits>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/sgemm.h"
@@ -101,6 +105,7 @@ double mfma_efficiency(int tile, bool vec) {
         switch (tile) {
             case 8: case 9: case 11: case 12: return 0.66;
             case 10: case 13: case 14: return 0.58;
+            case 15: return 0.55;
             case 2: return 0.62;
             case 4: return 0.60;
             default: return 0.55;
@@ -112,6 +117,7 @@ double mfma_efficiency(int tile, bool vec) {
         case 9: return 0.905;
         case 13: return 0.89;
         case 14: return 0.885;
+        case 15: return 0.80;
         case 3: case 6: return 0.89;
         case 10: return 0.87;
         case 0: case 1: case 7: return 0.85;
@@ -122,12 +128,15 @@ double mfma_efficiency(int tile, bool vec) {
 
 // Share of the CU's peak when the CU holds a single workgroup of a tile
 // built for two or more per CU (a tail shorter than one wave of
-// workgroups).  Direct-to-LDS tiles keep most of their rate alone;
-// register-staged ones depend on a second workgroup to hide their loads.
+// workgroups).  Register-staged tiles depend on a second workgroup to hide
+// their loads; the 128x128 direct-to-LDS tile keeps most of its rate; the
+// 64x64 one, which moves twice the bytes per multiply-add of the 128x128
+// tile through the CU's load path and LDS, runs faster with them to itself.
 double mfma_alone_efficiency(int tile, bool vec) {
     const double e = mfma_efficiency(tile, vec);
     switch (tile) {
         case 13: return 0.79 * e;
+        case 15: return 1.125 * e;
         case 2: return 0.75 * e;
         default: return e;
     }
@@ -260,7 +269,7 @@ void choose_split(int64_t tiles, int64_t K, int bk, int64_t target_wgs, int64_t 
 Candidate mfma_best(const sgemm_options& o, bool vec, bool trans, int64_t M, int64_t N, int64_t K) {
     std::vector<int> cands;
     if (o.tile >= 0) cands.push_back(o.tile);
-    else cands = {11, 14, 13, 8, 3, 10, 0, 1, 2, 5, 4};
+    else cands = {11, 14, 13, 15, 8, 3, 10, 0, 1, 2, 5, 4};
     Candidate best;
     bool have = false;
     for (int tile : cands) {
@@ -275,9 +284,12 @@ Candidate mfma_best(const sgemm_options& o, bool vec, bool trans, int64_t M, int
                 const int64_t slots = (int64_t)kNumCUs * wgs_per_cu(t);
                 cs.push_back(tiles_candidate(tile, vec, M, N, K, 1));
                 if (tiles < slots) {
+                    // enough slices to fill every slot, and half as many
+                    // (less partial traffic, one short wave)
                     int64_t s = 1, kc = K;
                     choose_split(tiles, K, t.bk, slots, 32, &s, &kc);
                     cs.push_back(tiles_candidate(tile, vec, M, N, K, s));
+                    if (s >= 4) cs.push_back(tiles_candidate(tile, vec, M, N, K, s / 2));
                 }
             }
         }
@@ -295,7 +307,7 @@ Candidate mfma_best(const sgemm_options& o, bool vec, bool trans, int64_t M, int
 
 constexpr double kPackBw = 3e12;   // bytes/s read + written by the pack kernel
 
-sgemm_status make_plan(const Call& c, const sgemm_options* opts, Plan* out) {
+sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* out) {
     sgemm_status st = validate(c);
     if (st != SGEMM_OK) return st;
     sgemm_options o{};
@@ -353,17 +365,18 @@ sgemm_status make_plan(const Call& c, const sgemm_options* opts, Plan* out) {
         best.tile = 0;
         best.k_chunk = K;
     } else if (path == SGEMM_PATH_SKINNY) {
-        // The 8-wave tile splits K inside the workgroup; split K across
-        // workgroups only while fewer than ~1024 waves would stream B.
-        best.tile = o.tile >= 0 ? o.tile : 1;
+        // A workgroup streams its slice of B at a rate that one CU's loads in
+        // flight cap, so the 4-wave tile runs one workgroup per CU: K is
+        // split across workgroups as far as the workgroups still fit one
+        // per CU (a second workgroup on some CUs makes those the tail).
+        best.tile = o.tile >= 0 ? o.tile : 0;
         const TileShape& t = kSkinnyTiles[best.tile];
-        const int waves = t.waves_m * t.waves_n;
         const int64_t tiles = cdiv(N, t.bn);
         int64_t splits = 1;
         if (o.split_k > 0) {
             splits = o.split_k;
         } else {
-            splits = std::max<int64_t>(1, cdiv(4 * kNumCUs, tiles * waves));
+            splits = std::max<int64_t>(1, kNumCUs / tiles);
             splits = std::min<int64_t>(splits, std::max<int64_t>(1, K / (4 * t.bk)));
         }
         splits = std::min<int64_t>(splits, cdiv(K, t.bk));
@@ -471,6 +484,108 @@ sgemm_status make_plan(const Call& c, const sgemm_options* opts, Plan* out) {
     return SGEMM_OK;
 }
 
+// Plans are a pure function of the shape, the operand layouts, the
+// 16-byte alignment of A and B and of their leading dimensions, whether A
+// and B are read at all, and the options that steer the choice; the time
+// model walks every tile and every stream-K workgroup, so plans are kept
+// per key (argument checks still run on every call).
+struct PlanKey {
+    int64_t M, N, K;
+    int32_t flags;                 // ta | tb | reads_ab | A, B 16-byte aligned | lda, ldb % 4 == 0
+    int32_t path, tile, split_k, vector, decomposition, pack;
+    bool operator==(const PlanKey& o) const {
+        return std::tie(M, N, K, flags, path, tile, split_k, vector, decomposition, pack) ==
+               std::tie(o.M, o.N, o.K, o.flags, o.path, o.tile, o.split_k, o.vector, o.decomposition, o.pack);
+    }
+};
+struct PlanKeyHash {
+    size_t operator()(const PlanKey& k) const {
+        uint64_t h = 1469598103934665603ull;
+        for (int64_t v : {k.M, k.N, k.K, (int64_t)k.flags, (int64_t)k.path, (int64_t)k.tile, (int64_t)k.split_k,
+                          (int64_t)k.vector, (int64_t)k.decomposition, (int64_t)k.pack})
+            h = (h ^ (uint64_t)v) * 1099511628211ull;
+        return (size_t)h;
+    }
+};
+constexpr size_t kPlanCacheMax = 4096;
+std::mutex g_plan_mu;
+std::unordered_map<PlanKey, Plan, PlanKeyHash> g_plans;
+
+sgemm_status make_plan(const Call& c, const sgemm_options* opts, Plan* out) {
+    const sgemm_status st = validate(c);
+    if (st != SGEMM_OK) return st;
+    if (opts != nullptr && opts->workspace != nullptr && !aligned(opts->workspace, 256)) return SGEMM_ERR_INVALID_ARG;
+    sgemm_options o{};
+    if (opts) o = *opts;
+    const PlanKey key{c.M, c.N, c.K,
+                      (c.ta ? 1 : 0) | (c.tb ? 2 : 0) | (c.reads_ab() ? 4 : 0) | (aligned(c.A, 16) ? 8 : 0) |
+                          (aligned(c.B, 16) ? 16 : 0) | (c.lda % 4 == 0 ? 32 : 0) | (c.ldb % 4 == 0 ? 64 : 0),
+                      o.path, o.tile, o.split_k, o.vector, o.decomposition, o.pack};
+    {
+        std::lock_guard<std::mutex> lock(g_plan_mu);
+        auto it = g_plans.find(key);
+        if (it != g_plans.end()) {
+            *out = it->second;
+            return SGEMM_OK;
+        }
+    }
+    const sgemm_status s2 = make_plan_uncached(c, opts, out);
+    if (s2 == SGEMM_OK) {
+        std::lock_guard<std::mutex> lock(g_plan_mu);
+        if (g_plans.size() >= kPlanCacheMax) g_plans.clear();
+        g_plans.emplace(key, *out);
+    }
+    return s2;
+}
+
+// Workspace kept between calls, one buffer per (device, stream).  Calls on
+// one stream run in order, so a call may reuse the buffer the previous call
+// on that stream used; a larger request frees it (stream-ordered) and
+// allocates a larger one.  The lock stays held (in `lock`) until the call
+// has enqueued all its kernels, so that calls from several host threads on
+// one stream cannot interleave their kernels around the shared buffer.
+// Requests above kWsCacheMax, and calls on a stream that is being captured
+// into a graph, allocate and free their own.
+constexpr size_t kWsCacheMax = size_t(512) << 20;
+struct CachedWs {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, CachedWs> g_ws;
+
+// *ws: a cached buffer of at least `bytes`, or null if the caller must allocate its own
+hipError_t cached_workspace(size_t bytes, hipStream_t stream, void** ws, std::unique_lock<std::mutex>& lock) {
+    *ws = nullptr;
+    if (bytes > kWsCacheMax) return hipSuccess;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return e;
+    if (cs != hipStreamCaptureStatusNone) return hipSuccess;
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    lock = std::unique_lock<std::mutex>(g_ws_mu);
+    CachedWs& w = g_ws[{dev, stream}];
+    if (w.bytes < bytes) {
+        if (w.ptr != nullptr) {
+            e = hipFreeAsync(w.ptr, stream);
+            w.ptr = nullptr;
+            w.bytes = 0;
+            if (e != hipSuccess) return e;
+        }
+        const size_t want = std::min(kWsCacheMax, std::max(bytes, size_t(1) << 20));
+        e = hipMallocAsync(&w.ptr, want, stream);
+        if (e != hipSuccess || w.ptr == nullptr) {
+            w.ptr = nullptr;
+            return e != hipSuccess ? e : hipErrorOutOfMemory;
+        }
+        w.bytes = want;
+    }
+    *ws = w.ptr;
+    return hipSuccess;
+}
+
 sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_options* opts) {
     Plan p;
     sgemm_status st = make_plan(c, opts, &p);
@@ -485,16 +600,23 @@ sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_option
 
     void* ws = nullptr;
     bool owned = false;
+    std::unique_lock<std::mutex> ws_lock;     // held while the cached workspace is in use
     if (q.workspace_bytes > 0) {
         if (opts != nullptr && opts->workspace != nullptr) {
             if (opts->workspace_bytes < q.workspace_bytes) return SGEMM_ERR_ALLOC;
             ws = opts->workspace;
         } else {
-            if (hipMallocAsync(&ws, q.workspace_bytes, stream) != hipSuccess || ws == nullptr) {
+            if (cached_workspace(q.workspace_bytes, stream, &ws, ws_lock) != hipSuccess) {
                 (void)hipGetLastError();
                 return SGEMM_ERR_ALLOC;
             }
-            owned = true;
+            if (ws == nullptr) {
+                if (hipMallocAsync(&ws, q.workspace_bytes, stream) != hipSuccess || ws == nullptr) {
+                    (void)hipGetLastError();
+                    return SGEMM_ERR_ALLOC;
+                }
+                owned = true;
+            }
         }
     }
 

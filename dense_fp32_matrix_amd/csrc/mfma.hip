@@ -437,11 +437,11 @@ struct KmLayout {
     static constexpr bool KC = false;
     static constexpr int SEG = 64 * W;
     static constexpr int ROWS = 256 / R;                  // k rows per 1 KB block
-    static constexpr int GS = ROWS == 1 ? R + 8 : ROWS * R + 16;   // floats between blocks
+    static constexpr int GS = 256 + 8 * ROWS;            // floats between blocks
     static constexpr int SEGS = 256 / SEG;                // instructions per block
     static constexpr int INSTR = BK / ROWS * SEGS;
     static constexpr int FLOATS = BK / ROWS * GS;
-    static_assert(R == 128 || R == 256, "blocks hold one or two rows");
+    static_assert(R == 64 || R == 128 || R == 256, "blocks hold one, two or four rows");
     static_assert((4 / ROWS) * GS % 64 == 32, "lane halves of a fragment read 32 banks apart");
     static __device__ __forceinline__ void elem(int ins, int lane, int& r, int& k) {
         const int f = (ins % SEGS) * SEG + W * lane;       // float within the block
@@ -474,8 +474,11 @@ struct DtlStageFloats<true, OPS, BM, BN, BK> {
 // source pointer that one issue advances by one K-step (steps are issued in
 // order), so a step inside the K range costs one 64-bit add per load.
 // r0 is the tile's first non-K index and lim its bound (M or N): lanes past
-// it read the last valid row or column instead, which only reaches outputs
-// outside C that are never written.  Only the K range needs the zero block,
+// it read the last valid row (k-contiguous layout), or the last whole lane
+// group of columns (k-major layout: a lane fetches L::SEG / 64 consecutive
+// columns, so the clamp keeps its first column a multiple of that width and
+// its last one inside the stored row), instead; that data only reaches
+// outputs outside C that are never written.  Only the K range needs the zero block,
 // on the steps that cross its end (checked()).
 template <class L, int PER>
 struct DtlLoads {
@@ -488,7 +491,8 @@ struct DtlLoads {
         for (int i = 0; i < PER; ++i) {
             int r, k;
             L::elem(i * waves + wave, lane, r, k);
-            const int rr = min(r0 + r, lim - 1);
+            constexpr int lanew = L::SEG / 64;
+            const int rr = min(r0 + r, L::KC ? lim - 1 : (lim - 1) & ~(lanew - 1));
             ptr[i] = X + (L::KC ? (int64_t)rr * ld + kb + k : (int64_t)(kb + k) * ld + rr);
             kk[i] = k;
         }
@@ -860,11 +864,12 @@ hipError_t launch_mfma(int tile, bool vec, int ops, const GemmArgs& g, int split
         SGEMM_MFMA_CASE(12)
         SGEMM_MFMA_CASE(13)
         SGEMM_MFMA_CASE(14)
+        SGEMM_MFMA_CASE(15)
         default:
             return hipErrorInvalidValue;
     }
 #undef SGEMM_MFMA_CASE
 }
-static_assert(kNumMfmaTiles == 15, "launch_mfma covers every MFMA tile");
+static_assert(kNumMfmaTiles == 16, "launch_mfma covers every MFMA tile");
 
 }  // namespace sgemm_impl

@@ -62,6 +62,7 @@ PLANS = [
     {"path": "mfma", "tile": 11, "decomposition": "tiles", "split_k": 3},
     {"path": "mfma", "tile": 13, "decomposition": "stream_k"},
     {"path": "mfma", "tile": 14, "decomposition": "tiles", "split_k": 2},
+    {"path": "mfma", "tile": 15, "decomposition": "tiles", "split_k": 1},
     {"path": "naive"},
 ]
 

@@ -112,7 +112,8 @@ def test_skinny(oracle_mod, shape, vector, split_k):
     check_case(oracle_mod, *shape, f"skinny/v{vector}/s{split_k}", path="skinny", vector=vector, split_k=split_k)
 
 
-@pytest.mark.parametrize("path,tile", [("mfma", 0), ("mfma", 2), ("mfma", 4), ("mfma", 8), ("mfma", 13), ("mfma", 14), ("valu", 0)])
+@pytest.mark.parametrize("path,tile", [("mfma", 0), ("mfma", 2), ("mfma", 4), ("mfma", 8), ("mfma", 13), ("mfma", 14),
+                                       ("mfma", 15), ("valu", 0)])
 @pytest.mark.parametrize("split_k", [2, 5, 16])
 def test_split_k(oracle_mod, path, tile, split_k):
     check_case(oracle_mod, 200, 136, 2000, f"{path}/{tile}/split{split_k}", path=path, tile=tile,
@@ -128,7 +129,7 @@ STREAMK_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("tile", [3, 0, 2, 8, 10, 11, 12, 13, 14])
+@pytest.mark.parametrize("tile", [3, 0, 2, 8, 10, 11, 12, 13, 14, 15])
 @pytest.mark.parametrize("vector", [0, 1])
 @pytest.mark.parametrize("shape", STREAMK_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_stream_k(oracle_mod, shape, tile, vector):
@@ -304,6 +305,70 @@ def test_caller_workspace_and_stream(oracle_mod):
     small = torch.empty(16, dtype=torch.float32, device=DEV)
     with pytest.raises(lib.SgemmError):
         lib.sgemm_ex(Ad, Bd, C, path="mfma", tile=2, split_k=4, workspace=small)
+
+
+def test_library_workspace_reuse(oracle_mod):
+    """Calls without a caller workspace share one library-held buffer per
+    stream: growing requests, shrinking ones and two streams in turn, with
+    nothing synchronised between the calls, each checked bit-exact."""
+    cases = [((200, 136, 2000), {"path": "mfma", "tile": 2, "split_k": 4}),
+             ((600, 517, 700), {"path": "mfma", "tile": 11, "decomposition": "stream_k"}),
+             ((1000, 900, 3000), {"path": "mfma", "tile": 13, "split_k": 6, "decomposition": "tiles"}),
+             ((16, 700, 5000), {"path": "skinny", "split_k": 3}),
+             ((300, 260, 900), {"path": "mfma", "tile": 15, "decomposition": "stream_k"})]
+    side = torch.cuda.Stream()
+    jobs = []
+    for i, ((M, N, K), opts) in enumerate(cases * 2):
+        A, B = inputs(M, N, K, "integer", 40 + i)
+        jobs.append((A, B, to_dev(A), to_dev(B), torch.full((M, N), float("nan"), device=DEV), opts, i % 2))
+    torch.cuda.synchronize()
+    for A, B, Ad, Bd, C, opts, on_side in jobs:
+        say(f"workspace reuse {tuple(C.shape)} {opts} side={on_side}")
+        if on_side:
+            with torch.cuda.stream(side):
+                lib.sgemm_ex(Ad, Bd, C, stream=side, **opts)
+        else:
+            lib.sgemm_ex(Ad, Bd, C, **opts)
+    torch.cuda.synchronize()
+    for A, B, Ad, Bd, C, opts, on_side in jobs:
+        ref = oracle_mod.round_to_f32(oracle_mod.sgemm(A.numpy(), B.numpy()))
+        assert_bit_exact(C.cpu().numpy(), ref, what=f"workspace reuse {opts}")
+
+
+@pytest.mark.parametrize("opts", [{"path": "mfma", "tile": 13, "split_k": 4, "decomposition": "tiles"},
+                                  {"path": "mfma", "tile": 15, "decomposition": "stream_k"}, {}],
+                         ids=["split4", "streamk", "auto"])
+def test_graph_capture_replays(oracle_mod, opts):
+    """A call captured into a graph (its workspace then belongs to the graph,
+    not to the library's per-stream buffer) replays correctly: new inputs are
+    copied in eagerly between replays, and every replay is checked."""
+    say(f"graph capture {opts}")
+    M, N, K = 520, 390, 1100
+    Ad = torch.empty((M, K), device=DEV)
+    Bd = torch.empty((K, N), device=DEV)
+    C = torch.empty((M, N), device=DEV)
+    A0, B0 = inputs(M, N, K, "integer", 60)
+    Ad.copy_(A0)
+    Bd.copy_(B0)
+    lib.sgemm_ex(Ad, Bd, C, **opts)           # eager call first (plans and library workspace in place)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lib.sgemm_ex(Ad, Bd, C, **opts)
+    torch.cuda.synchronize()
+    for r in range(3):
+        A, B = inputs(M, N, K, "integer", 61 + r)
+        Ad.copy_(A)
+        Bd.copy_(B)
+        C.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle_mod.round_to_f32(oracle_mod.sgemm(A.numpy(), B.numpy()))
+        assert_bit_exact(C.cpu().numpy(), ref, what=f"graph replay {r} {opts}")
+        lib.sgemm_ex(Ad, Bd, C, **opts)       # eager work between replays
+        torch.cuda.synchronize()
+        assert_bit_exact(C.cpu().numpy(), ref, what=f"eager after replay {r} {opts}")
 
 
 # --- the benchmark workloads at full size, in the benchmark's launch configuration ---------
