@@ -6,9 +6,11 @@ the workload's seeded synthetic inputs, already resident in HBM.  The default
 workload is M = N = K = 4096 with A, B i.i.d. uniform on [-1, 1).
 
 Prints one JSON line with the throughput (TFLOP/s, 2MNK per step), the
-roofline of the dominant kernel (its own launch time from HIP events on the
-launch stream, against the FP32 matrix-core peak), and the host oracle's
-throughput on a bounded sample of the same workload.
+roofline of the dominant kernel (its time per step from two HIP events on the
+launch stream around the timed steps; for a plan of one launch per step that
+is the kernel's own launch time plus the gap to the next launch, for a plan of
+several launches it covers all of them), against the FP32 matrix-core peak,
+and the host oracle's throughput on a bounded sample of the same workload.
 """
 import argparse
 import hashlib
@@ -45,6 +47,8 @@ def parse():
                     help="target host time of the oracle sample (0 = skip the CPU baseline)")
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="size of the cache-flush buffer for the flushed per-launch median")
+    ap.add_argument("--probe-seconds", type=float, default=1.5,
+                    help="untimed steps before the timed region while rocm-smi samples the clocks (0 = none)")
     return ap.parse_args()
 
 
@@ -155,39 +159,48 @@ def main():
     torch.cuda.synchronize()
 
     # Clock and power while the workload runs: an untimed probe phase of
-    # about 1.5 s after the warmup steps, which also brings the clocks to
+    # --probe-seconds after the warmup steps, which also brings the clocks to
     # their steady state before the timed region.
     samples = {"sclk_mhz": [], "power_w": []}
-    stop = threading.Event()
-    th = threading.Thread(target=sample_clocks, args=(stop, samples))
-    th.start()
-    t_end = time.perf_counter() + 1.5
-    while time.perf_counter() < t_end:
-        for _ in range(8):
-            step()
-        torch.cuda.synchronize()
-    stop.set()
-    th.join()
+    if args.probe_seconds > 0:
+        stop = threading.Event()
+        th = threading.Thread(target=sample_clocks, args=(stop, samples))
+        th.start()
+        t_end = time.perf_counter() + args.probe_seconds
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                step()
+            torch.cuda.synchronize()
+        stop.set()
+        # keep the GPU busy until the last rocm-smi reading has returned: an
+        # idle gap here lets the clocks drop, and the first timed steps would
+        # then run while they ramp back up
+        while th.is_alive():
+            for _ in range(4):
+                step()
+            torch.cuda.synchronize()
+        th.join()
     clocks = None
     if samples["sclk_mhz"]:
         tail = samples["sclk_mhz"][len(samples["sclk_mhz"]) // 2:]
         clocks = {"sclk_mhz_median_2nd_half": statistics.median(tail), "sclk_mhz_min": min(samples["sclk_mhz"]),
                   "sclk_mhz_max": max(samples["sclk_mhz"]), "samples": len(samples["sclk_mhz"]),
                   "power_w_median": statistics.median(samples["power_w"]) if samples["power_w"] else None,
-                  "source": "rocm-smi during ~1.5 s of untimed steps before the timed region"}
+                  "source": f"rocm-smi during {args.probe_seconds:g} s of untimed steps before the timed region"}
 
-    # timed region: K back-to-back steps, plus events around every step on the launch stream
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # timed region: K back-to-back steps on the launch stream between two
+    # events (no markers between the steps, which would add gaps of their own)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
+    ev0.record(stream)
+    for _ in range(args.steps):
         step()
-        ends[i].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_step_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    event_ms_per_step = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
     flops, alg_bytes = algorithmic(w)
@@ -207,7 +220,7 @@ def main():
         fl.append(s.elapsed_time(e))
     del flush
 
-    kernel_ms = statistics.mean(per_step_ms)
+    kernel_ms = event_ms_per_step
     main_kernel = {1: "naive_gemm_kernel", 2: "valu_gemm_kernel", 3: "mfma_gemm_kernel",
                    4: "skinny_gemm_kernel"}.get(plan["path"], "?")
     src = {1: "simple.hip", 2: "valu.hip", 3: "mfma.hip", 4: "skinny.hip"}.get(plan["path"], "mfma.hip")
@@ -256,8 +269,6 @@ def main():
         "clocks": clocks,
         "flushed_launch_ms_median": statistics.median(fl),
         "flushed_tflops": flops / (statistics.median(fl) * 1e-3) / 1e12,
-        "step_ms_min": min(per_step_ms),
-        "step_ms_median": statistics.median(per_step_ms),
     }
     print(json.dumps(out), flush=True)
 

@@ -94,7 +94,8 @@ constexpr double kMacRate = 128.0 * 2.4e9;   // FP32 MACs per second per CU at p
 constexpr double kPartialBw = 4e12;          // bytes/s for split-K partial slices (mostly cache resident)
 constexpr double kStreamKBw = 1e13;          // bytes/s for stream-K partial tiles (written and read back
                                              // by neighbouring workgroups, cache resident)
-constexpr double kLaunch = 6e-6;             // one more dependent kernel launch
+constexpr double kLaunch = 8e-6;             // one more dependent kernel launch
+constexpr double kTileVisit = 2e-6;          // filling and draining one tile's pipeline, and its epilogue
 
 // Share of the CU's peak one tile shape sustains when its CU is full, with
 // 16-byte (vec) or 4-byte loaders.  The register-staged 4-byte loaders need
@@ -116,7 +117,7 @@ double mfma_efficiency(int tile, bool vec) {
         case 8: return 0.91;
         case 9: return 0.905;
         case 13: return 0.89;
-        case 14: return 0.885;
+        case 14: return 0.91;
         case 15: return 0.80;
         case 3: case 6: return 0.89;
         case 10: return 0.87;
@@ -131,12 +132,13 @@ double mfma_efficiency(int tile, bool vec) {
 // workgroups).  Register-staged tiles depend on a second workgroup to hide
 // their loads; the 128x128 direct-to-LDS tile keeps most of its rate; the
 // 64x64 one, which moves twice the bytes per multiply-add of the 128x128
-// tile through the CU's load path and LDS, runs faster with them to itself.
+// tile through the CU's load path and LDS, runs a little faster with them
+// to itself.
 double mfma_alone_efficiency(int tile, bool vec) {
     const double e = mfma_efficiency(tile, vec);
     switch (tile) {
         case 13: return 0.79 * e;
-        case 15: return 1.125 * e;
+        case 15: return 1.0375 * e;
         case 2: return 0.75 * e;
         default: return e;
     }
@@ -166,12 +168,13 @@ Candidate tiles_candidate(int tile, bool vec, int64_t M, int64_t N, int64_t K, i
     const int64_t wgs = tiles * c.splits;
     const int64_t full_waves = wgs / (kNumCUs * per_cu);
     const int64_t tail = wgs - full_waves * kNumCUs * per_cu;
-    const double wg_time = (double)t.bm * t.bn * c.k_chunk * per_cu / (kMacRate * mfma_efficiency(tile, vec));
+    const double wg_time =
+        (double)t.bm * t.bn * c.k_chunk * per_cu / (kMacRate * mfma_efficiency(tile, vec)) + kTileVisit * per_cu;
     // a tail of at most one workgroup per CU runs alone on its CU
     double tail_time = 0;
     if (tail > 0)
         tail_time = (tail <= kNumCUs && per_cu > 1)
-                        ? (double)t.bm * t.bn * c.k_chunk / (kMacRate * mfma_alone_efficiency(tile, vec))
+                        ? (double)t.bm * t.bn * c.k_chunk / (kMacRate * mfma_alone_efficiency(tile, vec)) + kTileVisit
                         : wg_time;
     c.time = full_waves * wg_time + tail_time;
     if (c.splits > 1) c.time += (2.0 * c.splits + 1) * M * N * 4 / kPartialBw + kLaunch;
@@ -195,7 +198,9 @@ Candidate streamk_candidate(int tile, bool vec, int64_t M, int64_t N, int64_t K)
     const int64_t units = c.sk_tiles * c.k_steps;
     c.sk_ipw = cdiv(units, grid);
     const double step_time = (double)t.bm * t.bn * t.bk * wgs_per_cu(t) / (kMacRate * mfma_efficiency(tile, vec));
-    c.time = (double)(c.dp_tiles / grid) * c.k_steps * step_time + c.sk_ipw * step_time;
+    // a workgroup's shared range touches one or two tiles
+    c.time = (double)(c.dp_tiles / grid) * (c.k_steps * step_time + kTileVisit * wgs_per_cu(t)) +
+             c.sk_ipw * step_time + 2 * kTileVisit * wgs_per_cu(t);
     // partial tiles: count the workgroup ranges' segments that do not cover a
     // whole tile; each is written to a slot and read back once
     int64_t partial = 0;
