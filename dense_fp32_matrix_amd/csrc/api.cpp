@@ -105,7 +105,7 @@ double mfma_efficiency(int tile, bool vec) {
     if (!vec) {
         switch (tile) {
             case 8: case 9: case 11: case 12: return 0.66;
-            case 10: case 13: case 14: return 0.58;
+            case 10: case 13: case 14: case 16: return 0.58;
             case 15: return 0.55;
             case 2: return 0.62;
             case 4: return 0.60;
@@ -117,7 +117,8 @@ double mfma_efficiency(int tile, bool vec) {
         case 8: return 0.91;
         case 9: return 0.905;
         case 13: return 0.89;
-        case 14: return 0.91;
+        case 16: return 0.91;
+        case 14: return 0.90;
         case 15: return 0.80;
         case 3: case 6: return 0.89;
         case 10: return 0.87;
@@ -274,7 +275,7 @@ void choose_split(int64_t tiles, int64_t K, int bk, int64_t target_wgs, int64_t 
 Candidate mfma_best(const sgemm_options& o, bool vec, bool trans, int64_t M, int64_t N, int64_t K) {
     std::vector<int> cands;
     if (o.tile >= 0) cands.push_back(o.tile);
-    else cands = {11, 14, 13, 15, 8, 3, 10, 0, 1, 2, 5, 4};
+    else cands = {11, 16, 13, 15, 8, 3, 10, 0, 1, 2, 5, 4};
     Candidate best;
     bool have = false;
     for (int tile : cands) {
