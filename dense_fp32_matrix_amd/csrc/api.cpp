@@ -104,7 +104,7 @@ constexpr double kTileVisit = 2e-6;          // filling and draining one tile's 
 double mfma_efficiency(int tile, bool vec) {
     if (!vec) {
         switch (tile) {
-            case 8: case 9: case 11: case 12: return 0.66;
+            case 8: case 9: case 11: case 12: case 17: return 0.66;
             case 10: case 13: case 14: case 16: return 0.58;
             case 15: return 0.55;
             case 2: return 0.62;
@@ -113,6 +113,7 @@ double mfma_efficiency(int tile, bool vec) {
         }
     }
     switch (tile) {
+        case 17: return 0.927;
         case 11: case 12: return 0.92;
         case 8: return 0.91;
         case 9: return 0.905;
@@ -275,7 +276,7 @@ void choose_split(int64_t tiles, int64_t K, int bk, int64_t target_wgs, int64_t 
 Candidate mfma_best(const sgemm_options& o, bool vec, bool trans, int64_t M, int64_t N, int64_t K) {
     std::vector<int> cands;
     if (o.tile >= 0) cands.push_back(o.tile);
-    else cands = {11, 16, 13, 15, 8, 3, 10, 0, 1, 2, 5, 4};
+    else cands = {17, 11, 16, 13, 15, 8, 3, 10, 0, 1, 2, 5, 4};
     Candidate best;
     bool have = false;
     for (int tile : cands) {

@@ -97,6 +97,7 @@ constexpr TileShape kMfmaTiles[] = {
     {128, 128, 32, 2, 2, 1, 1, 3, true},   // 14: as 13 with a 32-deep K-step (half the barriers), one per CU
     {64, 64, 32, 2, 2, 2, 1, 3, true},     // 15: direct-to-LDS, 4 waves of 32x32: small products, thin M or N
     {128, 128, 16, 2, 4, 2, 1, 3, true},   // 16: as 14 with 8 waves (two per SIMD) of 64x32, 16-deep K-step
+    {256, 256, 16, 4, 2, 2, 1, 3, true},   // 17: as 11 with the 8 waves as 4 x 2 (64x128 each)
 };
 constexpr int kNumMfmaTiles = sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]);
 

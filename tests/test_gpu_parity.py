@@ -129,7 +129,7 @@ STREAMK_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("tile", [3, 0, 2, 8, 10, 11, 12, 13, 14, 15, 16])
+@pytest.mark.parametrize("tile", [3, 0, 2, 8, 10, 11, 12, 13, 14, 15, 16, 17])
 @pytest.mark.parametrize("vector", [0, 1])
 @pytest.mark.parametrize("shape", STREAMK_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_stream_k(oracle_mod, shape, tile, vector):
