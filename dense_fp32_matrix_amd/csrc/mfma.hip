@@ -160,9 +160,43 @@ struct TileOut {
 // l % 32), masked at the tile's limits, as alpha * sum + beta * out.  With
 // beta != 0 the old values are read one block at a time (the fence keeps the
 // scheduler from hoisting all of them next to the live accumulators).
-template <int MB, int NB, int WM, int WN>
+// IB (interleaved columns, NB == 4): column c of block nb is wave column
+// 4c + nb instead of 32 nb + c, so a lane holds 4 adjacent columns of each
+// row, written as one 16-byte store where the output allows it.
+template <int MB, int NB, int WM, int WN, bool IB = false>
 __device__ __forceinline__ void write_tile(const TileOut& o, const f32x16 (&acc)[MB][NB], int wm, int wn, int l32,
                                            int lh) {
+    if constexpr (IB) {
+        static_assert(NB == 4, "interleaved columns come in groups of four blocks");
+        const bool vec_out = ((reinterpret_cast<uintptr_t>(o.out) | (uintptr_t)(o.ldo * 4)) & 15) == 0;
+        const int j0 = o.col0 + wn * WN + 4 * l32;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int ib = o.row0 + wm * WM + mb * 32 + 4 * lh;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = ib + 8 * (r >> 2) + (r & 3);
+                if (i >= o.row_lim) continue;
+                float* p = o.out + (int64_t)i * o.ldo + j0;
+                f32x4 v = {o.alpha * acc[mb][0][r], o.alpha * acc[mb][1][r], o.alpha * acc[mb][2][r],
+                           o.alpha * acc[mb][3][r]};
+                if (vec_out && j0 + 3 < o.col_lim) {
+                    if (o.beta != 0.f) {
+                        const f32x4 c = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(o.beta, c[q], v[q]);
+                    }
+                    *reinterpret_cast<f32x4*>(p) = v;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (j0 + q < o.col_lim) p[q] = o.beta == 0.f ? v[q] : __builtin_fmaf(o.beta, p[q], v[q]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -548,6 +582,11 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
     using P = MfmaCfg<BM, BN, BK, WGM, WGN, true>;
     using LA = ALayout<(OPS & 1) != 0, BM, BK, W>;
     using LB = BLayout<(OPS & 2) != 0, BN, BK, W>;
+    // a k-major B with four column blocks per wave reads the four blocks'
+    // values of one k row as one 16-byte chunk (interleaved columns); with
+    // A k-major as well this measured slower (139.8 against 145.2 TFLOP/s
+    // at 4096^3), so it is kept to a k-contiguous A
+    constexpr bool IB = !LB::KC && LA::KC && P::NB == 4;
     constexpr int WAVES = WGM * WGN;
     constexpr int A_PER = LA::INSTR / WAVES;
     constexpr int B_PER = LB::INSTR / WAVES;
@@ -615,6 +654,7 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
     }
     const int a_col = wm * P::WM + l32;
     const int b_col = wn * P::WN + l32;
+    const int b_col4 = wn * P::WN + 4 * l32;
 
     f32x4 fa[2][P::MB];
     float fb[2][P::NB][4];
@@ -634,10 +674,19 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
                 const f32x4 v = *reinterpret_cast<const f32x4*>(st + b_frag[kg][nb]);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) fb[set][nb][q] = v[q];
-            } else {
+            } else if constexpr (!IB) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     fb[set][nb][q] = st[LA::FLOATS + LB::krow(8 * kg + 4 * lh + q) + b_col + nb * 32];
+            }
+        }
+        if constexpr (IB) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 v =
+                    *reinterpret_cast<const f32x4*>(st + LA::FLOATS + LB::krow(8 * kg + 4 * lh + q) + b_col4);
+#pragma unroll
+                for (int nb = 0; nb < P::NB; ++nb) fb[set][nb][q] = v[nb];
             }
         }
     };
@@ -712,7 +761,7 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
         wait_vmcnt<0>();                     // loads issued past the end land before the LDS is reused
     }
 
-    write_tile<P::MB, P::NB, P::WM, P::WN>(o, acc, wm, wn, l32, lh);
+    write_tile<P::MB, P::NB, P::WM, P::WN, IB>(o, acc, wm, wn, l32, lh);
 }
 
 // The kernel has two work decompositions.
