@@ -258,3 +258,32 @@ def test_stream_k_plans():
         lib.sgemm_plan_query(512, 512, 512, path="valu", decomposition="stream_k")
     with pytest.raises(lib.SgemmError):
         lib.sgemm_plan_query(512, 512, 512, path="mfma", split_k=2, decomposition="stream_k")
+
+
+def test_plan_cache_keys():
+    """Plans are cached per key: repeated queries agree, and every input the
+    plan depends on (operand alignment, leading dimensions, layouts, whether
+    A and B are read, options) still changes it after a cached query."""
+    M, N, K = 1000, 900, 1200
+    first = lib.sgemm_plan_query(M, N, K)
+    for _ in range(3):
+        assert lib.sgemm_plan_query(M, N, K) == first
+    assert first["vector"] == 1 and first["packed"] == 0
+    # A 4 bytes off a 16-byte boundary: no 16-byte lanes on A as stored
+    mis = lib.sgemm_plan_query(M, N, K, A=0x100004)
+    assert mis["vector"] == 0 or mis["packed"] & 1
+    # odd leading dimension of B
+    odd = lib.sgemm_plan_query(M, N, K, ldb=N + 1)
+    assert odd["vector"] == 0 or odd["packed"] & 2
+    assert lib.sgemm_plan_query(M, N, K) == first              # the aligned plan is unchanged
+    # forced options are part of the key
+    forced = lib.sgemm_plan_query(M, N, K, path="mfma", tile=2, split_k=3, decomposition="tiles")
+    assert (forced["tile"], forced["split_k"], forced["decomposition_name"]) == (2, 3, "tiles")
+    assert lib.sgemm_plan_query(M, N, K, path="valu")["path_name"] == "valu"
+    assert lib.sgemm_plan_query(M, N, K) == first
+    # layouts and alpha == 0 (no matrix kernel: one scaling launch)
+    t = lib.gemm_plan_query("T", "N", M, N, K)
+    assert t["path_name"] == "mfma" and t["tile"] in (8, 11, 13, 14, 15, 16, 17)
+    z = lib.gemm_plan_query("N", "N", M, N, K, alpha=0.0, beta=2.0)
+    assert z["launches"] == 1 and z["workspace_bytes"] == 0
+    assert lib.gemm_plan_query("N", "N", M, N, K) == first
