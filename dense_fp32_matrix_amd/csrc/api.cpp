@@ -356,10 +356,10 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
 
     int path = o.path;
     if (path == SGEMM_PATH_AUTO) {
-        path = (M <= 16 && !trans) ? SGEMM_PATH_SKINNY : SGEMM_PATH_MFMA;
+        path = (M <= 32 && !trans) ? SGEMM_PATH_SKINNY : SGEMM_PATH_MFMA;
         o.tile = -1;                 // the tile index belongs to an explicit path
     }
-    if (path == SGEMM_PATH_SKINNY && M > 16) return SGEMM_ERR_INVALID_ARG;
+    if (path == SGEMM_PATH_SKINNY && M > 32) return SGEMM_ERR_INVALID_ARG;
     const int ntiles = tile_count(path);
     if (o.tile < -1 || o.tile >= ntiles) return SGEMM_ERR_INVALID_ARG;
     if (path == SGEMM_PATH_MFMA && trans && o.tile >= 0 && !kMfmaTiles[o.tile].trans) return SGEMM_ERR_INVALID_ARG;
@@ -376,8 +376,9 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
         // flight cap, so the 4-wave tile runs one workgroup per CU: K is
         // split across workgroups as far as the workgroups still fit one
         // per CU (a second workgroup on some CUs makes those the tail).
-        best.tile = o.tile >= 0 ? o.tile : 0;
+        best.tile = o.tile >= 0 ? o.tile : (M <= 16 ? 0 : 2);
         const TileShape& t = kSkinnyTiles[best.tile];
+        if (M > t.bm) return SGEMM_ERR_INVALID_ARG;     // the tile holds at most bm rows of A
         const int64_t tiles = cdiv(N, t.bn);
         int64_t splits = 1;
         if (o.split_k > 0) {

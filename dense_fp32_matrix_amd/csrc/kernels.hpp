@@ -116,6 +116,7 @@ constexpr int kNumNaiveTiles = 1;
 constexpr TileShape kSkinnyTiles[] = {
     {16, 64, 64, 1, 4, 2},     // 0: 4 waves
     {16, 64, 128, 1, 8, 2},    // 1: 8 waves
+    {32, 64, 64, 1, 4, 2},     // 2: 4 waves, two 16-row blocks of A (M <= 32)
 };
 constexpr int kNumSkinnyTiles = sizeof(kSkinnyTiles) / sizeof(kSkinnyTiles[0]);
 

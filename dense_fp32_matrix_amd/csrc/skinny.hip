@@ -1,4 +1,4 @@
-// Skinny SGEMM (M <= 16) on FP32 matrix cores.
+// Skinny SGEMM (M <= 32) on FP32 matrix cores.
 //
 // With few rows of A every element of B is used at most M times, so the
 // product is bound by reading B once from HBM, not by arithmetic -- the
@@ -15,7 +15,9 @@
 //     number c, whose 16 output columns are n + 4j + c (j = 0..15): the four
 //     instructions together cover the 64 columns, and lane jj of each stores
 //     its 4 outputs of a row as 4 consecutive columns;
-//   * A (M x K, at most 16 rows) is read from L2 as 16-byte runs of one row;
+//   * A (M x K, at most 16 MT rows) is read from L2 as 16-byte runs of one
+//     row; with two 16-row blocks (MT = 2, M <= 32) each B vector feeds the
+//     MFMAs of both blocks, so B is still read once;
 //   * masked-off elements (rows >= M, columns >= N, k past the slice) load
 //     from a 16-byte zero block, so loads are never followed by a select;
 //   * two register stages of 4 k-groups of 16 each keep 2 x 4 x 4 = 32 16-byte
@@ -39,10 +41,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kGroups = 4;                 // k-groups of 16 per register stage
 constexpr int kStageK = 16 * kGroups;      // K elements per stage per wave
 
-template <bool VEC, int WAVES>
+// MT: 16-row blocks of A (M <= 16 MT); every B vector feeds MT x 4 MFMAs.
+template <bool VEC, int WAVES, int MT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES), amdgpu_waves_per_eu(2, 2)))
 void skinny_gemm_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) float red[WAVES][16][64];
+    __shared__ __attribute__((aligned(16))) float red[WAVES][16 * MT][64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -57,25 +60,33 @@ void skinny_gemm_kernel(GemmArgs g) {
     const int wkb = min(ke, kb + wave * kq);
     const int wke = min(ke, wkb + kq);
 
-    const bool a_row_ok = jj < g.M;
-    const float* a_row = g.A + (int64_t)(a_row_ok ? jj : 0) * g.lda;
+    bool a_row_ok[MT];
+    const float* a_row[MT];
+#pragma unroll
+    for (int b = 0; b < MT; ++b) {
+        a_row_ok[b] = 16 * b + jj < g.M;
+        a_row[b] = g.A + (int64_t)(a_row_ok[b] ? 16 * b + jj : 0) * g.lda;
+    }
     const int ncol = n_w + 4 * jj;               // first of this lane's 4 columns
 
-    f32x4 ra[2][kGroups];
+    f32x4 ra[2][MT][kGroups];
     f32x4 rb[2][kGroups][4];
 
     auto load_stage = [&](int buf, int k0) {
 #pragma unroll
         for (int gi = 0; gi < kGroups; ++gi) {
             const int ka = k0 + 16 * gi + 4 * kk;          // this lane's 4 k's
-            if constexpr (VEC) {
-                const bool ok = a_row_ok && ka < wke;
-                ra[buf][gi] = *reinterpret_cast<const f32x4*>(ok ? a_row + ka : kZeroSkinny);
-            } else {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const bool ok = a_row_ok && ka + t < wke;
-                    ra[buf][gi][t] = *(ok ? a_row + ka + t : kZeroSkinny);
+            for (int b = 0; b < MT; ++b) {
+                if constexpr (VEC) {
+                    const bool ok = a_row_ok[b] && ka < wke;
+                    ra[buf][b][gi] = *reinterpret_cast<const f32x4*>(ok ? a_row[b] + ka : kZeroSkinny);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const bool ok = a_row_ok[b] && ka + t < wke;
+                        ra[buf][b][gi][t] = *(ok ? a_row[b] + ka + t : kZeroSkinny);
+                    }
                 }
             }
 #pragma unroll
@@ -96,9 +107,11 @@ void skinny_gemm_kernel(GemmArgs g) {
         }
     };
 
-    f32x4 acc[4];
+    f32x4 acc[MT][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < MT; ++b)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[b][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto compute_stage = [&](int buf) {
 #pragma unroll
@@ -107,8 +120,10 @@ void skinny_gemm_kernel(GemmArgs g) {
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[buf][gi][t], rb[buf][gi][t][c],
-                                                                  acc[c], 0, 0, 0);
+#pragma unroll
+                    for (int b = 0; b < MT; ++b)
+                        acc[b][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[buf][b][gi][t], rb[buf][gi][t][c],
+                                                                         acc[b][c], 0, 0, 0);
     };
 
     const int nst = (wke - wkb + kStageK - 1) / kStageK;
@@ -124,37 +139,41 @@ void skinny_gemm_kernel(GemmArgs g) {
         if (s < nst) compute_stage(0);
     }
 
-    // wave partials -> LDS: block c, register r is row 4kk + r, column 4jj + c
+    // wave partials -> LDS: row block b, MFMA c, register r is row 16b + 4kk + r, column 4jj + c
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<f32x4*>(&red[wave][4 * kk + r][4 * jj]) =
-            f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+    for (int b = 0; b < MT; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<f32x4*>(&red[wave][16 * b + 4 * kk + r][4 * jj]) =
+                f32x4{acc[b][0][r], acc[b][1][r], acc[b][2][r], acc[b][3][r]};
     __syncthreads();
 
     // sum the wave partials in wave order and write rows < M, columns < N
-    if (tid >= 256) return;                       // 16 rows x 16 column groups
-    const int i = tid >> 4;
-    const int c4 = (tid & 15) * 4;
-    f32x4 s4 = *reinterpret_cast<const f32x4*>(&red[0][i][c4]);
+    // (16 MT rows x 16 groups of 4 columns)
+    const float alpha = g.c_slice ? 1.f : g.alpha;    // slices are raw partial sums
+    const float beta = g.c_slice ? 0.f : g.beta;
+    for (int e = tid; e < 16 * MT * 16; e += 64 * WAVES) {
+        const int i = e >> 4;
+        const int c4 = (e & 15) * 4;
+        f32x4 s4 = *reinterpret_cast<const f32x4*>(&red[0][i][c4]);
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) s4 += *reinterpret_cast<const f32x4*>(&red[w][i][c4]);
-    if (i < g.M) {
-        float* crow = g.C + (int64_t)blockIdx.z * g.c_slice + (int64_t)i * g.ldc;
-        const float alpha = g.c_slice ? 1.f : g.alpha;    // slices are raw partial sums
-        const float beta = g.c_slice ? 0.f : g.beta;
+        for (int w = 1; w < WAVES; ++w) s4 += *reinterpret_cast<const f32x4*>(&red[w][i][c4]);
+        if (i < g.M) {
+            float* crow = g.C + (int64_t)blockIdx.z * g.c_slice + (int64_t)i * g.ldc;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (n_w + c4 + c < g.N) store_scaled(crow + n_w + c4 + c, s4[c], alpha, beta);
+            for (int c = 0; c < 4; ++c)
+                if (n_w + c4 + c < g.N) store_scaled(crow + n_w + c4 + c, s4[c], alpha, beta);
+        }
     }
 }
 
-template <int WAVES>
+template <int WAVES, int MT>
 hipError_t launch_waves(bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
     dim3 grid((unsigned)g.tiles_n, 1, (unsigned)splits);
     if (vec)
-        hipLaunchKernelGGL((skinny_gemm_kernel<true, WAVES>), grid, dim3(64 * WAVES), 0, stream, g);
+        hipLaunchKernelGGL((skinny_gemm_kernel<true, WAVES, MT>), grid, dim3(64 * WAVES), 0, stream, g);
     else
-        hipLaunchKernelGGL((skinny_gemm_kernel<false, WAVES>), grid, dim3(64 * WAVES), 0, stream, g);
+        hipLaunchKernelGGL((skinny_gemm_kernel<false, WAVES, MT>), grid, dim3(64 * WAVES), 0, stream, g);
     return hipGetLastError();
 }
 
@@ -162,11 +181,12 @@ hipError_t launch_waves(bool vec, const GemmArgs& g, int splits, hipStream_t str
 
 hipError_t launch_skinny(int tile, bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
     switch (tile) {
-        case 0: return launch_waves<kSkinnyTiles[0].waves_n>(vec, g, splits, stream);
-        case 1: return launch_waves<kSkinnyTiles[1].waves_n>(vec, g, splits, stream);
+        case 0: return launch_waves<kSkinnyTiles[0].waves_n, kSkinnyTiles[0].bm / 16>(vec, g, splits, stream);
+        case 1: return launch_waves<kSkinnyTiles[1].waves_n, kSkinnyTiles[1].bm / 16>(vec, g, splits, stream);
+        case 2: return launch_waves<kSkinnyTiles[2].waves_n, kSkinnyTiles[2].bm / 16>(vec, g, splits, stream);
         default: return hipErrorInvalidValue;
     }
 }
-static_assert(kNumSkinnyTiles == 2, "launch_skinny covers every skinny tile");
+static_assert(kNumSkinnyTiles == 3, "launch_skinny covers every skinny tile");
 
 }  // namespace sgemm_impl

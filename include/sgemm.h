@@ -80,7 +80,7 @@ typedef enum sgemm_path {
     SGEMM_PATH_NAIVE = 1,   /* one thread per output, operands straight from memory */
     SGEMM_PATH_VALU = 2,    /* LDS-tiled, per-lane 8x8 outer-product update on FP32 FMA */
     SGEMM_PATH_MFMA = 3,    /* LDS-tiled, FP32 matrix-core contraction (v_mfma_f32_32x32x2_f32) */
-    SGEMM_PATH_SKINNY = 4   /* M <= 16: streams B once, FP32 matrix cores (16x16x4) */
+    SGEMM_PATH_SKINNY = 4   /* M <= 32: streams B once, FP32 matrix cores (16x16x4) */
 } sgemm_path;
 
 /* Work decompositions of the tiled paths. */

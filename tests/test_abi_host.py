@@ -114,8 +114,9 @@ def test_gemm_plans():
         with pytest.raises(lib.SgemmError):
             lib.gemm_plan_query("N", "T", 16, 512, 512, **kw)
     assert lib.gemm_plan_query("T", "T", 300, 200, 20, path="naive")["path_name"] == "naive"
-    # M <= 16 with a transposed operand: the MFMA path, not the skinny one
+    # M <= 32 with a transposed operand: the MFMA path, not the skinny one
     assert lib.gemm_plan_query("N", "T", 16, 11008, 4096)["path_name"] == "mfma"
+    assert lib.gemm_plan_query("N", "T", 32, 11008, 4096)["path_name"] == "mfma"
     assert lib.gemm_workspace_size("N", "T", M, N, K) == p["workspace_bytes"]
 
 
@@ -124,7 +125,9 @@ def test_bad_options_rejected():
     assert lib.sgemm_raw(*base, opts=lib._options(path=7)) == 1
     assert lib.sgemm_raw(*base, opts=lib._options(path="mfma", tile=99)) == 1
     assert lib.sgemm_raw(*base, opts=lib._options(split_k=-2)) == 1
-    assert lib.sgemm_raw(*base, opts=lib._options(path="skinny")) == 1          # M > 16
+    assert lib.sgemm_raw(*base, opts=lib._options(path="skinny")) == 1          # M > 32
+    few = (20, 64, 64, A, 64, B, 64, C, 64)
+    assert lib.sgemm_raw(*few, opts=lib._options(path="skinny", tile=0)) == 1   # tile 0 holds 16 rows
     assert lib.sgemm_raw(*base, opts=lib._options(path="naive", split_k=2)) == 1
     assert lib.sgemm_raw(*base, opts=lib._options(workspace=A + 16, workspace_bytes=1 << 20)) == 1
     assert lib.sgemm_raw(*base, opts=lib._options(pack=-1)) == 1
@@ -226,6 +229,9 @@ def test_default_plans_fill_the_chip():
             assert p["launches"] == 2 + bin(p["packed"]).count("1")
         assert lib.sgemm_workspace_size(M, N, K) == p["workspace_bytes"]
     assert lib.sgemm_plan_query(16, 11008, 4096)["path_name"] == "skinny"
+    p32 = lib.sgemm_plan_query(32, 11008, 4096)
+    assert p32["path_name"] == "skinny" and p32["bm"] == 32
+    assert lib.sgemm_plan_query(33, 11008, 4096)["path_name"] == "mfma"
     p = lib.sgemm_plan_query(512, 512, 65536)
     assert p["split_k"] > 1 or p["decomposition_name"] == "stream_k"   # long K is shared out
 

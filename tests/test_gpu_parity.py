@@ -106,10 +106,18 @@ def test_valu_tiles(oracle_mod, shape, tile, vector):
 
 @pytest.mark.parametrize("vector", [0, 1])
 @pytest.mark.parametrize("shape", [(1, 1, 1), (16, 64, 64), (5, 300, 1000), (16, 1000, 4100), (9, 11008, 512),
-                                   (16, 7, 3)], ids=lambda s: "x".join(map(str, s)))
+                                   (16, 7, 3), (17, 300, 1000), (32, 1000, 4100), (24, 65, 129), (32, 7, 3)],
+                         ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("split_k", [1, 3])
 def test_skinny(oracle_mod, shape, vector, split_k):
     check_case(oracle_mod, *shape, f"skinny/v{vector}/s{split_k}", path="skinny", vector=vector, split_k=split_k)
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2])
+def test_skinny_tiles(oracle_mod, tile):
+    """Every skinny tile on the rows it holds (16, or 32 with two row blocks)."""
+    M = lib.sgemm_tile_info("skinny", tile)["bm"]
+    check_case(oracle_mod, M, 517, 2100, f"skinny tile {tile}", path="skinny", tile=tile, split_k=2)
 
 
 @pytest.mark.parametrize("path,tile", [("mfma", 0), ("mfma", 2), ("mfma", 4), ("mfma", 8), ("mfma", 13), ("mfma", 14),
