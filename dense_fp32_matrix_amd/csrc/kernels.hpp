@@ -77,6 +77,8 @@ struct TileShape {
                             // with 8 * (sched - 1) MFMAs after the last LDS write of a K-step
     int dtl = 0;            // > 0: stages of the direct-to-LDS loader (3 at most with 4-byte lanes)
     bool trans = false;     // also instantiated for operands stored transposed (direct-to-LDS tiles only)
+    bool prio = false;      // direct-to-LDS tiles: raise the wave's priority while it issues a K-step's
+                            // MFMAs after its direct loads, back to normal before the barrier
 };
 
 constexpr TileShape kMfmaTiles[] = {
@@ -95,8 +97,8 @@ constexpr TileShape kMfmaTiles[] = {
     {256, 256, 16, 2, 4, 2, 1, 4},   // 12: as 11, four stages
     {128, 128, 16, 2, 2, 2, 1, 3, true},   // 13: direct-to-LDS, 4 waves of 64x64, up to two workgroups per CU
     {128, 128, 32, 2, 2, 1, 1, 3, true},   // 14: as 13 with a 32-deep K-step (half the barriers), one per CU
-    {64, 64, 32, 2, 2, 2, 1, 3, true},     // 15: direct-to-LDS, 4 waves of 32x32: small products, thin M or N
-    {128, 128, 16, 2, 4, 2, 1, 3, true},   // 16: as 14 with 8 waves (two per SIMD) of 64x32, 16-deep K-step
+    {64, 64, 32, 2, 2, 2, 1, 3, true, true},   // 15: direct-to-LDS, 4 waves of 32x32: small products, thin M or N
+    {128, 128, 16, 2, 4, 2, 1, 3, true, true},   // 16: as 14 with 8 waves (two per SIMD) of 64x32, 16-deep K-step
     {256, 256, 16, 4, 2, 2, 1, 3, true},   // 17: as 11 with the 8 waves as 4 x 2 (64x128 each)
 };
 constexpr int kNumMfmaTiles = sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]);
