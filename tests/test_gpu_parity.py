@@ -343,6 +343,27 @@ def test_library_workspace_reuse(oracle_mod):
         assert_bit_exact(C.cpu().numpy(), ref, what=f"workspace reuse {opts}")
 
 
+def test_large_workspace_allocated_per_call(oracle_mod):
+    """A split-K workspace above the library's cached limit (1 GiB of slices
+    here) is allocated and freed with the call; checked on sampled entries,
+    twice in a row."""
+    M, N, K = 4096, 4096, 8192
+    opts = {"path": "mfma", "tile": 17, "split_k": 16, "decomposition": "tiles"}
+    assert lib.sgemm_plan_query(M, N, K, **opts)["workspace_bytes"] > (512 << 20)
+    A, B = inputs(M, N, K, "integer", 70)
+    Ad, Bd = to_dev(A), to_dev(B)
+    rows, cols = workloads.sample_indices(M, N, 512, seed=71)
+    ref = oracle_mod.round_to_f32(oracle_mod.sgemm_entries(A.numpy(), B.numpy(), rows, cols)[0])
+    for r in range(2):
+        say(f"large workspace call {r}")
+        C = torch.full((M, N), float("nan"), device=DEV)
+        lib.sgemm_ex(Ad, Bd, C, **opts)
+        torch.cuda.synchronize()
+        got = C[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)].cpu().numpy()
+        assert_bit_exact(got, ref, what=f"large workspace call {r}")
+        del C
+
+
 @pytest.mark.parametrize("opts", [{"path": "mfma", "tile": 13, "split_k": 4, "decomposition": "tiles"},
                                   {"path": "mfma", "tile": 15, "decomposition": "stream_k"}, {}],
                          ids=["split4", "streamk", "auto"])
