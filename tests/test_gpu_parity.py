@@ -168,6 +168,23 @@ def test_padded_leading_dimensions(oracle_mod, path):
     assert_bit_exact(Cbuf.numpy(), ref, what=f"{path} padded")
 
 
+@pytest.mark.parametrize("tile", [17, 8, 11, 16, 15])
+@pytest.mark.parametrize("gap", [4, 7], ids=["ldc16B", "ldcodd"])
+def test_epilogue_keeps_ldc_gap(oracle_mod, tile, gap):
+    """Each tile's epilogue (the 16-byte interleaved-column stores of tiles 8
+    and 17 included) writes exactly [0, M) x [0, N): the NaN gap of a padded
+    ldc survives, with N ragged against the tile and against 4 columns."""
+    M, N, K = 300, 270, 100
+    ldc = N + gap
+    say(f"ldc gap tile={tile} ldc={ldc}")
+    A, B = inputs(M, N, K, "integer", 11)
+    C = run(A, B, ldc=ldc, path="mfma", tile=tile, decomposition="tiles", split_k=1)
+    full = torch.as_strided(C, (M, ldc), (ldc, 1)).cpu().numpy()
+    assert np.all(np.isnan(full[:, N:])), "wrote into the ldc gap"
+    ref = oracle_mod.round_to_f32(oracle_mod.sgemm(A.numpy(), B.numpy()))
+    assert_bit_exact(full[:, :N], ref, what=f"tile {tile} ldc {ldc}")
+
+
 @pytest.mark.parametrize("path,pack", [("valu", "never"), ("mfma", "never"), ("mfma", "always"),
                                        ("skinny", "never")])
 def test_misaligned_base_pointers(oracle_mod, path, pack):
