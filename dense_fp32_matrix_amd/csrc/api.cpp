@@ -546,21 +546,28 @@ sgemm_status make_plan(const Call& c, const sgemm_options* opts, Plan* out) {
     return s2;
 }
 
-// Workspace kept between calls, one buffer per (device, stream).  Calls on
-// one stream run in order, so a call may reuse the buffer the previous call
-// on that stream used; a larger request frees it (stream-ordered) and
-// allocates a larger one.  The lock stays held (in `lock`) until the call
-// has enqueued all its kernels, so that calls from several host threads on
-// one stream cannot interleave their kernels around the shared buffer.
-// Requests above kWsCacheMax, and calls on a stream that is being captured
-// into a graph, allocate and free their own.
+// Workspace kept between calls, one buffer per (device, stream) for up to
+// kWsStreams streams per device.  Calls on one stream run in order, so a call
+// may reuse the buffer the previous call on that stream used; a larger
+// request frees it (stream-ordered) and allocates a larger one.  The lock
+// stays held (in `lock`) until the call has enqueued all its kernels, so that
+// calls from several host threads on one stream cannot interleave their
+// kernels around the buffer.  Requests above kWsCacheMax, calls from further
+// streams, and calls on a stream that is being captured into a graph,
+// allocate and free their own.  No event orders a buffer's uses, since a
+// marker per call cost 3-6 us of device time: the buffer of a stream handle
+// is therefore assumed not to outlive the stream's work (a stream destroyed
+// with calls still running, and a new stream created with the same handle,
+// would share it).  The buffers live until the process ends.
 constexpr size_t kWsCacheMax = size_t(512) << 20;
+constexpr int kWsStreams = 8;
 struct CachedWs {
     void* ptr = nullptr;
     size_t bytes = 0;
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, CachedWs> g_ws;
+std::map<int, int> g_ws_count;   // streams with a buffer, per device
 
 // *ws: a cached buffer of at least `bytes`, or null if the caller must allocate its own
 hipError_t cached_workspace(size_t bytes, hipStream_t stream, void** ws, std::unique_lock<std::mutex>& lock) {
@@ -574,7 +581,16 @@ hipError_t cached_workspace(size_t bytes, hipStream_t stream, void** ws, std::un
     e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     lock = std::unique_lock<std::mutex>(g_ws_mu);
-    CachedWs& w = g_ws[{dev, stream}];
+    auto it = g_ws.find({dev, stream});
+    if (it == g_ws.end()) {
+        if (g_ws_count[dev] >= kWsStreams) {
+            lock.unlock();
+            return hipSuccess;
+        }
+        it = g_ws.emplace(std::make_pair(dev, stream), CachedWs{}).first;
+        ++g_ws_count[dev];
+    }
+    CachedWs& w = it->second;
     if (w.bytes < bytes) {
         if (w.ptr != nullptr) {
             e = hipFreeAsync(w.ptr, stream);

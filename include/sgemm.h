@@ -31,8 +31,14 @@
  * `stream` (0 = the null stream) and the call returns without waiting;
  * the caller synchronises.  Calls on one stream run in order.  When a plan
  * needs scratch memory (packed operand copies, split-K or stream-K
- * partials), `sgemm` allocates it stream-ordered on `stream`
- * (hipMallocAsync / hipFreeAsync); `sgemm_ex` can take a caller buffer.
+ * partials) and the caller passes none (`sgemm_ex` can take one), the
+ * library uses a buffer it keeps for the (device, stream) pair, grown
+ * stream-ordered (hipMallocAsync / hipFreeAsync) and held until the process
+ * ends, at most 512 MiB each for up to 8 streams per device; larger requests,
+ * further streams and calls under graph capture allocate and free their own,
+ * stream-ordered.  Because the kept buffer belongs to the stream handle,
+ * synchronise a stream before destroying it if a call of this library may
+ * still be running on it.
  *
  * Errors: every argument check below runs on the host before any HIP call;
  * on failure nothing is enqueued and C is untouched.  No exception crosses
@@ -111,8 +117,8 @@ typedef enum sgemm_decomposition {
  *                   16-byte path on the same values.
  *   workspace     : 256-byte aligned device buffer of workspace_bytes for packed
  *                   operands and split-K or stream-K partials, or NULL to let the
- *                   library allocate it stream-ordered.  The caller keeps it alive
- *                   until the work completes.
+ *                   library provide it (see "Memory and streams").  The caller keeps
+ *                   it alive until the work completes.
  */
 typedef struct sgemm_options {
     int32_t path;

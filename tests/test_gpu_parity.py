@@ -360,6 +360,31 @@ def test_library_workspace_reuse(oracle_mod):
         assert_bit_exact(C.cpu().numpy(), ref, what=f"workspace reuse {opts}")
 
 
+def test_workspace_on_many_streams(oracle_mod):
+    """More streams than the library keeps buffers for (8 per device): the
+    calls on the further streams allocate their own; all run concurrently,
+    unsynchronised, and every result is bit-exact."""
+    M, N, K = 260, 300, 1500
+    opts = {"path": "mfma", "tile": 15, "split_k": 4, "decomposition": "tiles"}
+    streams = [torch.cuda.Stream() for _ in range(11)]
+    jobs = []
+    for i, st in enumerate(streams):
+        A, B = inputs(M, N, K, "integer", 80 + i)
+        jobs.append((A, B, to_dev(A), to_dev(B), torch.full((M, N), float("nan"), device=DEV), st))
+    torch.cuda.synchronize()
+    for rep in range(2):
+        say(f"many streams, round {rep}")
+        for A, B, Ad, Bd, C, st in jobs:
+            with torch.cuda.stream(st):
+                lib.sgemm_ex(Ad, Bd, C, stream=st, **opts)
+        torch.cuda.synchronize()
+        for A, B, Ad, Bd, C, st in jobs:
+            ref = oracle_mod.round_to_f32(oracle_mod.sgemm(A.numpy(), B.numpy()))
+            assert_bit_exact(C.cpu().numpy(), ref, what=f"many streams round {rep}")
+            C.fill_(float("nan"))
+        torch.cuda.synchronize()
+
+
 def test_large_workspace_allocated_per_call(oracle_mod):
     """A split-K workspace above the library's cached limit (1 GiB of slices
     here) is allocated and freed with the call; checked on sampled entries,
