@@ -95,6 +95,9 @@ constexpr double kPartialBw = 4e12;          // bytes/s for split-K partial slic
 constexpr double kStreamKBw = 1e13;          // bytes/s for stream-K partial tiles (written and read back
                                              // by neighbouring workgroups, cache resident)
 constexpr double kLaunch = 8e-6;             // one more dependent kernel launch
+constexpr double kSkinnyCuBw = 31e9;         // bytes/s one CU's skinny workgroup streams from B (one row
+                                             // block; two row blocks are bound by the matrix pipe at 20e9)
+constexpr double kSkinnyHbmBw = 5.3e12;      // bytes/s the whole chip streams B at
 constexpr double kTileVisit = 2e-6;          // filling and draining one tile's pipeline, and its epilogue
 
 // Share of the CU's peak one tile shape sustains when its CU is full, with
@@ -364,7 +367,8 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
     if (o.tile < -1 || o.tile >= ntiles) return SGEMM_ERR_INVALID_ARG;
     if (path == SGEMM_PATH_MFMA && trans && o.tile >= 0 && !kMfmaTiles[o.tile].trans) return SGEMM_ERR_INVALID_ARG;
     if (path == SGEMM_PATH_NAIVE && o.split_k > 1) return SGEMM_ERR_INVALID_ARG;
-    if (o.decomposition == SGEMM_DECOMP_STREAM_K && (path != SGEMM_PATH_MFMA || o.split_k > 1))
+    if (o.decomposition == SGEMM_DECOMP_STREAM_K &&
+        ((path != SGEMM_PATH_MFMA && path != SGEMM_PATH_SKINNY) || o.split_k > 1))
         return SGEMM_ERR_INVALID_ARG;
 
     Candidate best;
@@ -372,10 +376,15 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
         best.tile = 0;
         best.k_chunk = K;
     } else if (path == SGEMM_PATH_SKINNY) {
-        // A workgroup streams its slice of B at a rate that one CU's loads in
-        // flight cap, so the 4-wave tile runs one workgroup per CU: K is
-        // split across workgroups as far as the workgroups still fit one
-        // per CU (a second workgroup on some CUs makes those the tail).
+        // A workgroup streams its slice of B at a rate that one CU caps, so
+        // the skinny tiles run one workgroup per CU.  Either K is split
+        // uniformly across workgroups as far as they still fit one per CU (a
+        // second workgroup on some CUs makes those the tail), or stream-K
+        // shares the (strip, 64-deep K-step) units out evenly over one
+        // workgroup per CU and a fix-up sums the strips that two workgroups
+        // share.  Both are floored by the chip's streaming rate: with one row
+        // block 172 strips already reach it, and stream-K pays only where the
+        // CUs, not HBM, are the limit (two row blocks, long K).
         best.tile = o.tile >= 0 ? o.tile : (M <= 16 ? 0 : 2);
         const TileShape& t = kSkinnyTiles[best.tile];
         if (M > t.bm) return SGEMM_ERR_INVALID_ARG;     // the tile holds at most bm rows of A
@@ -391,6 +400,32 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
         const int64_t k_chunk = round_up(cdiv(K, splits), t.bk);
         best.splits = cdiv(K, k_chunk);
         best.k_chunk = k_chunk;
+        // stream-K units are the kernel's 64-deep K-steps (the tiles with bk == 64)
+        const bool sk_ok = t.bk == 64 && o.split_k <= 1 && o.decomposition != SGEMM_DECOMP_TILES;
+        if (sk_ok) {
+            const int64_t k_steps = cdiv(K, 64);
+            const int64_t units = tiles * k_steps;
+            const int64_t ipw = cdiv(units, kNumCUs);
+            const double cu_bw = t.bm > 16 ? 20e9 : kSkinnyCuBw;
+            const double per_unit = 64.0 * t.bn * 4 / cu_bw;           // B bytes of a unit at one CU's rate
+            const double floor = 4.0 * ((double)M * K + (double)K * N + (double)M * N) / kSkinnyHbmBw;
+            const int64_t wgs = tiles * best.splits;
+            const double t_tiles = std::max(floor, (double)cdiv(wgs, kNumCUs) * (k_chunk / 64.0) * per_unit) +
+                                   (best.splits > 1 ? kLaunch : 0.0);
+            const double t_sk = std::max(floor, ipw * per_unit) + kLaunch;
+            if (o.decomposition == SGEMM_DECOMP_STREAM_K || t_sk < 0.95 * t_tiles) {
+                best.decomposition = SGEMM_DECOMP_STREAM_K;
+                best.splits = 1;
+                best.k_chunk = K;
+                best.grid = std::min<int64_t>(kNumCUs, units);
+                best.k_steps = k_steps;
+                best.sk_tiles = tiles;
+                best.dp_tiles = 0;
+                best.sk_ipw = cdiv(units, best.grid);
+            }
+        } else if (o.decomposition == SGEMM_DECOMP_STREAM_K) {
+            return SGEMM_ERR_INVALID_ARG;
+        }
     } else if (path == SGEMM_PATH_MFMA) {
         best = mfma_best(o, q.vector != 0, trans, M, N, K);
         // Alternative: copy the misaligned operand(s), in their stored

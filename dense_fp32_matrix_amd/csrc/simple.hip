@@ -200,11 +200,13 @@ hipError_t launch_splitk_reduce(const float* W, int64_t ldw, int64_t w_slice, in
 }
 
 hipError_t launch_streamk_fixup(const GemmArgs& g, int bm, int bn, int sk_tiles, hipStream_t stream) {
-    // every tile shape holds a whole number of chunks
-    if ((bm * bn) % 4096 != 0) return hipErrorInvalidValue;
-    // workgroups contributing to one tile (at most): many -> smaller chunks, more workgroups
+    // every tile shape holds a whole number of 1024-element chunks
+    if ((bm * bn) % 1024 != 0) return hipErrorInvalidValue;
+    // workgroups contributing to one tile (at most): many -> smaller chunks, more
+    // workgroups; tiles that are no whole number of 4096-element chunks (the
+    // skinny strips) take 1024-element chunks as well
     const int64_t contributors = (g.k_steps + g.sk_ipw - 1) / g.sk_ipw + 1;
-    if (contributors > 8)
+    if (contributors > 8 || (bm * bn) % 4096 != 0)
         hipLaunchKernelGGL(streamk_fixup_kernel<1>, dim3((unsigned)sk_tiles, (unsigned)(bm * bn / 1024)), dim3(256),
                            0, stream, g, bm, bn);
     else

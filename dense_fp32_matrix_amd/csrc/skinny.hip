@@ -41,22 +41,23 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kGroups = 4;                 // k-groups of 16 per register stage
 constexpr int kStageK = 16 * kGroups;      // K elements per stage per wave
 
-// MT: 16-row blocks of A (M <= 16 MT); every B vector feeds MT x 4 MFMAs.
+// One segment: the 64-column strip of B starting at column n_w over
+// k in [kb, ke), split in K across the waves (quarters rounded up to 16),
+// contracted with all rows of A, summed over the waves in wave order, and
+// written as alpha * sum + beta * out to out[i * ldo + c] for rows i < M and
+// strip columns c < col_lim.  MT: 16-row blocks of A (M <= 16 MT); every B
+// vector feeds MT x 4 MFMAs.
 template <bool VEC, int WAVES, int MT>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES), amdgpu_waves_per_eu(2, 2)))
-void skinny_gemm_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) float red[WAVES][16 * MT][64];
-
+__device__ __forceinline__ void skinny_segment(const GemmArgs& g, float (&red)[WAVES][16 * MT][64], int n_w,
+                                               int kb, int ke, float* out, int64_t ldo, int col_lim, float alpha,
+                                               float beta) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int jj = lane & 15;
     const int kk = lane >> 4;
 
-    const int n_w = blockIdx.x * 64;
-    const int kb = blockIdx.z * g.k_chunk;
-    const int ke = min(g.K, kb + g.k_chunk);
-    const int kq = g.k_chunk / WAVES;             // a multiple of 16 (host guarantees)
+    const int kq = ((ke - kb + WAVES - 1) / WAVES + 15) / 16 * 16;
     const int wkb = min(ke, kb + wave * kq);
     const int wke = min(ke, wkb + kq);
 
@@ -148,10 +149,8 @@ void skinny_gemm_kernel(GemmArgs g) {
                 f32x4{acc[b][0][r], acc[b][1][r], acc[b][2][r], acc[b][3][r]};
     __syncthreads();
 
-    // sum the wave partials in wave order and write rows < M, columns < N
+    // sum the wave partials in wave order and write rows < M, columns < col_lim
     // (16 MT rows x 16 groups of 4 columns)
-    const float alpha = g.c_slice ? 1.f : g.alpha;    // slices are raw partial sums
-    const float beta = g.c_slice ? 0.f : g.beta;
     for (int e = tid; e < 16 * MT * 16; e += 64 * WAVES) {
         const int i = e >> 4;
         const int c4 = (e & 15) * 4;
@@ -159,17 +158,84 @@ void skinny_gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) s4 += *reinterpret_cast<const f32x4*>(&red[w][i][c4]);
         if (i < g.M) {
-            float* crow = g.C + (int64_t)blockIdx.z * g.c_slice + (int64_t)i * g.ldc;
+            float* crow = out + (int64_t)i * ldo;
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                if (n_w + c4 + c < g.N) store_scaled(crow + n_w + c4 + c, s4[c], alpha, beta);
+                if (c4 + c < col_lim) store_scaled(crow + c4 + c, s4[c], alpha, beta);
         }
+    }
+}
+
+// Two work decompositions, as in the matrix-core kernel:
+//  * one (strip, K slice) per workgroup (sk_iters == 0): strip blockIdx.x,
+//    slice blockIdx.z; slices go to C + z * c_slice as raw partial sums;
+//  * stream-K (sk_iters > 0): the (strip, 64-deep K-step) units, strip-major,
+//    cut into equal ranges of sk_ipw units, one per workgroup, so that every
+//    CU streams the same share of B whatever the strip count.  A segment
+//    covering a whole strip writes C; a partial strip goes to the
+//    workgroup's slot 2 * wg + (0 for its first segment, 1 afterwards), and
+//    the stream-K fix-up kernel sums each strip's slots in workgroup order.
+//    Strip j of the unit order is tile_coords' column of tile j, as the
+//    fix-up kernel maps it.
+template <bool VEC, int WAVES, int MT>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES), amdgpu_waves_per_eu(2, 2)))
+void skinny_gemm_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) float red[WAVES][16 * MT][64];
+    int64_t it = (int64_t)blockIdx.x * g.sk_ipw;
+    const int64_t it_end = min(it + g.sk_ipw, g.sk_iters);
+    bool first = true;
+    int which = 0;
+    while (true) {
+        int n_w, kb, ke, col_lim;
+        float* out;
+        int64_t ldo, step = 0;
+        float alpha, beta;
+        if (g.sk_iters == 0) {
+            if (!first) break;
+            n_w = blockIdx.x * 64;
+            kb = blockIdx.z * g.k_chunk;
+            ke = min(g.K, kb + g.k_chunk);
+            out = g.C + (int64_t)blockIdx.z * g.c_slice + n_w;
+            ldo = g.ldc;
+            col_lim = g.N - n_w;
+            alpha = g.c_slice ? 1.f : g.alpha;    // slices are raw partial sums
+            beta = g.c_slice ? 0.f : g.beta;
+        } else {
+            if (it >= it_end) break;
+            const int j = (int)(it / g.k_steps);
+            const int q0 = (int)(it - (int64_t)j * g.k_steps);
+            const int q1 = (int)min<int64_t>(g.k_steps, q0 + (it_end - it));
+            int tm, tn;
+            tile_coords(j, 1, g.tiles_n, 1, &tm, &tn);
+            n_w = tn * 64;
+            kb = q0 * kStageK;
+            ke = min(g.K, q1 * kStageK);
+            if (q0 == 0 && q1 == g.k_steps) {
+                out = g.C + n_w;
+                ldo = g.ldc;
+                col_lim = g.N - n_w;
+                alpha = g.alpha;
+                beta = g.beta;
+            } else {
+                out = g.ws + (int64_t)(2 * blockIdx.x + which) * (16 * MT * 64);
+                ldo = 64;
+                col_lim = 64;
+                alpha = 1.f;
+                beta = 0.f;
+            }
+            which = 1;
+            step = q1 - q0;
+        }
+        if (!first) __syncthreads();       // the previous segment is done with the LDS
+        first = false;
+        skinny_segment<VEC, WAVES, MT>(g, red, n_w, kb, ke, out, ldo, col_lim, alpha, beta);
+        it += step;
     }
 }
 
 template <int WAVES, int MT>
 hipError_t launch_waves(bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
-    dim3 grid((unsigned)g.tiles_n, 1, (unsigned)splits);
+    dim3 grid(g.sk_iters > 0 ? (unsigned)g.sk_grid : (unsigned)g.tiles_n, 1, g.sk_iters > 0 ? 1u : (unsigned)splits);
     if (vec)
         hipLaunchKernelGGL((skinny_gemm_kernel<true, WAVES, MT>), grid, dim3(64 * WAVES), 0, stream, g);
     else

@@ -99,6 +99,11 @@ def test_scalars_on_every_path(oracle_mod, path, tile):
     for split in (1, 3):
         check(oracle_mod, M, 264, 200, False, False, f"{path}/{tile}/split{split}", path=path, tile=tile,
               split_k=split, alpha=-1.5, beta=0.25)
+    if path == "skinny":       # alpha and beta applied by the stream-K fix-up and by whole strips
+        check(oracle_mod, M, 264, 200, False, False, "skinny/stream_k", path=path, decomposition="stream_k",
+              alpha=-1.5, beta=0.25)
+        check(oracle_mod, 24, 700, 130, False, False, "skinny/stream_k/32", path=path, decomposition="stream_k",
+              alpha=2.0, beta=-0.5)
 
 
 def test_beta_zero_ignores_c_and_alpha_zero_ignores_ab(oracle_mod):

@@ -113,6 +113,24 @@ def test_skinny(oracle_mod, shape, vector, split_k):
     check_case(oracle_mod, *shape, f"skinny/v{vector}/s{split_k}", path="skinny", vector=vector, split_k=split_k)
 
 
+@pytest.mark.parametrize("vector", [0, 1])
+@pytest.mark.parametrize("shape", [
+    (16, 3000, 1000),      # 47 strips x 16 K-steps over 256 workgroups: ranges straddle strips
+    (5, 700, 333),         # one K-step per workgroup: every strip summed from six slots, K tail
+    (32, 1000, 4100),      # two row blocks (tile 2)
+    (16, 12800, 128),      # whole strips only: no partial strip, no fix-up
+    (1, 1000, 200),        # a single row, K not a multiple of the step
+], ids=lambda s: "x".join(map(str, s)))
+def test_skinny_stream_k(oracle_mod, shape, vector):
+    """The skinny kernel's stream-K decomposition (equal ranges of (strip,
+    K-step) units, partial strips summed by the fix-up kernel)."""
+    M, N, K = shape
+    plan = lib.sgemm_plan_query(M, N, K, path="skinny", decomposition="stream_k", vector=vector)
+    assert plan["decomposition_name"] == "stream_k" and plan["workgroups"] <= 256
+    check_case(oracle_mod, M, N, K, f"skinny stream-K v{vector}", path="skinny", decomposition="stream_k",
+               vector=vector)
+
+
 @pytest.mark.parametrize("tile", [0, 1, 2])
 def test_skinny_tiles(oracle_mod, tile):
     """Every skinny tile on the rows it holds (16, or 32 with two row blocks)."""
