@@ -94,7 +94,7 @@ typedef enum sgemm_decomposition {
     SGEMM_DECOMP_AUTO = 0,      /* per-shape choice */
     SGEMM_DECOMP_TILES = 1,     /* one output tile (and K slice) per workgroup */
     SGEMM_DECOMP_STREAM_K = 2   /* persistent workgroups share the tiles' K-steps evenly
-                                   (MFMA path only) */
+                                   (MFMA path; skinny path with tiles 0 and 2) */
 } sgemm_decomposition;
 
 /*
