@@ -128,6 +128,15 @@ def test_bad_options_rejected():
     assert lib.sgemm_raw(*base, opts=lib._options(path="skinny")) == 1          # M > 32
     few = (20, 64, 64, A, 64, B, 64, C, 64)
     assert lib.sgemm_raw(*few, opts=lib._options(path="skinny", tile=0)) == 1   # tile 0 holds 16 rows
+    # skinny stream-K: the 64-deep K-step tiles only, and no split-K with it
+    sk = (16, 64, 640)
+    assert lib.sgemm_plan_query(*sk, path="skinny", tile=0, decomposition="stream_k")["decomposition_name"] == \
+        "stream_k"
+    for kw in ({"tile": 1}, {"split_k": 2}):
+        with pytest.raises(lib.SgemmError):
+            lib.sgemm_plan_query(*sk, path="skinny", decomposition="stream_k", **kw)
+    with pytest.raises(lib.SgemmError):
+        lib.sgemm_plan_query(*sk, path="valu", decomposition="stream_k")
     assert lib.sgemm_raw(*base, opts=lib._options(path="naive", split_k=2)) == 1
     assert lib.sgemm_raw(*base, opts=lib._options(workspace=A + 16, workspace_bytes=1 << 20)) == 1
     assert lib.sgemm_raw(*base, opts=lib._options(pack=-1)) == 1
