@@ -425,14 +425,15 @@ def test_large_workspace_allocated_per_call(oracle_mod):
 
 
 @pytest.mark.parametrize("opts", [{"path": "mfma", "tile": 13, "split_k": 4, "decomposition": "tiles"},
-                                  {"path": "mfma", "tile": 15, "decomposition": "stream_k"}, {}],
-                         ids=["split4", "streamk", "auto"])
+                                  {"path": "mfma", "tile": 15, "decomposition": "stream_k"}, {},
+                                  {"path": "skinny", "decomposition": "stream_k"}],
+                         ids=["split4", "streamk", "auto", "skinny-streamk"])
 def test_graph_capture_replays(oracle_mod, opts):
     """A call captured into a graph (its workspace then belongs to the graph,
     not to the library's per-stream buffer) replays correctly: new inputs are
     copied in eagerly between replays, and every replay is checked."""
     say(f"graph capture {opts}")
-    M, N, K = 520, 390, 1100
+    M, N, K = (24, 700, 1100) if opts.get("path") == "skinny" else (520, 390, 1100)
     Ad = torch.empty((M, K), device=DEV)
     Bd = torch.empty((K, N), device=DEV)
     C = torch.empty((M, N), device=DEV)
