@@ -463,15 +463,18 @@ def test_graph_capture_replays(oracle_mod, opts):
 
 # --- the benchmark workloads at full size, in the benchmark's launch configuration ---------
 
-def _full_size_check(oracle_mod, w, kind):
-    say(f"full size {w.name} inputs={kind}")
+def _full_size_check(oracle_mod, w, kind, opts=None):
+    say(f"full size {w.name} inputs={kind} opts={opts}")
     A = workloads.with_ld(workloads.draw(w.M, w.K, kind, w.seed_base + 0, w.a_std if kind != "integer" else 1.0),
                           w.lda)
     B = workloads.with_ld(workloads.draw(w.K, w.N, kind, w.seed_base + 1, w.b_std if kind != "integer" else 1.0),
                           w.ldb)
     Ad, Bd = to_dev(A), to_dev(B)
     C = torch.full((w.M, w.N), float("nan"), dtype=torch.float32, device=DEV)
-    lib.sgemm(Ad, Bd, C)                 # the default plan, as the benchmark runs it
+    if opts:
+        lib.sgemm_ex(Ad, Bd, C, **opts)
+    else:
+        lib.sgemm(Ad, Bd, C)             # the default plan, as the benchmark runs it
     torch.cuda.synchronize()
     del Ad, Bd
     Ch = C.cpu().numpy()
@@ -509,6 +512,15 @@ def _full_size_check(oracle_mod, w, kind):
 def test_full_size_workload(oracle_mod, name):
     w = workloads.CONFIGS[name]
     _full_size_check(oracle_mod, w, w.a_kind)
+
+
+@pytest.mark.parametrize("kind", ["normal", "integer"])
+def test_full_size_skinny_stream_k(oracle_mod, kind):
+    """The skinny workload at full size through the skinny stream-K plan (the
+    default plan streams it on 172 CUs instead; this one spreads it over all
+    256 and sums the shared strips in the fix-up)."""
+    w = workloads.CONFIGS["linear_skinny_16x4096x11008"]
+    _full_size_check(oracle_mod, w, kind, {"path": "skinny", "decomposition": "stream_k"})
 
 
 @pytest.mark.parametrize("name", list(workloads.CONFIGS))
