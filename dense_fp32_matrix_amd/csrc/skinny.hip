@@ -6,9 +6,11 @@
 // GEMV example of "如何让计算受限问题真正达到计算受限", section 7.  The kernel
 // is therefore built to stream B with deep memory-level parallelism and no
 // LDS staging:
-//   * a wave owns 64 columns of C and a quarter of the workgroup's K slice;
-//     a workgroup (4 or 8 waves) owns 64 columns and one K slice, and slices
-//     of K across workgroups are summed by the split-K reduction;
+//   * a wave owns 64 columns of C and a quarter of the workgroup's K range;
+//     a workgroup (4 or 8 waves) owns a 64-column strip and one K slice, whose
+//     partial sums across workgroups the split-K reduction adds, or (stream-K)
+//     an equal share of all (strip, K-step) units, partial strips being added
+//     by the stream-K fix-up;
 //   * lane l = 16 * kk + jj loads B[k][n + 4jj .. 4jj+3] as one 16-byte read
 //     for k = k0 + 4kk + t (t = 0..3): 16 lanes cover a 256-byte run of a row;
 //   * component c of that vector is the B operand of v_mfma_f32_16x16x4_f32
