@@ -107,7 +107,7 @@ constexpr double kTileVisit = 2e-6;          // filling and draining one tile's 
 double mfma_efficiency(int tile, bool vec) {
     if (!vec) {
         switch (tile) {
-            case 8: case 9: case 11: case 12: case 17: return 0.66;
+            case 8: case 9: case 11: case 12: case 17: case 18: return 0.66;
             case 10: case 13: case 14: case 16: return 0.58;
             case 15: return 0.55;
             case 2: return 0.62;
@@ -116,6 +116,7 @@ double mfma_efficiency(int tile, bool vec) {
         }
     }
     switch (tile) {
+        case 18: return 0.93;
         case 17: return 0.927;
         case 11: case 12: return 0.92;
         case 8: return 0.91;
@@ -275,11 +276,17 @@ void choose_split(int64_t tiles, int64_t K, int bk, int64_t target_wgs, int64_t 
     *k_chunk = kc;
 }
 
-// Best MFMA plan for the given operand alignment (vec), operand layouts (trans) and K.
-Candidate mfma_best(const sgemm_options& o, bool vec, bool trans, int64_t M, int64_t N, int64_t K) {
+// Best MFMA plan for the given operand alignment (vec), operand layouts
+// (ops: bit 0 = A stored transposed, bit 1 = B stored transposed) and K.
+// Of the two 256x256 eight-wave tiles, the two-stage one (18) measured faster
+// with A k-contiguous and B k-major, or A k-major (NN, TN, TT: +0.3 to
+// +1.4 %) and the three-stage one (17) with both k-contiguous (NT: +1 %), so
+// the automatic choice takes each where it is faster.
+Candidate mfma_best(const sgemm_options& o, bool vec, int ops, int64_t M, int64_t N, int64_t K) {
+    const bool trans = ops != 0;
     std::vector<int> cands;
     if (o.tile >= 0) cands.push_back(o.tile);
-    else cands = {17, 11, 16, 13, 15, 8, 3, 10, 0, 1, 2, 5, 4};
+    else cands = {ops == 2 ? 17 : 18, 11, 16, 13, 15, 8, 3, 10, 0, 1, 2, 5, 4};
     Candidate best;
     bool have = false;
     for (int tile : cands) {
@@ -329,6 +336,7 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
     if (o.workspace != nullptr && !aligned(o.workspace, 256)) return SGEMM_ERR_INVALID_ARG;
     const int64_t M = c.M, N = c.N, K = c.K;
     const bool trans = c.ta || c.tb;
+    const int ops = (c.ta ? 1 : 0) | (c.tb ? 2 : 0);
 
     Plan p;
     std::memset(&p.pub, 0, sizeof(p.pub));
@@ -427,7 +435,7 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
             return SGEMM_ERR_INVALID_ARG;
         }
     } else if (path == SGEMM_PATH_MFMA) {
-        best = mfma_best(o, q.vector != 0, trans, M, N, K);
+        best = mfma_best(o, q.vector != 0, ops, M, N, K);
         // Alternative: copy the misaligned operand(s), in their stored
         // orientation, into aligned, zero-padded workspace first and run the
         // 16-byte loaders.  A K that the KC layout would cut mid-chunk is
@@ -442,7 +450,7 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
             double bytes = 0;
             if (pack_a) bytes += 4.0 * (c.a_rows() * c.a_cols() + ar * ac);
             if (pack_b) bytes += 4.0 * (c.b_rows() * c.b_cols() + br * bc);
-            Candidate cand = mfma_best(o, true, trans, M, N, kp);
+            Candidate cand = mfma_best(o, true, ops, M, N, kp);
             cand.time += bytes / kPackBw + (pack_a + pack_b) * kLaunch;
             if (o.pack == 2 || cand.time < best.time) {
                 best = cand;

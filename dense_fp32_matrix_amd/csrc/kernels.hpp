@@ -100,6 +100,7 @@ constexpr TileShape kMfmaTiles[] = {
     {64, 64, 32, 2, 2, 2, 1, 3, true, true},   // 15: direct-to-LDS, 4 waves of 32x32: small products, thin M or N
     {128, 128, 16, 2, 4, 2, 1, 3, true, true},   // 16: as 14 with 8 waves (two per SIMD) of 64x32, 16-deep K-step
     {256, 256, 16, 4, 2, 2, 1, 3, true},   // 17: as 11 with the 8 waves as 4 x 2 (64x128 each)
+    {256, 256, 16, 4, 2, 2, 1, 2, true},   // 18: as 17 with two stages: step s + 1 loads during step s
 };
 constexpr int kNumMfmaTiles = sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]);
 

@@ -922,11 +922,12 @@ hipError_t launch_mfma(int tile, bool vec, int ops, const GemmArgs& g, int split
         SGEMM_MFMA_CASE(15)
         SGEMM_MFMA_CASE(16)
         SGEMM_MFMA_CASE(17)
+        SGEMM_MFMA_CASE(18)
         default:
             return hipErrorInvalidValue;
     }
 #undef SGEMM_MFMA_CASE
 }
-static_assert(kNumMfmaTiles == 18, "launch_mfma covers every MFMA tile");
+static_assert(kNumMfmaTiles == 19, "launch_mfma covers every MFMA tile");
 
 }  // namespace sgemm_impl

@@ -65,6 +65,7 @@ PLANS = [
     {"path": "mfma", "tile": 15, "decomposition": "tiles", "split_k": 1},
     {"path": "mfma", "tile": 16, "decomposition": "stream_k"},
     {"path": "mfma", "tile": 17, "decomposition": "tiles", "split_k": 1},
+    {"path": "mfma", "tile": 18, "decomposition": "stream_k"},
     {"path": "naive"},
 ]
 

@@ -155,7 +155,7 @@ STREAMK_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("tile", [3, 0, 2, 8, 10, 11, 12, 13, 14, 15, 16, 17])
+@pytest.mark.parametrize("tile", [3, 0, 2, 8, 10, 11, 12, 13, 14, 15, 16, 17, 18])
 @pytest.mark.parametrize("vector", [0, 1])
 @pytest.mark.parametrize("shape", STREAMK_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_stream_k(oracle_mod, shape, tile, vector):
@@ -186,7 +186,7 @@ def test_padded_leading_dimensions(oracle_mod, path):
     assert_bit_exact(Cbuf.numpy(), ref, what=f"{path} padded")
 
 
-@pytest.mark.parametrize("tile", [17, 8, 11, 16, 15])
+@pytest.mark.parametrize("tile", [18, 17, 8, 11, 16, 15])
 @pytest.mark.parametrize("gap", [4, 7], ids=["ldc16B", "ldcodd"])
 def test_epilogue_keeps_ldc_gap(oracle_mod, tile, gap):
     """Each tile's epilogue (the 16-byte interleaved-column stores of tiles 8
