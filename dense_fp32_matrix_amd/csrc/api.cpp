@@ -96,7 +96,8 @@ constexpr double kStreamKBw = 1e13;          // bytes/s for stream-K partial til
                                              // by neighbouring workgroups, cache resident)
 constexpr double kLaunch = 8e-6;             // one more dependent kernel launch
 constexpr double kSkinnyCuBw = 31e9;         // bytes/s one CU's skinny workgroup streams from B (one row
-                                             // block; two row blocks are bound by the matrix pipe at 20e9)
+                                             // block; two row blocks, with twice the MFMAs per byte and
+                                             // half the loads in flight, at 20e9)
 constexpr double kSkinnyHbmBw = 5.3e12;      // bytes/s the whole chip streams B at
 constexpr double kTileVisit = 2e-6;          // filling and draining one tile's pipeline, and its epilogue
 
