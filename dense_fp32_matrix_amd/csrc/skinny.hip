@@ -22,11 +22,11 @@
 //     MFMAs of both blocks, so B is still read once;
 //   * masked-off elements (rows >= M, columns >= N, k past the slice) load
 //     from a 16-byte zero block, so loads are never followed by a select;
-//   * two register stages of 4 k-groups of 16 each keep 2 x 4 x 4 = 32 16-byte
-//     B loads per lane in flight while the previous stage is contracted; with
-//     two row blocks a stage holds 2 k-groups, so that the A and B registers
-//     of both stages fit the 256 of a wave at two waves per SIMD (4 groups
-//     spill there, and measured 9-14 % slower at M = 17-32);
+//   * two register stages of 2 k-groups of 16 each keep 2 x 2 x 4 = 16 16-byte
+//     B loads per lane in flight while the previous stage is contracted
+//     (measured: 4 groups per stage are 2-4 % slower with one row block and
+//     spill with two, 9-14 % slower; 3 are 3-12 % slower and 1 is 6 % slower
+//     with two row blocks);
 //   * the waves' partial tiles are summed through LDS in wave order.
 // Operand layout of v_mfma_f32_16x16x4_f32 (wave64):
 //   A: lane l holds A[i = l % 16][kk = l / 16];  B: lane l holds B[kk = l / 16][j = l % 16];
@@ -43,8 +43,9 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGroups = 4;                 // k-groups of 16 per register stage (one row block)
-constexpr int kStageK = 16 * kGroups;      // K elements of one stream-K unit
+constexpr int kStageK = 64;                // K elements of one stream-K unit
+constexpr int kGroups = 2;                 // k-groups of 16 per register stage
+constexpr int kRegK = 16 * kGroups;        // K elements per register stage per wave
 
 // One segment: the 64-column strip of B starting at column n_w over
 // k in [kb, ke), split in K across the waves (quarters rounded up to 16),
@@ -76,14 +77,12 @@ __device__ __forceinline__ void skinny_segment(const GemmArgs& g, float (&red)[W
     const int ncol = n_w + 4 * jj;               // first of this lane's 4 columns
 
     static_assert(MT == 1 || MT == 2, "one or two row blocks");
-    constexpr int SG = kGroups / MT;           // k-groups per register stage
-    constexpr int SK = 16 * SG;                // K elements per stage per wave
-    f32x4 ra[2][MT][SG];
-    f32x4 rb[2][SG][4];
+    f32x4 ra[2][MT][kGroups];
+    f32x4 rb[2][kGroups][4];
 
     auto load_stage = [&](int buf, int k0) {
 #pragma unroll
-        for (int gi = 0; gi < SG; ++gi) {
+        for (int gi = 0; gi < kGroups; ++gi) {
             const int ka = k0 + 16 * gi + 4 * kk;          // this lane's 4 k's
 #pragma unroll
             for (int b = 0; b < MT; ++b) {
@@ -124,7 +123,7 @@ __device__ __forceinline__ void skinny_segment(const GemmArgs& g, float (&red)[W
 
     auto compute_stage = [&](int buf) {
 #pragma unroll
-        for (int gi = 0; gi < SG; ++gi)
+        for (int gi = 0; gi < kGroups; ++gi)
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -135,14 +134,14 @@ __device__ __forceinline__ void skinny_segment(const GemmArgs& g, float (&red)[W
                                                                          acc[b][c], 0, 0, 0);
     };
 
-    const int nst = (wke - wkb + SK - 1) / SK;
+    const int nst = (wke - wkb + kRegK - 1) / kRegK;
     if (nst > 0) {
         load_stage(0, wkb);
         int s = 0;
         for (; s + 2 <= nst; s += 2) {
-            load_stage(1, wkb + (s + 1) * SK);
+            load_stage(1, wkb + (s + 1) * kRegK);
             compute_stage(0);
-            if (s + 2 < nst) load_stage(0, wkb + (s + 2) * SK);
+            if (s + 2 < nst) load_stage(0, wkb + (s + 2) * kRegK);
             compute_stage(1);
         }
         if (s < nst) compute_stage(0);
