@@ -392,8 +392,9 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
         // shares the (strip, 64-deep K-step) units out evenly over one
         // workgroup per CU and a fix-up sums the strips that two workgroups
         // share.  Both are floored by the chip's streaming rate: with one row
-        // block 172 strips already reach it, and stream-K pays only where the
-        // CUs, not HBM, are the limit (two row blocks, long K).
+        // block 172 strips already reach it, and stream-K pays where the CUs,
+        // not HBM, are the limit (two row blocks, long K) or where the uniform
+        // split needs 4 or more slices.
         best.tile = o.tile >= 0 ? o.tile : (M <= 16 ? 0 : 2);
         const TileShape& t = kSkinnyTiles[best.tile];
         if (M > t.bm) return SGEMM_ERR_INVALID_ARG;     // the tile holds at most bm rows of A
@@ -422,7 +423,11 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
             const double t_tiles = std::max(floor, (double)cdiv(wgs, kNumCUs) * (k_chunk / 64.0) * per_unit) +
                                    (best.splits > 1 ? kLaunch : 0.0);
             const double t_sk = std::max(floor, ipw * per_unit) + kLaunch;
-            if (o.decomposition == SGEMM_DECOMP_STREAM_K || t_sk < 0.95 * t_tiles) {
+            // with 4 or more uniform slices the two plans stream the same
+            // shares; the stream-K fix-up then measured 2-12 % faster than the
+            // split-K reduction of the slices, so stream-K takes the tie there
+            const bool sk_wins = best.splits >= 4 ? t_sk <= t_tiles : t_sk < 0.95 * t_tiles;
+            if (o.decomposition == SGEMM_DECOMP_STREAM_K || sk_wins) {
                 best.decomposition = SGEMM_DECOMP_STREAM_K;
                 best.splits = 1;
                 best.k_chunk = K;
