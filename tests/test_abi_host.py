@@ -302,3 +302,20 @@ def test_plan_cache_keys():
     z = lib.gemm_plan_query("N", "N", M, N, K, alpha=0.0, beta=2.0)
     assert z["launches"] == 1 and z["workspace_bytes"] == 0
     assert lib.gemm_plan_query("N", "N", M, N, K) == first
+
+
+def test_skinny_stream_k_takes_ties_at_four_slices():
+    """The skinny planner's choice between uniform K slices and stream-K:
+    where the uniform plan needs 4 or more slices the two stream equal
+    shares and stream-K is chosen; with 172 strips and no split (one
+    workgroup per strip), or 2 slices, the uniform plan stays."""
+    for M, N, K in [(16, 256, 65536), (4, 1024, 16384), (16, 2048, 8192), (32, 4096, 4096), (16, 4096, 11008)]:
+        p = lib.sgemm_plan_query(M, N, K)
+        assert p["path_name"] == "skinny" and p["decomposition_name"] == "stream_k", (M, N, K, p)
+        assert p["split_k"] == 1 and p["workgroups"] == 256
+        tiles = lib.sgemm_plan_query(M, N, K, decomposition="tiles")
+        assert tiles["split_k"] >= 4, (M, N, K, tiles)
+    for M, N, K, split in [(16, 11008, 4096, 1), (8, 8192, 8192, 2)]:
+        p = lib.sgemm_plan_query(M, N, K)
+        assert p["path_name"] == "skinny" and p["decomposition_name"] == "tiles", (M, N, K, p)
+        assert p["split_k"] == split
