@@ -121,8 +121,7 @@ def _options(path="auto", tile=-1, split_k=0, vector=0, decomposition="auto", wo
     return o
 
 
-def _matrix(t, name):
-    """(pointer, rows, cols, ld) of a 2-D float32 device tensor with unit column stride."""
+def _check_tensor(t, name):
     import torch
     if not isinstance(t, torch.Tensor) or t.dim() != 2:
         raise TypeError(f"{name} must be a 2-D torch tensor")
@@ -130,11 +129,37 @@ def _matrix(t, name):
         raise TypeError(f"{name} must be float32, got {t.dtype}")
     if not t.is_cuda:
         raise TypeError(f"{name} must be on a GPU")
+
+
+def _storage_layout(shape, strides, name, allow_column_major=False):
+    """(op, ld) of a 2-D view with this shape and these element strides:
+    op 0 for a row-major view (ld = the row stride), op 1 for a column-major
+    one (the transpose of a row-major matrix, ld = the column stride; only
+    when allow_column_major).  Stored rows must not overlap: a leading
+    dimension below the stored width -- a broadcast view with stride 0, or
+    an as_strided view whose rows share elements -- is rejected rather than
+    widened, which would address memory outside the tensor."""
+    rows, cols = shape
+    rs, cs = strides
+    if cols <= 1 or cs == 1:
+        if rows > 1 and rs < max(cols, 1):
+            raise ValueError(f"{name}: row stride {rs} is below the row width {cols} (overlapping rows)")
+        return 0, (rs if rows > 1 else max(cols, 1))
+    if allow_column_major and (rows <= 1 or rs == 1):
+        if cs < max(rows, 1):
+            raise ValueError(f"{name}: column stride {cs} is below the column height {rows} (overlapping columns)")
+        return 1, cs
+    if allow_column_major:
+        raise ValueError(f"{name} must be row-major or column-major (one unit stride)")
+    raise ValueError(f"{name} must have unit column stride (row-major)")
+
+
+def _matrix(t, name):
+    """(pointer, rows, cols, ld) of a 2-D float32 row-major device tensor."""
+    _check_tensor(t, name)
     rows, cols = t.shape
-    if cols > 1 and t.stride(1) != 1:
-        raise ValueError(f"{name} must have unit column stride (row-major)")
-    ld = t.stride(0) if rows > 1 else max(cols, 1)
-    return (t.data_ptr() if t.numel() else None), rows, cols, max(ld, cols, 1)
+    _, ld = _storage_layout((rows, cols), t.stride(), name)
+    return (t.data_ptr() if t.numel() else None), rows, cols, ld
 
 
 def _stream_handle(stream, device):
@@ -202,21 +227,10 @@ def _operand(t, name):
     """(pointer, op, rows, cols, ld) of the logical 2-D operand t: a row-major
     tensor is passed as stored (op N); a column-major one (a transposed view of
     a row-major matrix) as the stored matrix with op T."""
-    import torch
-    if not isinstance(t, torch.Tensor) or t.dim() != 2:
-        raise TypeError(f"{name} must be a 2-D torch tensor")
-    if t.dtype != torch.float32:
-        raise TypeError(f"{name} must be float32, got {t.dtype}")
-    if not t.is_cuda:
-        raise TypeError(f"{name} must be on a GPU")
+    _check_tensor(t, name)
     rows, cols = t.shape
-    if cols <= 1 or t.stride(1) == 1:
-        ld = t.stride(0) if rows > 1 else max(cols, 1)
-        return (t.data_ptr() if t.numel() else None), 0, rows, cols, max(ld, cols, 1)
-    if rows <= 1 or t.stride(0) == 1:
-        ld = t.stride(1) if cols > 1 else max(rows, 1)
-        return (t.data_ptr() if t.numel() else None), 1, rows, cols, max(ld, rows, 1)
-    raise ValueError(f"{name} must be row-major or column-major (one unit stride)")
+    op, ld = _storage_layout((rows, cols), t.stride(), name, allow_column_major=True)
+    return (t.data_ptr() if t.numel() else None), op, rows, cols, ld
 
 
 def gemm(A, B, C=None, stream=None, *, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, **options):

@@ -102,53 +102,33 @@ constexpr double kSkinnyHbmBw = 5.3e12;      // bytes/s the whole chip streams B
 constexpr double kTileVisit = 2e-6;          // filling and draining one tile's pipeline, and its epilogue
 
 // Share of the CU's peak one tile shape sustains when its CU is full, with
-// 16-byte (vec) or 4-byte loaders.  The register-staged 4-byte loaders need
-// more registers than the larger tiles leave and spill; the direct-to-LDS
-// tiles (8-10) stage nothing in registers.
+// 16-byte (vec) or 4-byte load lanes (measured; the 256 x 256 tiles have no
+// 4-byte-lane build).
 double mfma_efficiency(int tile, bool vec) {
     if (!vec) {
         switch (tile) {
-            case 8: case 9: case 11: case 12: case 17: case 18: return 0.66;
-            case 10: case 13: case 14: case 16: return 0.58;
-            case 15: return 0.55;
-            case 2: return 0.62;
-            case 4: return 0.60;
-            default: return 0.55;
+            case 2: return 0.58;
+            case 3: return 0.55;
+            default: return 0.0;
         }
     }
     switch (tile) {
-        case 18: return 0.93;
-        case 17: return 0.927;
-        case 11: case 12: return 0.92;
-        case 8: return 0.91;
-        case 9: return 0.905;
-        case 13: return 0.89;
-        case 16: return 0.91;
-        case 14: return 0.90;
-        case 15: return 0.80;
-        case 3: case 6: return 0.89;
-        case 10: return 0.87;
-        case 0: case 1: case 7: return 0.85;
-        case 2: case 5: return 0.83;
+        case 0: return 0.93;
+        case 1: return 0.927;
+        case 2: return 0.91;
+        case 3: return 0.80;
         default: return 0.70;
     }
 }
 
 // Share of the CU's peak when the CU holds a single workgroup of a tile
 // built for two or more per CU (a tail shorter than one wave of
-// workgroups).  Register-staged tiles depend on a second workgroup to hide
-// their loads; the 128x128 direct-to-LDS tile keeps most of its rate; the
-// 64x64 one, which moves twice the bytes per multiply-add of the 128x128
-// tile through the CU's load path and LDS, runs a little faster with them
-// to itself.
+// workgroups).  The 64 x 64 tile, which moves twice the bytes per
+// multiply-add of the 128 x 128 tile through the CU's load path and LDS,
+// runs a little faster with them to itself.
 double mfma_alone_efficiency(int tile, bool vec) {
     const double e = mfma_efficiency(tile, vec);
-    switch (tile) {
-        case 13: return 0.79 * e;
-        case 15: return 1.0375 * e;
-        case 2: return 0.75 * e;
-        default: return e;
-    }
+    return tile == 3 ? 1.0375 * e : e;
 }
 
 int wgs_per_cu(const TileShape& t) { return std::max(1, t.waves_per_simd * 4 / (t.waves_m * t.waves_n)); }
@@ -278,20 +258,20 @@ void choose_split(int64_t tiles, int64_t K, int bk, int64_t target_wgs, int64_t 
 }
 
 // Best MFMA plan for the given operand alignment (vec), operand layouts
-// (ops: bit 0 = A stored transposed, bit 1 = B stored transposed) and K.
-// Of the two 256x256 eight-wave tiles, the two-stage one (18) measured faster
-// with A k-contiguous and B k-major, or A k-major (NN, TN, TT: +0.3 to
-// +1.4 %) and the three-stage one (17) with both k-contiguous (NT: +1 %), so
-// the automatic choice takes each where it is faster.
-Candidate mfma_best(const sgemm_options& o, bool vec, int ops, int64_t M, int64_t N, int64_t K) {
-    const bool trans = ops != 0;
+// (ops: bit 0 = A stored transposed, bit 1 = B stored transposed) and K;
+// false when no tile fits (a forced 256 x 256 tile with 4-byte lanes).
+// Of the two 256 x 256 tiles, the two-stage one (0) measured faster with A
+// k-contiguous and B k-major, or A k-major (NN, TN, TT: +0.3 to +1.4 %) and
+// the three-stage one (1) with both k-contiguous (NT: +1 %), so the
+// automatic choice takes each where it is faster.
+bool mfma_best(const sgemm_options& o, bool vec, int ops, int64_t M, int64_t N, int64_t K, Candidate* out) {
     std::vector<int> cands;
     if (o.tile >= 0) cands.push_back(o.tile);
-    else cands = {ops == 2 ? 17 : 18, 11, 16, 13, 15, 8, 3, 10, 0, 1, 2, 5, 4};
+    else cands = {ops == 2 ? 1 : 0, 2, 3};
     Candidate best;
     bool have = false;
     for (int tile : cands) {
-        if (trans && !kMfmaTiles[tile].trans) continue;   // operands stored transposed
+        if (!vec && !kMfmaTiles[tile].narrow) continue;   // built for 16-byte lanes only
         std::vector<Candidate> cs;
         if (o.decomposition != SGEMM_DECOMP_STREAM_K) {
             if (o.split_k > 0) {
@@ -320,7 +300,8 @@ Candidate mfma_best(const sgemm_options& o, bool vec, int ops, int64_t M, int64_
             }
         }
     }
-    return best;
+    if (have) *out = best;
+    return have;
 }
 
 constexpr double kPackBw = 3e12;   // bytes/s read + written by the pack kernel
@@ -374,7 +355,6 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
     if (path == SGEMM_PATH_SKINNY && M > 32) return SGEMM_ERR_INVALID_ARG;
     const int ntiles = tile_count(path);
     if (o.tile < -1 || o.tile >= ntiles) return SGEMM_ERR_INVALID_ARG;
-    if (path == SGEMM_PATH_MFMA && trans && o.tile >= 0 && !kMfmaTiles[o.tile].trans) return SGEMM_ERR_INVALID_ARG;
     if (path == SGEMM_PATH_NAIVE && o.split_k > 1) return SGEMM_ERR_INVALID_ARG;
     if (o.decomposition == SGEMM_DECOMP_STREAM_K &&
         ((path != SGEMM_PATH_MFMA && path != SGEMM_PATH_SKINNY) || o.split_k > 1))
@@ -395,7 +375,7 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
         // block 172 strips already reach it, and stream-K pays where the CUs,
         // not HBM, are the limit (two row blocks, long K) or where the uniform
         // split needs 4 or more slices.
-        best.tile = o.tile >= 0 ? o.tile : (M <= 16 ? 0 : 2);
+        best.tile = o.tile >= 0 ? o.tile : (M <= 16 ? 0 : 1);
         const TileShape& t = kSkinnyTiles[best.tile];
         if (M > t.bm) return SGEMM_ERR_INVALID_ARG;     // the tile holds at most bm rows of A
         const int64_t tiles = cdiv(N, t.bn);
@@ -410,8 +390,8 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
         const int64_t k_chunk = round_up(cdiv(K, splits), t.bk);
         best.splits = cdiv(K, k_chunk);
         best.k_chunk = k_chunk;
-        // stream-K units are the kernel's 64-deep K-steps (the tiles with bk == 64)
-        const bool sk_ok = t.bk == 64 && o.split_k <= 1 && o.decomposition != SGEMM_DECOMP_TILES;
+        // stream-K units are the kernel's 64-deep K-steps
+        const bool sk_ok = o.split_k <= 1 && o.decomposition != SGEMM_DECOMP_TILES;
         if (sk_ok) {
             const int64_t k_steps = cdiv(K, 64);
             const int64_t units = tiles * k_steps;
@@ -437,11 +417,12 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
                 best.dp_tiles = 0;
                 best.sk_ipw = cdiv(units, best.grid);
             }
-        } else if (o.decomposition == SGEMM_DECOMP_STREAM_K) {
-            return SGEMM_ERR_INVALID_ARG;
         }
     } else if (path == SGEMM_PATH_MFMA) {
-        best = mfma_best(o, q.vector != 0, ops, M, N, K);
+        // With 4-byte lanes only the narrow tiles are built; a forced tile
+        // without them can still run on packed copies.
+        const bool have = mfma_best(o, q.vector != 0, ops, M, N, K, &best);
+        if (!have && (o.vector == 1 || o.pack == 1)) return SGEMM_ERR_INVALID_ARG;
         // Alternative: copy the misaligned operand(s), in their stored
         // orientation, into aligned, zero-padded workspace first and run the
         // 16-byte loaders.  A K that the KC layout would cut mid-chunk is
@@ -456,9 +437,10 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
             double bytes = 0;
             if (pack_a) bytes += 4.0 * (c.a_rows() * c.a_cols() + ar * ac);
             if (pack_b) bytes += 4.0 * (c.b_rows() * c.b_cols() + br * bc);
-            Candidate cand = mfma_best(o, true, ops, M, N, kp);
+            Candidate cand;
+            mfma_best(o, true, ops, M, N, kp, &cand);
             cand.time += bytes / kPackBw + (pack_a + pack_b) * kLaunch;
-            if (o.pack == 2 || cand.time < best.time) {
+            if (o.pack == 2 || !have || cand.time < best.time) {
                 best = cand;
                 q.vector = 1;
                 q.packed = (pack_a ? 1 : 0) | (pack_b ? 2 : 0);

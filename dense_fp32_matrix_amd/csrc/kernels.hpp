@@ -73,40 +73,28 @@ struct TileShape {
     int bm, bn, bk;
     int waves_m, waves_n;   // waves per workgroup along M and N
     int waves_per_simd;     // occupancy the register budget is sized for
-    int sched = 1;          // >= 1: interleave LDS and global memory instructions between MFMAs,
-                            // with 8 * (sched - 1) MFMAs after the last LDS write of a K-step
-    int dtl = 0;            // > 0: stages of the direct-to-LDS loader (3 at most with 4-byte lanes)
-    bool trans = false;     // also instantiated for operands stored transposed (direct-to-LDS tiles only)
-    bool prio = false;      // direct-to-LDS tiles: raise the wave's priority while it issues a K-step's
+    int stages = 0;         // matrix-core tiles: LDS stages filled by direct global -> LDS loads
+    bool narrow = false;    // matrix-core tiles: also built with 4-byte load lanes (unaligned operands)
+    bool prio = false;      // matrix-core tiles: raise the wave's priority while it issues a K-step's
                             // MFMAs after its direct loads, back to normal before the barrier
 };
 
+// Matrix-core tiles.  Every one reads its operands with direct global -> LDS
+// loads and is built for the four operand layouts (A and B each as stored or
+// stored transposed).  The 256 x 256 tiles are built for 16-byte load lanes
+// only: with 4-byte lanes their running load pointers do not fit the
+// registers left next to 128 accumulators per lane, so unaligned operands
+// take the 128 x 128 or 64 x 64 tile, or are packed.
 constexpr TileShape kMfmaTiles[] = {
-    {256, 128, 16, 2, 2, 2, 0},   // 0: two workgroups per CU
-    {128, 256, 16, 2, 2, 2, 0},   // 1: two workgroups per CU, wide N
-    {128, 128, 16, 2, 2, 2, 0},   // 2: medium
-    {256, 256, 16, 2, 2, 1, 1},   // 3: one workgroup (one wave per SIMD) per CU, interleaved schedule
-    {64, 64, 16, 2, 2, 4, 0},     // 4: small products / split-K
-    {128, 128, 32, 2, 2, 2, 0},   // 5: medium, deeper K-step
-    {256, 256, 32, 2, 2, 1, 1},   // 6: as 3 with a deeper K-step (half the barriers)
-    {128, 256, 16, 2, 2, 2, 1},   // 7: as 1, interleaved schedule
-    {256, 256, 16, 2, 2, 1, 1, 3, true},   // 8: as 3, direct-to-LDS loads, three stages
-    {256, 256, 16, 2, 2, 1, 1, 4},   // 9: as 3, direct-to-LDS loads, four stages
-    {256, 128, 16, 2, 2, 2, 0, 3},   // 10: as 0, direct-to-LDS loads, three stages
-    {256, 256, 16, 2, 4, 2, 1, 3, true},   // 11: as 8 with 8 waves (two per SIMD), 128x64 per wave
-    {256, 256, 16, 2, 4, 2, 1, 4},   // 12: as 11, four stages
-    {128, 128, 16, 2, 2, 2, 1, 3, true},   // 13: direct-to-LDS, 4 waves of 64x64, up to two workgroups per CU
-    {128, 128, 32, 2, 2, 1, 1, 3, true},   // 14: as 13 with a 32-deep K-step (half the barriers), one per CU
-    {64, 64, 32, 2, 2, 2, 1, 3, true, true},   // 15: direct-to-LDS, 4 waves of 32x32: small products, thin M or N
-    {128, 128, 16, 2, 4, 2, 1, 3, true, true},   // 16: as 14 with 8 waves (two per SIMD) of 64x32, 16-deep K-step
-    {256, 256, 16, 4, 2, 2, 1, 3, true},   // 17: as 11 with the 8 waves as 4 x 2 (64x128 each)
-    {256, 256, 16, 4, 2, 2, 1, 2, true},   // 18: as 17 with two stages: step s + 1 loads during step s
+    {256, 256, 16, 4, 2, 2, 2},               // 0: 8 waves (two per SIMD) of 64 x 128; step s + 1 loads during step s
+    {256, 256, 16, 4, 2, 2, 3},               // 1: as 0 with three stages (faster when both operands are k-contiguous)
+    {128, 128, 16, 2, 4, 2, 3, true, true},   // 2: 8 waves of 64 x 32: fewer tiles than CUs at 256 x 256, long K
+    {64, 64, 32, 2, 2, 2, 3, true, true},     // 3: 4 waves of 32 x 32: small products, thin M or N
 };
 constexpr int kNumMfmaTiles = sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]);
 
 constexpr TileShape kValuTiles[] = {
     {128, 128, 8, 2, 2, 2},    // 0: 8x8 outputs per lane, 8x8 lanes per wave
-    {128, 128, 16, 2, 2, 2},   // 1: same, deeper K-step
 };
 constexpr int kNumValuTiles = sizeof(kValuTiles) / sizeof(kValuTiles[0]);
 
@@ -114,17 +102,18 @@ constexpr int kNumValuTiles = sizeof(kValuTiles) / sizeof(kValuTiles[0]);
 constexpr TileShape kNaiveTiles[] = {{4, 64, 1, 1, 1, 4}};
 constexpr int kNumNaiveTiles = 1;
 
-// Skinny products (M <= 16): a workgroup owns 16 rows x 64 columns and one K
-// slice, split over its waves (4 or 8); K slices are multiples of bk = 16 x waves.
+// Skinny products (M <= 32): a workgroup of 4 waves owns 16 (or 32) rows x
+// 64 columns and one K slice, split over its waves; K slices are multiples
+// of bk = 64, the stream-K unit.
 constexpr TileShape kSkinnyTiles[] = {
-    {16, 64, 64, 1, 4, 2},     // 0: 4 waves
-    {16, 64, 128, 1, 8, 2},    // 1: 8 waves
-    {32, 64, 64, 1, 4, 2},     // 2: 4 waves, two 16-row blocks of A (M <= 32)
+    {16, 64, 64, 1, 4, 2},     // 0: one 16-row block of A (M <= 16)
+    {32, 64, 64, 1, 4, 2},     // 1: two 16-row blocks of A (M <= 32)
 };
 constexpr int kNumSkinnyTiles = sizeof(kSkinnyTiles) / sizeof(kSkinnyTiles[0]);
 
 hipError_t launch_naive(const GemmArgs& g, hipStream_t stream);
-// ops: bit 0 = A stored transposed, bit 1 = B stored transposed (tiles with `trans` only).
+// ops: bit 0 = A stored transposed, bit 1 = B stored transposed.  vec == false
+// (4-byte lanes) only for the tiles marked `narrow`.
 hipError_t launch_mfma(int tile, bool vec, int ops, const GemmArgs& g, int splits, hipStream_t stream);
 hipError_t launch_valu(int tile, bool vec, const GemmArgs& g, int splits, hipStream_t stream);
 hipError_t launch_skinny(int tile, bool vec, const GemmArgs& g, int splits, hipStream_t stream);

@@ -5,16 +5,13 @@
 //   * Each workgroup owns one BM x BN tile of C (output-stationary, as in the
 //     throughput-matching page "如何让计算受限问题真正达到计算受限", section 1.2)
 //     and walks K in steps of BK.
-//   * Per K-step, the A tile (BM x BK) and B tile (BK x BN) reach LDS either
-//     straight from global memory (the direct-to-LDS tiles, the default; see
-//     mfma_tile_dtl) or through registers with coalesced loads (the
-//     register-staged tiles described here); out-of-range elements are
-//     zero-filled (the padding argument of section 七: a zero term leaves the
-//     sum alone).
-//   * Register-staged: two LDS stages; the loads of step t+1 are issued
-//     before step t is computed and land in the other stage afterwards, so
-//     one barrier per K-step suffices (section 六.1; "SGEMM 纯 CUDA 优化总结",
-//     ex9).
+//   * Per K-step, the A tile (BM x BK) and B tile (BK x BN) reach LDS
+//     straight from global memory (direct-to-LDS loads, see mfma_tile_dtl);
+//     elements past the end of K are zero-filled (the padding argument of
+//     section 七: a zero term leaves the sum alone).
+//   * DS LDS stages: the loads of step s + DS - 1 are issued while step s is
+//     computed, and one barrier per K-step makes a stage visible (section 六;
+//     "SGEMM 纯 CUDA 优化总结", ex9).
 //   * Each wave owns a WM x WN sub-tile as (WM/32) x (WN/32) blocks of
 //     v_mfma_f32_32x32x2_f32: true FP32 products, FP32 accumulation.
 //
@@ -25,29 +22,8 @@
 //              i = 8 * (r / 4) + 4 * (l / 32) + (r % 4)          (32 x 32)
 // A k-group of 8 is split so that lane half h = l / 32 takes k = 4h + q for
 // q = 0..3 and instruction q contracts k in {q, 4 + q}: every k of the group
-// is used once, and the A fragment of a lane is 4 consecutive k of one row,
-// read from LDS with a single 16-byte read.
-//
-// LDS layout of the register-staged tiles, per stage:
-//   As[BM][BK]      row-major like A, no padding; the 16-byte chunk c of row
-//                   r is stored at chunk position c ^ swz(r).  The XOR
-//                   swizzle (one of the three bank-conflict fixes of "SGEMM
-//                   纯 CUDA 优化总结", Q7) is chosen so that both the 16-byte
-//                   fragment reads (32 rows, one chunk each) and the 16-byte
-//                   tile writes (BK/4 lanes per row) hit distinct banks, for
-//                   32 or 64 four-byte banks.
-//   Bs[BK][BN + 8]  row-major like B; the two lane halves read rows 4 apart,
-//                   offset by 4 * (BN + 8) = 32 (mod 64) banks.
-//
-// Schedule of one register-staged K-step t (stages alternate between two
-// LDS buffers):
-//   issue the global loads of step t+1;
-//   for each k-group but the last: read the next group's fragments from
-//     LDS, then issue this group's MFMAs;
-//   write step t+1's registers to the other buffer; barrier;
-//   read the first fragments of step t+1, then issue the last group's MFMAs
-//     of step t, whose registers were read before the barrier -- so the LDS
-//     latency after the barrier is covered by matrix-core work.
+// is used once, and the fragment of a lane is 4 k's of one row or column,
+// read from a k-contiguous stage as a single 16-byte LDS read.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -73,36 +49,20 @@ struct IntC {
     static constexpr int value = V;
 };
 
-template <int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+template <int BM, int BN, int BK, int WGM, int WGN>
 struct MfmaCfg {
-    static constexpr int T = 64 * WGM * WGN;
     static constexpr int WM = BM / WGM;
     static constexpr int WN = BN / WGN;
     static constexpr int MB = WM / 32;
     static constexpr int NB = WN / 32;
-    static constexpr int LDA_S = BK;
-    static constexpr int LDB_S = BN + 8;
     static constexpr int KG = BK / 8;           // k-groups of 8 per K-step
-    static constexpr int A_STAGE = BM * LDA_S;
-    static constexpr int B_STAGE = BK * LDB_S;
-    static constexpr int STAGE = A_STAGE + B_STAGE;
-    // elements per thread per K-step
-    static constexpr int A_PER = BM * BK / T;
-    static constexpr int B_PER = BK * BN / T;
-    // 16-byte vectors per thread per K-step
-    static constexpr int A_V = A_PER / 4;
-    static constexpr int B_V = B_PER / 4;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(BK == 16 || BK == 32, "A-tile swizzle is defined for BK = 16 and 32");
-    static_assert(A_PER * T == BM * BK && B_PER * T == BK * BN, "loader must cover the tile");
-    static_assert(!VEC || (A_V * 4 == A_PER && B_V * 4 == B_PER), "vector loader must cover the tile");
-    static_assert(T % (BK / 4) == 0 && T % (BN / 4) == 0, "vector loader rows");
-    static_assert(T % BK == 0 && T % BN == 0, "scalar loader rows");
-    static_assert(2 * STAGE * 4 <= 160 * 1024, "LDS budget");
+    static_assert(BK == 16 || BK == 32, "the chunk swizzle is defined for BK = 16 and 32");
     static_assert(KG % 2 == 0, "the fragment sets alternate within a K-step");
 };
 
-// Chunk-position swizzle of A-tile row r (BK/4 chunks of 16 bytes per row).
+// Chunk-position swizzle of row r of a k-contiguous stage (BK/4 chunks of
+// 16 bytes per row): logical chunk c is stored at chunk c ^ swz(r).
 template <int BK>
 __device__ __forceinline__ int a_swizzle(int r) {
     if constexpr (BK == 16) return ((r >> 1) ^ (r >> 3)) & 3;
@@ -111,37 +71,24 @@ __device__ __forceinline__ int a_swizzle(int r) {
 
 // Scheduling hints for one K-loop iteration of KG groups of NM MFMAs each:
 // in every group one LDS read (the next group's fragments, NR of them) is
-// placed after each of the first MFMAs; the next MFMA slots of the first
-// group take the NV global loads of the next K-step, and the last NV slots
-// of the last group its NV LDS writes.  __builtin_amdgcn_sched_group_barrier needs
-// constant arguments, hence the recursion over template parameters.
-constexpr int kMaskMfma = 0x008, kMaskVmemRead = 0x020, kMaskDsRead = 0x100, kMaskDsWrite = 0x200;
+// placed after each of the first MFMAs.  __builtin_amdgcn_sched_group_barrier
+// needs constant arguments, hence the recursion over template parameters.
+constexpr int kMaskMfma = 0x008, kMaskDsRead = 0x100;
 
-template <int I, int NM, int NR, int NV, int EXTRA_MASK, int TAIL>
+template <int I, int NM, int NR>
 __device__ __forceinline__ void interleave_group() {
     if constexpr (I < NM) {
         __builtin_amdgcn_sched_group_barrier(kMaskMfma, 1, 0);
-        if constexpr (I < NR) {
-            __builtin_amdgcn_sched_group_barrier(kMaskDsRead, 1, 0);
-        } else if constexpr (EXTRA_MASK == kMaskVmemRead) {
-            if constexpr (I - NR < NV) __builtin_amdgcn_sched_group_barrier(EXTRA_MASK, 1, 0);
-        } else if constexpr (EXTRA_MASK == kMaskDsWrite) {
-            // LDS writes late in the group, far from the loads they wait for,
-            // with TAIL MFMAs left after them to cover the writes' latency
-            // before the barrier
-            if constexpr (I >= NM - NV - TAIL && I < NM - TAIL)
-                __builtin_amdgcn_sched_group_barrier(EXTRA_MASK, 1, 0);
-        }
-        interleave_group<I + 1, NM, NR, NV, EXTRA_MASK, TAIL>();
+        if constexpr (I < NR) __builtin_amdgcn_sched_group_barrier(kMaskDsRead, 1, 0);
+        interleave_group<I + 1, NM, NR>();
     }
 }
 
-template <int NM, int NR, int NV, int KG, int TAIL, int G = 0>
+template <int NM, int NR, int KG, int G = 0>
 __device__ __forceinline__ void interleave_hints() {
     if constexpr (G < KG) {
-        constexpr int extra = G == 0 ? kMaskVmemRead : (G == KG - 1 ? kMaskDsWrite : 0);
-        interleave_group<0, NM, NR, NV, extra, TAIL>();
-        interleave_hints<NM, NR, NV, KG, TAIL, G + 1>();
+        interleave_group<0, NM, NR>();
+        interleave_hints<NM, NR, KG, G + 1>();
     }
 }
 
@@ -224,208 +171,22 @@ __device__ __forceinline__ void write_tile(const TileOut& o, const f32x16 (&acc)
     }
 }
 
-// One output tile (tm, tn) over k in [kb, ke): load, contract, write.  All
-// threads of the workgroup call it together; smem is the workgroup's LDS.
-template <int BM, int BN, int BK, int WGM, int WGN, bool VEC, int SCHED>
-__device__ __forceinline__ void mfma_tile(const GemmArgs& g, float* smem, int tm, int tn, int kb, int ke,
-                                          const TileOut& o) {
-    using P = MfmaCfg<BM, BN, BK, WGM, WGN, VEC>;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / WGN;
-    const int wn = wave % WGN;
-
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
-    const int steps = (ke - kb + BK - 1) / BK;
-
-    // ---- loader bookkeeping (constant over the K loop) ----
-    // VEC: vector r of A covers row q / (BK/4), columns 4 * (q % (BK/4)) .. +3, q = tid + r*T
-    //      vector r of B covers row q / (BN/4), columns 4 * (q % (BN/4)) .. +3
-    // scalar: element r of A is row q / BK, column q % BK; of B row q / BN, column q % BN
-    constexpr int AN = VEC ? P::A_V : P::A_PER;
-    constexpr int BNL = VEC ? P::B_V : P::B_PER;
-    constexpr int A_COLS = VEC ? BK / 4 : BK;     // loader slots per A row
-    constexpr int B_COLS = VEC ? BN / 4 : BN;     // loader slots per B row
-    constexpr int A_W = VEC ? 4 : 1;              // elements per slot
-
-    int64_t a_off[AN];
-    int a_kc[AN];          // column within the K-step
-    bool a_rok[AN];
-    int a_lds[AN];
-#pragma unroll
-    for (int r = 0; r < AN; ++r) {
-        const int q = tid + r * P::T;
-        const int row = q / A_COLS;
-        const int col = (q % A_COLS) * A_W;
-        const int gm = m0 + row;
-        a_rok[r] = gm < g.M;
-        a_off[r] = (int64_t)(a_rok[r] ? gm : 0) * g.lda + col;
-        a_kc[r] = col;
-        a_lds[r] = row * P::LDA_S + 4 * ((col >> 2) ^ a_swizzle<BK>(row)) + (col & 3);
-    }
-    int64_t b_off[BNL];
-    int b_kr[BNL];         // row within the K-step
-    bool b_cok[BNL];
-    int b_lds[BNL];
-#pragma unroll
-    for (int r = 0; r < BNL; ++r) {
-        const int q = tid + r * P::T;
-        const int row = q / B_COLS;
-        const int col = (q % B_COLS) * A_W;
-        const int gn = n0 + col;
-        b_cok[r] = gn < g.N;
-        b_off[r] = (int64_t)row * g.ldb + (b_cok[r] ? gn : 0);
-        b_kr[r] = row;
-        b_lds[r] = P::A_STAGE + row * P::LDB_S + col;
-    }
-
-    f32x4 va[VEC ? AN : 1], vb[VEC ? BNL : 1];
-    float sa[VEC ? 1 : AN], sb[VEC ? 1 : BNL];
-
-    // Masked-off elements load from kZeroMfma, so the loaded registers are
-    // final and nothing waits on them before they are written to LDS.
-    // The K-step's base addresses are uniform (scalar) and every per-lane
-    // address is a plain select, so the loads never sit behind a branch.
-    auto load = [&](int k0) {
-        const float* abase = g.A + k0;
-        const float* bbase = g.B + (int64_t)k0 * g.ldb;
-#pragma unroll
-        for (int r = 0; r < AN; ++r) {
-            const bool ok = a_rok[r] && (k0 + a_kc[r] < ke);
-            const float* p = ok ? abase + a_off[r] : kZeroMfma;
-            if constexpr (VEC) va[r] = *reinterpret_cast<const f32x4*>(p);
-            else sa[r] = *p;
-        }
-#pragma unroll
-        for (int r = 0; r < BNL; ++r) {
-            const bool ok = b_cok[r] && (k0 + b_kr[r] < ke);
-            const float* p = ok ? bbase + b_off[r] : kZeroMfma;
-            if constexpr (VEC) vb[r] = *reinterpret_cast<const f32x4*>(p);
-            else sb[r] = *p;
-        }
-    };
-    auto store = [&](int buf) {
-        float* s = smem + buf * P::STAGE;
-#pragma unroll
-        for (int r = 0; r < AN; ++r) {
-            if constexpr (VEC) *reinterpret_cast<f32x4*>(s + a_lds[r]) = va[r];
-            else s[a_lds[r]] = sa[r];
-        }
-#pragma unroll
-        for (int r = 0; r < BNL; ++r) {
-            if constexpr (VEC) *reinterpret_cast<f32x4*>(s + b_lds[r]) = vb[r];
-            else s[b_lds[r]] = sb[r];
-        }
-    };
-
-    f32x16 acc[P::MB][P::NB];
-#pragma unroll
-    for (int mb = 0; mb < P::MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < P::NB; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
-
-    const int l32 = lane & 31;
-    const int lh = lane >> 5;
-    // fragment offsets within a stage (floats).  A: row wm*WM + mb*32 + l32,
-    // logical chunk 2*kg + lh, stored at chunk (2*kg + lh) ^ swz(row).
-    int a_frag[P::KG][P::MB];
-#pragma unroll
-    for (int mb = 0; mb < P::MB; ++mb) {
-        const int row = wm * P::WM + mb * 32 + l32;
-        const int sw = a_swizzle<BK>(row);
-#pragma unroll
-        for (int kg = 0; kg < P::KG; ++kg) a_frag[kg][mb] = row * P::LDA_S + 4 * ((2 * kg + lh) ^ sw);
-    }
-    const int b_frag = P::A_STAGE + (4 * lh) * P::LDB_S + wn * P::WN + l32;
-
-    // two fragment sets: group kg's operands live in set kg & 1
-    f32x4 fa[2][P::MB];
-    float fb[2][P::NB][4];
-    auto read_frags = [&](int buf, int kg, int set) {
-        const float* s = smem + buf * P::STAGE;
-#pragma unroll
-        for (int mb = 0; mb < P::MB; ++mb)
-            fa[set][mb] = *reinterpret_cast<const f32x4*>(s + a_frag[kg][mb]);
-#pragma unroll
-        for (int nb = 0; nb < P::NB; ++nb)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) fb[set][nb][q] = s[b_frag + (8 * kg + q) * P::LDB_S + nb * 32];
-    };
-    auto mfmas = [&](int set) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int mb = 0; mb < P::MB; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < P::NB; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[set][mb][q], fb[set][nb][q],
-                                                                       acc[mb][nb], 0, 0, 0);
-    };
-
-    // The K loop is rotated so that its body is one basic block that starts
-    // at a barrier: nothing in it is conditional (a load past the end of the
-    // slice reads the zero block, and the last stage write lands in a buffer
-    // nobody reads), which lets the scheduler interleave the memory
-    // instructions with the MFMAs.  Iteration s (1 <= s < steps):
-    //   barrier; read group 0 of step s; MFMAs of the last group of step s-1;
-    //   load step s+1; groups 0..KG-2 of step s (each reading the next
-    //   group's fragments first); write step s+1 to the other buffer.
-    if (steps > 0) {
-        load(kb);
-        store(0);
-        __syncthreads();
-        read_frags(0, 0, 0);
-        load(kb + BK);
-#pragma unroll
-        for (int kg = 0; kg + 1 < P::KG; ++kg) {
-            read_frags(0, kg + 1, (kg + 1) & 1);
-            mfmas(kg & 1);
-        }
-        store(1);
-        for (int s = 1; s < steps; ++s) {
-            const int cur = s & 1;
-            __syncthreads();
-            read_frags(cur, 0, 0);          // KG is even: group 0 goes to set 0 ...
-            mfmas(1);                        // ... while step s-1's last group (set 1) runs
-            load(kb + (s + 1) * BK);
-#pragma unroll
-            for (int kg = 0; kg + 1 < P::KG; ++kg) {
-                read_frags(cur, kg + 1, (kg + 1) & 1);
-                mfmas(kg & 1);
-            }
-            store(cur ^ 1);
-            // SCHED = 1 + (MFMAs left after the LDS writes) / 8
-            if constexpr (SCHED) interleave_hints<P::MB * P::NB * 4, P::MB + 2 * P::NB, AN + BNL, P::KG, 8 * (SCHED - 1)>();
-        }
-        mfmas(1);                            // last group of the last step
-    }
-
-    // ---- epilogue: overwrite the destination (masked at its edges) ----
-    write_tile<P::MB, P::NB, P::WM, P::WN>(o, acc, wm, wn, l32, lh);
-}
-
-
 // ---------------------------------------------------------------------------
-// Direct-to-LDS variant of one output tile.
+// One output tile, loaded direct-to-LDS.
 //
 // gfx950's global_load_lds_dwordx4 moves 16 bytes per lane from global
 // memory straight into LDS: lane l of a wave lands at (wave-uniform base) +
 // 16 * l, so one instruction fills 1 KB of LDS in lane order while the
 // source address of each lane is free.  global_load_lds_dword does the same
 // with 4 bytes per lane (256 B per instruction); it serves operands whose
-// rows are not 16-byte aligned and builds exactly the same stage layout.  That removes the staging registers
-// and the LDS write instructions of the register-staged pipeline (the
-// direct global -> shared copy that "GEMM from naive to tiled" section 六.2
+// rows are not 16-byte aligned and builds exactly the same stage layout.
+// There are no staging registers and no LDS write instructions (the direct
+// global -> shared copy that "GEMM from naive to tiled" section 六.2
 // describes for cp.async, and the register-free prefetch of "SGEMM 纯 CUDA
-// 优化总结" Q10), and lets DS stages of LDS be in flight at once:
+// 优化总结" Q10), and DS stages of LDS can be in flight at once:
 //   * A stage [BM][BK]: an instruction fills whole rows, and the lane that
 //     lands in physical 4-float chunk c of row r fetches logical chunk
-//     c ^ swz(r), so the swizzled layout of the register-staged path is
-//     produced as is;
+//     c ^ swz(r), so the stage holds the swizzled layout;
 //   * B stage: blocks of R = 256 / BN whole rows (1 KB, one 16-byte-lane
 //     instruction or four 4-byte-lane ones), GS floats apart, GS chosen so
 //     that the fragment reads of rows k and k + 4 (the two lane halves) fall
@@ -493,13 +254,9 @@ template <bool TB, int BN, int BK, int W>
 using BLayout = std::conditional_t<TB, KcLayout<BN, BK, W>, KmLayout<BN, BK, W>>;
 
 // Floats per stage of the direct-to-LDS layout: A region, then B region (the
-// same for both lane widths; only instantiated when used).
-template <bool ON, int OPS, int BM, int BN, int BK>
-struct DtlStageFloats {
-    static constexpr int value = 4;
-};
+// same for both lane widths).
 template <int OPS, int BM, int BN, int BK>
-struct DtlStageFloats<true, OPS, BM, BN, BK> {
+struct DtlStageFloats {
     static constexpr int value = ALayout<(OPS & 1) != 0, BM, BK, 4>::FLOATS + BLayout<(OPS & 2) != 0, BN, BK, 4>::FLOATS;
 };
 
@@ -575,11 +332,11 @@ __device__ __forceinline__ void dma_lanes(const float* src, const float* lds) {
         asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(base));
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int SCHED, int DS, int W, int OPS, bool PRIO>
+template <int BM, int BN, int BK, int WGM, int WGN, int DS, int W, int OPS, bool PRIO>
 __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, float* st1, float* st2, float* st3,
                                               int tm, int tn, int kb, int ke, const TileOut& o) {
     float* const stg[4] = {st0, st1, st2, st3};
-    using P = MfmaCfg<BM, BN, BK, WGM, WGN, true>;
+    using P = MfmaCfg<BM, BN, BK, WGM, WGN>;
     using LA = ALayout<(OPS & 1) != 0, BM, BK, W>;
     using LB = BLayout<(OPS & 2) != 0, BN, BK, W>;
     // a k-major B with four column blocks per wave reads the four blocks'
@@ -728,8 +485,7 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
                 mfmas(kg & 1);
             }
             if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
-            if constexpr (SCHED)
-                interleave_hints<P::MB * P::NB * 4, P::MB + 2 * P::NB, 0, P::KG, 8 * (SCHED - 1)>();
+            interleave_hints<P::MB * P::NB * 4, P::MB + 2 * P::NB, P::KG>();
         };
         // Unrolled by DS so that every iteration names its stages statically.
         // The first loop runs whole trips of iterations whose refill step lies
@@ -782,24 +538,21 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
 //    and the stream-K fix-up kernel sums the slots of each tile in range
 //    order.  The cut depends only on the shapes, so the sums always happen in
 //    the same order (the work-splitting of "GEMM from naive to tiled", 十.1).
-template <int BM, int BN, int BK, int WGM, int WGN, bool VEC, int WPE, int SCHED, int DS, int OPS, bool PRIO>
+template <int BM, int BN, int BK, int WGM, int WGN, bool VEC, int WPE, int DS, int OPS, bool PRIO>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void mfma_gemm_kernel(GemmArgs g) {
-    using P = MfmaCfg<BM, BN, BK, WGM, WGN, VEC>;
-    static_assert(DS > 0 || OPS == 0, "operands stored transposed need the direct-to-LDS loader");
-    // LDS: two stages for the register-staged loader, or DSE separate stage
-    // arrays for the direct-to-LDS loader (16-byte lanes when the operands
-    // are 16-byte aligned, else 4-byte lanes, which keep three stages so
+    // LDS: DSE separate stage arrays (16-byte lanes when the operands are
+    // 16-byte aligned, else 4-byte lanes, which keep at most three stages so
     // that the loads in flight fit the vmcnt counter)
-    constexpr bool DTL = DS > 0;
+    static_assert(DS >= 2 && DS <= 4, "two to four stages");
     constexpr int DSE = VEC || DS < 3 ? DS : 3;
     constexpr int W = VEC ? 4 : 1;
-    constexpr int QS = DtlStageFloats<DTL, OPS, BM, BN, BK>::value;
-    __shared__ __attribute__((aligned(16))) float lds0[DTL ? QS : 2 * P::STAGE];
-    __shared__ __attribute__((aligned(16))) float lds1[DTL ? QS : 4];
-    __shared__ __attribute__((aligned(16))) float lds2[DTL && DSE > 2 ? QS : 4];
-    __shared__ __attribute__((aligned(16))) float lds3[DTL && DSE > 3 ? QS : 4];
+    constexpr int QS = DtlStageFloats<OPS, BM, BN, BK>::value;
+    __shared__ __attribute__((aligned(16))) float lds0[QS];
+    __shared__ __attribute__((aligned(16))) float lds1[QS];
+    __shared__ __attribute__((aligned(16))) float lds2[DSE > 2 ? QS : 4];
+    __shared__ __attribute__((aligned(16))) float lds3[DSE > 3 ? QS : 4];
     // One call site for every work item, so that a single copy of the tile
     // code serves all decompositions: (tile, slice) in the one-tile mode;
     // the data-parallel tiles, then the K-step ranges, in stream-K mode.
@@ -855,79 +608,58 @@ void mfma_gemm_kernel(GemmArgs g) {
         }
         if (!first) __syncthreads();                             // the next tile's prologue overwrites LDS
         first = false;
-        if constexpr (DTL)
-            mfma_tile_dtl<BM, BN, BK, WGM, WGN, SCHED, DSE, W, OPS, PRIO>(g, lds0, lds1, lds2, lds3, tm, tn, kb, ke, o);
-        else mfma_tile<BM, BN, BK, WGM, WGN, VEC, SCHED>(g, lds0, tm, tn, kb, ke, o);
+        mfma_tile_dtl<BM, BN, BK, WGM, WGN, DSE, W, OPS, PRIO>(g, lds0, lds1, lds2, lds3, tm, tn, kb, ke, o);
         it += step;
     }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int WPE, int SCHED, int DS, int OPS, bool PRIO>
+template <int BM, int BN, int BK, int WGM, int WGN, int WPE, int DS, bool NARROW, bool PRIO, int OPS>
 hipError_t launch_ops(bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
     dim3 grid(g.sk_iters > 0 ? (unsigned)g.sk_grid : (unsigned)((int64_t)g.tiles_m * g.tiles_n), 1,
               g.sk_iters > 0 ? 1u : (unsigned)splits);
     dim3 block(64 * WGM * WGN);
-    if (vec)
-        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, true, WPE, SCHED, DS, OPS, PRIO>), grid, block, 0,
-                           stream, g);
-    else
-        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, false, WPE, SCHED, DS, OPS, PRIO>), grid, block, 0,
-                           stream, g);
+    if (vec) {
+        hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, true, WPE, DS, OPS, PRIO>), grid, block, 0, stream,
+                           g);
+    } else {
+        if constexpr (!NARROW) return hipErrorInvalidValue;   // not built with 4-byte lanes
+        else
+            hipLaunchKernelGGL((mfma_gemm_kernel<BM, BN, BK, WGM, WGN, false, WPE, DS, OPS, PRIO>), grid, block, 0,
+                               stream, g);
+    }
     return hipGetLastError();
 }
 
-// ops: bit 0 = A stored transposed, bit 1 = B stored transposed; only the
-// tiles whose table entry says so are instantiated for the transposed layouts.
-template <int BM, int BN, int BK, int WGM, int WGN, int WPE, int SCHED, int DS, bool TRANS, bool PRIO>
+// ops: bit 0 = A stored transposed, bit 1 = B stored transposed.
+template <int BM, int BN, int BK, int WGM, int WGN, int WPE, int DS, bool NARROW, bool PRIO>
 hipError_t launch_one(bool vec, int ops, const GemmArgs& g, int splits, hipStream_t stream) {
-    if constexpr (TRANS) {
-        switch (ops) {
-            case 0: return launch_ops<BM, BN, BK, WGM, WGN, WPE, SCHED, DS, 0, PRIO>(vec, g, splits, stream);
-            case 1: return launch_ops<BM, BN, BK, WGM, WGN, WPE, SCHED, DS, 1, PRIO>(vec, g, splits, stream);
-            case 2: return launch_ops<BM, BN, BK, WGM, WGN, WPE, SCHED, DS, 2, PRIO>(vec, g, splits, stream);
-            case 3: return launch_ops<BM, BN, BK, WGM, WGN, WPE, SCHED, DS, 3, PRIO>(vec, g, splits, stream);
-            default: return hipErrorInvalidValue;
-        }
-    } else {
-        if (ops != 0) return hipErrorInvalidValue;
-        return launch_ops<BM, BN, BK, WGM, WGN, WPE, SCHED, DS, 0, PRIO>(vec, g, splits, stream);
+    switch (ops) {
+        case 0: return launch_ops<BM, BN, BK, WGM, WGN, WPE, DS, NARROW, PRIO, 0>(vec, g, splits, stream);
+        case 1: return launch_ops<BM, BN, BK, WGM, WGN, WPE, DS, NARROW, PRIO, 1>(vec, g, splits, stream);
+        case 2: return launch_ops<BM, BN, BK, WGM, WGN, WPE, DS, NARROW, PRIO, 2>(vec, g, splits, stream);
+        case 3: return launch_ops<BM, BN, BK, WGM, WGN, WPE, DS, NARROW, PRIO, 3>(vec, g, splits, stream);
+        default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
 hipError_t launch_mfma(int tile, bool vec, int ops, const GemmArgs& g, int splits, hipStream_t stream) {
-#define SGEMM_MFMA_CASE(ID)                                                                     \
-    case ID:                                                                                    \
-        return launch_one<kMfmaTiles[ID].bm, kMfmaTiles[ID].bn, kMfmaTiles[ID].bk,             \
-                          kMfmaTiles[ID].waves_m, kMfmaTiles[ID].waves_n,                      \
-                          kMfmaTiles[ID].waves_per_simd, kMfmaTiles[ID].sched, kMfmaTiles[ID].dtl, \
-                          kMfmaTiles[ID].trans, kMfmaTiles[ID].prio>(vec, ops, g, splits, stream);
+#define SGEMM_MFMA_CASE(ID)                                                                          \
+    case ID:                                                                                         \
+        return launch_one<kMfmaTiles[ID].bm, kMfmaTiles[ID].bn, kMfmaTiles[ID].bk, kMfmaTiles[ID].waves_m, \
+                          kMfmaTiles[ID].waves_n, kMfmaTiles[ID].waves_per_simd, kMfmaTiles[ID].stages,      \
+                          kMfmaTiles[ID].narrow, kMfmaTiles[ID].prio>(vec, ops, g, splits, stream);
     switch (tile) {
         SGEMM_MFMA_CASE(0)
         SGEMM_MFMA_CASE(1)
         SGEMM_MFMA_CASE(2)
         SGEMM_MFMA_CASE(3)
-        SGEMM_MFMA_CASE(4)
-        SGEMM_MFMA_CASE(5)
-        SGEMM_MFMA_CASE(6)
-        SGEMM_MFMA_CASE(7)
-        SGEMM_MFMA_CASE(8)
-        SGEMM_MFMA_CASE(9)
-        SGEMM_MFMA_CASE(10)
-        SGEMM_MFMA_CASE(11)
-        SGEMM_MFMA_CASE(12)
-        SGEMM_MFMA_CASE(13)
-        SGEMM_MFMA_CASE(14)
-        SGEMM_MFMA_CASE(15)
-        SGEMM_MFMA_CASE(16)
-        SGEMM_MFMA_CASE(17)
-        SGEMM_MFMA_CASE(18)
         default:
             return hipErrorInvalidValue;
     }
 #undef SGEMM_MFMA_CASE
 }
-static_assert(kNumMfmaTiles == 19, "launch_mfma covers every MFMA tile");
+static_assert(kNumMfmaTiles == 4, "launch_mfma covers every MFMA tile");
 
 }  // namespace sgemm_impl

@@ -7,7 +7,7 @@
 // is therefore built to stream B with deep memory-level parallelism and no
 // LDS staging:
 //   * a wave owns 64 columns of C and a quarter of the workgroup's K range;
-//     a workgroup (4 or 8 waves) owns a 64-column strip and one K slice, whose
+//     a workgroup (4 waves) owns a 64-column strip and one K slice, whose
 //     partial sums across workgroups the split-K reduction adds, or (stream-K)
 //     an equal share of all (strip, K-step) units, partial strips being added
 //     by the stream-K fix-up;
@@ -256,10 +256,9 @@ hipError_t launch_skinny(int tile, bool vec, const GemmArgs& g, int splits, hipS
     switch (tile) {
         case 0: return launch_waves<kSkinnyTiles[0].waves_n, kSkinnyTiles[0].bm / 16>(vec, g, splits, stream);
         case 1: return launch_waves<kSkinnyTiles[1].waves_n, kSkinnyTiles[1].bm / 16>(vec, g, splits, stream);
-        case 2: return launch_waves<kSkinnyTiles[2].waves_n, kSkinnyTiles[2].bm / 16>(vec, g, splits, stream);
         default: return hipErrorInvalidValue;
     }
 }
-static_assert(kNumSkinnyTiles == 3, "launch_skinny covers every skinny tile");
+static_assert(kNumSkinnyTiles == 2, "launch_skinny covers every skinny tile");
 
 }  // namespace sgemm_impl

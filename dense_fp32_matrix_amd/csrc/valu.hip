@@ -214,12 +214,10 @@ hipError_t launch_valu(int tile, bool vec, const GemmArgs& g, int splits, hipStr
     switch (tile) {
         case 0:
             return launch_one<kValuTiles[0].bm, kValuTiles[0].bn, kValuTiles[0].bk>(vec, g, splits, stream);
-        case 1:
-            return launch_one<kValuTiles[1].bm, kValuTiles[1].bn, kValuTiles[1].bk>(vec, g, splits, stream);
         default:
             return hipErrorInvalidValue;
     }
 }
-static_assert(kNumValuTiles == 2, "launch_valu covers every VALU tile");
+static_assert(kNumValuTiles == 1, "launch_valu covers every VALU tile");
 
 }  // namespace sgemm_impl

@@ -67,7 +67,7 @@ typedef enum sgemm_status {
 
 /*
  * C = A.B (see the file comment).
- *   M, N, K : sizes, each >= 0 and < 2^31.
+ *   M, N, K : sizes, each >= 0 and < 2^30 (larger sizes: SGEMM_ERR_UNSUPPORTED).
  *   A, lda  : M x K, lda >= max(1, K).   May be NULL when M == 0 or K == 0.
  *   B, ldb  : K x N, ldb >= max(1, N).   May be NULL when K == 0 or N == 0.
  *   C, ldc  : M x N, ldc >= max(1, N).   May be NULL when M == 0 or N == 0.
@@ -94,7 +94,7 @@ typedef enum sgemm_decomposition {
     SGEMM_DECOMP_AUTO = 0,      /* per-shape choice */
     SGEMM_DECOMP_TILES = 1,     /* one output tile (and K slice) per workgroup */
     SGEMM_DECOMP_STREAM_K = 2   /* persistent workgroups share the tiles' K-steps evenly
-                                   (MFMA path; skinny path with tiles 0 and 2) */
+                                   (MFMA and skinny paths) */
 } sgemm_decomposition;
 
 /*
@@ -106,7 +106,11 @@ typedef enum sgemm_decomposition {
  *                   partial products are summed in slice order 0..S-1 by a second
  *                   kernel (one-tile-per-workgroup decomposition only).
  *   vector        : 0 = choose (16-byte loads when the operands allow them),
- *                   1 = force 4-byte loads.
+ *                   1 = force 4-byte loads.  The 256 x 256 matrix-core tiles are
+ *                   built for 16-byte loads only: forcing one of them with 4-byte
+ *                   loads, or on unaligned operands with pack = 1, is
+ *                   SGEMM_ERR_INVALID_ARG (with pack = 0 or 2 it runs on packed
+ *                   copies).
  *   decomposition : an sgemm_decomposition.
  *   pack          : operands whose rows are not 16-byte aligned (or K, N not multiples
  *                   of 4) can first be copied into zero-padded, aligned workspace

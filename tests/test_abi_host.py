@@ -95,22 +95,22 @@ def test_gemm_plans():
     operand's contiguous dimension."""
     M, N, K = 8192, 11008, 4096
     p = lib.gemm_plan_query("N", "T", M, N, K)                   # nn.Linear: X . W^T
-    assert p["path_name"] == "mfma" and p["tile"] in (8, 11, 17, 18) and p["vector"] == 1 and p["packed"] == 0
+    assert p["path_name"] == "mfma" and (p["bm"], p["bn"]) == (256, 256) and p["vector"] == 1 and p["packed"] == 0
     for ops in [("T", "N"), ("T", "T"), ("N", "T")]:
         q = lib.gemm_plan_query(*ops, 4096, 4096, 4096)
-        assert q["tile"] in (8, 11, 17, 18) and q["vector"] == 1
+        assert (q["bm"], q["bn"]) == (256, 256) and q["vector"] == 1
     # alpha == 0: C = beta * C only, A and B may be NULL
     q = lib.gemm_plan_query("N", "N", 64, 64, 64, alpha=0.0, A=0, B=0, beta=2.0)
     assert q["launches"] == 1 and q["workspace_bytes"] == 0
     # k-major operands (A stored K x M, B stored K x N) need no K padding for odd K
-    q = lib.gemm_plan_query("T", "N", 512, 512, 511, path="mfma", tile=11, split_k=1, decomposition="tiles")
+    q = lib.gemm_plan_query("T", "N", 512, 512, 511, path="mfma", tile=0, split_k=1, decomposition="tiles")
     assert q["vector"] == 1 and q["packed"] == 0 and q["k_padded"] == 511
     # odd K with a k-contiguous operand: pads K, packs both
-    q = lib.gemm_plan_query("N", "T", 512, 512, 511, path="mfma", tile=11, split_k=1, decomposition="tiles",
+    q = lib.gemm_plan_query("N", "T", 512, 512, 511, path="mfma", tile=0, split_k=1, decomposition="tiles",
                             pack="always")
     assert q["packed"] == 3 and q["k_padded"] == 512
-    # the paths that read row-major operands only, and tiles without transposed variants
-    for kw in ({"path": "valu"}, {"path": "skinny"}, {"path": "mfma", "tile": 3}):
+    # the paths that read row-major operands only
+    for kw in ({"path": "valu"}, {"path": "skinny"}):
         with pytest.raises(lib.SgemmError):
             lib.gemm_plan_query("N", "T", 16, 512, 512, **kw)
     assert lib.gemm_plan_query("T", "T", 300, 200, 20, path="naive")["path_name"] == "naive"
@@ -128,18 +128,38 @@ def test_bad_options_rejected():
     assert lib.sgemm_raw(*base, opts=lib._options(path="skinny")) == 1          # M > 32
     few = (20, 64, 64, A, 64, B, 64, C, 64)
     assert lib.sgemm_raw(*few, opts=lib._options(path="skinny", tile=0)) == 1   # tile 0 holds 16 rows
-    # skinny stream-K: the 64-deep K-step tiles only, and no split-K with it
+    # skinny stream-K: both tiles, and no split-K with it
     sk = (16, 64, 640)
-    assert lib.sgemm_plan_query(*sk, path="skinny", tile=0, decomposition="stream_k")["decomposition_name"] == \
-        "stream_k"
-    for kw in ({"tile": 1}, {"split_k": 2}):
-        with pytest.raises(lib.SgemmError):
-            lib.sgemm_plan_query(*sk, path="skinny", decomposition="stream_k", **kw)
+    for tile in (0, 1):
+        assert lib.sgemm_plan_query(*sk, path="skinny", tile=tile, decomposition="stream_k")["decomposition_name"] \
+            == "stream_k"
+    with pytest.raises(lib.SgemmError):
+        lib.sgemm_plan_query(*sk, path="skinny", decomposition="stream_k", split_k=2)
     with pytest.raises(lib.SgemmError):
         lib.sgemm_plan_query(*sk, path="valu", decomposition="stream_k")
     assert lib.sgemm_raw(*base, opts=lib._options(path="naive", split_k=2)) == 1
     assert lib.sgemm_raw(*base, opts=lib._options(workspace=A + 16, workspace_bytes=1 << 20)) == 1
     assert lib.sgemm_raw(*base, opts=lib._options(pack=-1)) == 1
+
+
+def test_wide_tiles_have_no_narrow_lanes():
+    """The 256 x 256 tiles are built for 16-byte lanes only: forcing them with
+    4-byte lanes, or on unaligned operands with packing off, is an invalid
+    argument; on unaligned operands with packing allowed they run on packed
+    copies; the 128 x 128 and 64 x 64 tiles take 4-byte lanes."""
+    for tile in (0, 1):
+        with pytest.raises(lib.SgemmError):
+            lib.sgemm_plan_query(512, 512, 512, path="mfma", tile=tile, vector=1)
+        with pytest.raises(lib.SgemmError):
+            lib.sgemm_plan_query(512, 509, 512, path="mfma", tile=tile, pack="never")
+        p = lib.sgemm_plan_query(512, 509, 512, path="mfma", tile=tile)
+        assert p["tile"] == tile and p["vector"] == 1 and p["packed"] == 2
+    for tile in (2, 3):
+        p = lib.sgemm_plan_query(512, 512, 512, path="mfma", tile=tile, vector=1)
+        assert p["tile"] == tile and p["vector"] == 0 and p["packed"] == 0
+    # unaligned operands with packing off: the planner picks a tile with 4-byte lanes
+    p = lib.sgemm_plan_query(4097, 3001, 2049, lda=2049, ldb=3001, ldc=3001, pack="never")
+    assert p["path_name"] == "mfma" and p["vector"] == 0 and p["tile"] in (2, 3)
 
 
 def test_empty_problems_plan_no_launch():
@@ -154,7 +174,7 @@ def test_empty_problems_plan_no_launch():
 
 def test_tile_tables():
     info = lib.sgemm_tile_info("mfma", 0)
-    assert info["count"] >= 5 and (info["bm"], info["bn"], info["bk"]) == (256, 128, 16)
+    assert info["count"] == 4 and (info["bm"], info["bn"], info["bk"]) == (256, 256, 16)
     for t in range(info["count"]):
         ti = lib.sgemm_tile_info("mfma", t)
         assert ti["bm"] % 32 == 0 and ti["bn"] % 32 == 0 and ti["bk"] % 8 == 0
@@ -194,7 +214,7 @@ def test_packing_plans():
     """Packed operands: which ones, K padded to a multiple of 4, the copies
     at the front of the workspace, one launch per packed operand."""
     M, N, K = 4097, 3001, 2049
-    p = lib.sgemm_plan_query(M, N, K, lda=K, ldb=N, ldc=N, path="mfma", tile=8, decomposition="tiles",
+    p = lib.sgemm_plan_query(M, N, K, lda=K, ldb=N, ldc=N, path="mfma", tile=0, decomposition="tiles",
                              split_k=1, pack="always")
     assert p["packed"] == 3 and p["vector"] == 1 and p["k_padded"] == 2052
     # copies with rows padded to 128 bytes: A 4097 x 2080, B 2052 x 3008
@@ -202,11 +222,11 @@ def test_packing_plans():
     assert p["workspace_bytes"] == r256(M * 2080 * 4) + r256(2052 * 3008 * 4)
     assert p["launches"] == 3
     # only B misaligned (N odd, K a multiple of 4): A is read in place
-    q = lib.sgemm_plan_query(512, 509, 512, path="mfma", tile=8, decomposition="tiles", split_k=1,
+    q = lib.sgemm_plan_query(512, 509, 512, path="mfma", tile=0, decomposition="tiles", split_k=1,
                              pack="always")
     assert q["packed"] == 2 and q["k_padded"] == 512 and q["workspace_bytes"] == 512 * 512 * 4
     # only A misaligned (odd lda)
-    q = lib.sgemm_plan_query(512, 512, 512, lda=513, path="mfma", tile=8, decomposition="tiles", split_k=1,
+    q = lib.sgemm_plan_query(512, 512, 512, lda=513, path="mfma", tile=0, decomposition="tiles", split_k=1,
                              pack="always")
     assert q["packed"] == 1 and q["workspace_bytes"] == 512 * 512 * 4 and q["launches"] == 2
     # aligned operands are never packed; other paths never pack
@@ -256,7 +276,7 @@ def test_forced_split_k_slices_cover_k():
 def test_stream_k_plans():
     """Stream-K on the 256 x 256 tile: all but the last full wave of tiles are
     data-parallel, the rest is cut into equal K-step ranges, one per CU."""
-    p = lib.sgemm_plan_query(8192, 11008, 4096, path="mfma", tile=3, decomposition="stream_k")
+    p = lib.sgemm_plan_query(8192, 11008, 4096, path="mfma", tile=0, decomposition="stream_k")
     tiles = p["tiles_m"] * p["tiles_n"]
     assert (p["tiles_m"], p["tiles_n"]) == (32, 43) and tiles == 1376
     assert p["decomposition_name"] == "stream_k" and p["workgroups"] == 256
@@ -265,7 +285,7 @@ def test_stream_k_plans():
     assert p["sk_units_per_wg"] == -(-p["sk_tiles"] * k_steps // 256)
     assert p["launches"] == 2 and p["workspace_bytes"] == 2 * 256 * 256 * 256 * 4
     # whole tiles per workgroup: no partial tiles, no fix-up
-    q = lib.sgemm_plan_query(4608, 4608, 32, path="mfma", tile=3, decomposition="stream_k")
+    q = lib.sgemm_plan_query(4608, 4608, 32, path="mfma", tile=0, decomposition="stream_k")
     assert q["sk_tiles"] == 324 and q["launches"] == 1 and q["workspace_bytes"] == 0 or \
         q["sk_units_per_wg"] % (32 // q["bk"]) != 0
     # stream-K is for the MFMA path without split-K
@@ -298,7 +318,7 @@ def test_plan_cache_keys():
     assert lib.sgemm_plan_query(M, N, K) == first
     # layouts and alpha == 0 (no matrix kernel: one scaling launch)
     t = lib.gemm_plan_query("T", "N", M, N, K)
-    assert t["path_name"] == "mfma" and t["tile"] in (8, 11, 13, 14, 15, 16, 17, 18)
+    assert t["path_name"] == "mfma" and 0 <= t["tile"] < lib.sgemm_tile_info("mfma", 0)["count"]
     z = lib.gemm_plan_query("N", "N", M, N, K, alpha=0.0, beta=2.0)
     assert z["launches"] == 1 and z["workspace_bytes"] == 0
     assert lib.gemm_plan_query("N", "N", M, N, K) == first
@@ -319,3 +339,29 @@ def test_skinny_stream_k_takes_ties_at_four_slices():
         p = lib.sgemm_plan_query(M, N, K)
         assert p["path_name"] == "skinny" and p["decomposition_name"] == "tiles", (M, N, K, p)
         assert p["split_k"] == split
+
+
+def test_binding_rejects_overlapping_rows():
+    """The binding passes a view's row stride as the leading dimension and
+    never widens it: broadcast views (stride 0) and as_strided views whose
+    rows overlap are refused before the C call; row- and column-major views
+    with padding give their stride."""
+    lay = lib._storage_layout
+    assert lay((4, 8), (8, 1), "A") == (0, 8)
+    assert lay((4, 8), (11, 1), "A") == (0, 11)              # padded rows
+    assert lay((1, 8), (0, 1), "A") == (0, 8)                # one row: any stride
+    assert lay((4, 1), (1, 1), "A") == (0, 1)                # one column
+    for shape, strides in [((4, 8), (0, 1)),                 # expand() of one row
+                           ((4, 8), (4, 1)),                 # as_strided rows sharing elements
+                           ((4, 1), (0, 1))]:                # broadcast column
+        with pytest.raises(ValueError):
+            lay(shape, strides, "A")
+    # column-major views: only where the operand may be transposed
+    assert lay((8, 4), (1, 8), "B", allow_column_major=True) == (1, 8)      # W.t() of an 4 x 8 W
+    assert lay((8, 4), (1, 9), "B", allow_column_major=True) == (1, 9)
+    with pytest.raises(ValueError):
+        lay((8, 4), (1, 4), "B", allow_column_major=True)                 # columns overlap
+    with pytest.raises(ValueError):
+        lay((8, 4), (1, 8), "C")                                          # C is row-major only
+    with pytest.raises(ValueError):
+        lay((8, 4), (2, 16), "B", allow_column_major=True)                # neither stride is 1

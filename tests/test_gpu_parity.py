@@ -80,8 +80,22 @@ SMALL_SHAPES = [
 
 
 def _mfma_tiles():
-    n = lib.sgemm_tile_info("mfma", 0)["count"]
-    return list(range(n))
+    return list(range(lib.sgemm_tile_info("mfma", 0)["count"]))
+
+
+def _narrow(tile):
+    """Whether a matrix-core tile is built with 4-byte load lanes."""
+    try:
+        lib.sgemm_plan_query(64, 64, 64, path="mfma", tile=tile, vector=1)
+        return True
+    except lib.SgemmError:
+        return False
+
+
+def _mfma_variants():
+    """(tile, vector) for every built instantiation: 16-byte lanes for all
+    tiles, 4-byte lanes (vector=1) for the narrow ones."""
+    return [(t, v) for t in _mfma_tiles() for v in (0, 1) if v == 0 or _narrow(t)]
 
 
 @pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -89,15 +103,14 @@ def test_naive(oracle_mod, shape):
     check_case(oracle_mod, *shape, "naive", path="naive")
 
 
-@pytest.mark.parametrize("tile", _mfma_tiles())
-@pytest.mark.parametrize("vector", [0, 1])
+@pytest.mark.parametrize("tile,vector", _mfma_variants())
 @pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_mfma_tiles(oracle_mod, shape, tile, vector):
     check_case(oracle_mod, *shape, f"mfma/{tile}/v{vector}", path="mfma", tile=tile, vector=vector, split_k=1,
                decomposition="tiles")
 
 
-@pytest.mark.parametrize("tile", [0, 1])
+@pytest.mark.parametrize("tile", [0])
 @pytest.mark.parametrize("vector", [0, 1])
 @pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_valu_tiles(oracle_mod, shape, tile, vector):
@@ -131,15 +144,14 @@ def test_skinny_stream_k(oracle_mod, shape, vector):
                vector=vector)
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2])
+@pytest.mark.parametrize("tile", [0, 1])
 def test_skinny_tiles(oracle_mod, tile):
     """Every skinny tile on the rows it holds (16, or 32 with two row blocks)."""
     M = lib.sgemm_tile_info("skinny", tile)["bm"]
     check_case(oracle_mod, M, 517, 2100, f"skinny tile {tile}", path="skinny", tile=tile, split_k=2)
 
 
-@pytest.mark.parametrize("path,tile", [("mfma", 0), ("mfma", 2), ("mfma", 4), ("mfma", 8), ("mfma", 13), ("mfma", 14),
-                                       ("mfma", 15), ("valu", 0)])
+@pytest.mark.parametrize("path,tile", [("mfma", 0), ("mfma", 1), ("mfma", 2), ("mfma", 3), ("valu", 0)])
 @pytest.mark.parametrize("split_k", [2, 5, 16])
 def test_split_k(oracle_mod, path, tile, split_k):
     check_case(oracle_mod, 200, 136, 2000, f"{path}/{tile}/split{split_k}", path=path, tile=tile,
@@ -155,12 +167,24 @@ STREAMK_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("tile", [3, 0, 2, 8, 10, 11, 12, 13, 14, 15, 16, 17, 18])
-@pytest.mark.parametrize("vector", [0, 1])
+@pytest.mark.parametrize("tile,vector", _mfma_variants())
 @pytest.mark.parametrize("shape", STREAMK_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_stream_k(oracle_mod, shape, tile, vector):
     check_case(oracle_mod, *shape, f"streamk/{tile}/v{vector}", path="mfma", tile=tile, vector=vector,
                decomposition="stream_k")
+
+
+@pytest.mark.parametrize("tile", _mfma_tiles())
+def test_stream_k_after_data_parallel_tiles(oracle_mod, tile):
+    """Stream-K where whole waves of tiles run data-parallel first (dp_tiles
+    > 0) and the remaining tiles' K-steps are shared out in ranges that cut
+    tiles (partial slots summed by the fix-up): the 8192 x 11008 x 4096
+    workload's default plan in miniature, checked element by element."""
+    M = N = 5888 if lib.sgemm_tile_info("mfma", tile)["bm"] == 256 else 2944
+    K = 160
+    plan = lib.sgemm_plan_query(M, N, K, path="mfma", tile=tile, decomposition="stream_k")
+    assert plan["dp_tiles"] > 0 and plan["sk_tiles"] > 0 and plan["launches"] == 2, plan
+    check_case(oracle_mod, M, N, K, f"streamk dp+sk tile {tile}", path="mfma", tile=tile, decomposition="stream_k")
 
 
 @pytest.mark.parametrize("shape", SMALL_SHAPES + [(64, 64, 8192), (20, 11008, 4096)],
@@ -186,12 +210,12 @@ def test_padded_leading_dimensions(oracle_mod, path):
     assert_bit_exact(Cbuf.numpy(), ref, what=f"{path} padded")
 
 
-@pytest.mark.parametrize("tile", [18, 17, 8, 11, 16, 15])
+@pytest.mark.parametrize("tile", _mfma_tiles())
 @pytest.mark.parametrize("gap", [4, 7], ids=["ldc16B", "ldcodd"])
 def test_epilogue_keeps_ldc_gap(oracle_mod, tile, gap):
-    """Each tile's epilogue (the 16-byte interleaved-column stores of tiles 8
-    and 17 included) writes exactly [0, M) x [0, N): the NaN gap of a padded
-    ldc survives, with N ragged against the tile and against 4 columns."""
+    """Each tile's epilogue (the 16-byte interleaved-column stores of the
+    256 x 256 tiles included) writes exactly [0, M) x [0, N): the NaN gap of a
+    padded ldc survives, with N ragged against the tile and against 4 columns."""
     M, N, K = 300, 270, 100
     ldc = N + gap
     say(f"ldc gap tile={tile} ldc={ldc}")
@@ -246,15 +270,19 @@ PACK_CASES = [
 ]
 
 
+@pytest.mark.parametrize("tile", _mfma_tiles())
 @pytest.mark.parametrize("decomposition", ["tiles", "stream_k"])
 @pytest.mark.parametrize("case", PACK_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"_lda{c[3]}_ldb{c[4]}")
-def test_packed_operands(oracle_mod, case, decomposition):
+def test_packed_operands(oracle_mod, case, decomposition, tile):
+    """Packed copies on every tile in both decompositions (the ragged
+    workload's default plan is packed operands on the 128 x 128 tile with
+    stream-K)."""
     M, N, K, lda, ldb, bits = case
-    plan = lib.sgemm_plan_query(M, N, K, lda=lda or K, ldb=ldb or N, path="mfma", tile=8, pack="always",
+    plan = lib.sgemm_plan_query(M, N, K, lda=lda or K, ldb=ldb or N, path="mfma", tile=tile, pack="always",
                                 decomposition=decomposition)
     assert plan["packed"] == bits and plan["vector"] == 1
     assert plan["k_padded"] == (K + 3) // 4 * 4
-    check_case(oracle_mod, M, N, K, f"packed/{decomposition}", lda=lda, ldb=ldb, path="mfma", tile=8,
+    check_case(oracle_mod, M, N, K, f"packed/{decomposition}/tile{tile}", lda=lda, ldb=ldb, path="mfma", tile=tile,
                pack="always", decomposition=decomposition)
 
 
@@ -268,8 +296,8 @@ def test_packed_matches_unpacked_bits():
     Kp, Np = 520, 304
     Ap = torch.zeros((M, Kp)); Ap[:, :K] = A
     Bp = torch.zeros((Kp, Np)); Bp[:K, :N] = B
-    C1 = run(A, B, path="mfma", tile=8, pack="always", decomposition="tiles")
-    C2 = run(Ap, Bp[:, :N], path="mfma", tile=8, decomposition="tiles")
+    C1 = run(A, B, path="mfma", tile=0, pack="always", decomposition="tiles")
+    C2 = run(Ap, Bp[:, :N], path="mfma", tile=0, decomposition="tiles")
     assert torch.equal(C1.cpu(), C2.cpu())
 
 
@@ -355,10 +383,10 @@ def test_library_workspace_reuse(oracle_mod):
     stream: growing requests, shrinking ones and two streams in turn, with
     nothing synchronised between the calls, each checked bit-exact."""
     cases = [((200, 136, 2000), {"path": "mfma", "tile": 2, "split_k": 4}),
-             ((600, 517, 700), {"path": "mfma", "tile": 11, "decomposition": "stream_k"}),
-             ((1000, 900, 3000), {"path": "mfma", "tile": 13, "split_k": 6, "decomposition": "tiles"}),
+             ((600, 517, 700), {"path": "mfma", "tile": 1, "decomposition": "stream_k"}),
+             ((1000, 900, 3000), {"path": "mfma", "tile": 2, "split_k": 6, "decomposition": "tiles"}),
              ((16, 700, 5000), {"path": "skinny", "split_k": 3}),
-             ((300, 260, 900), {"path": "mfma", "tile": 15, "decomposition": "stream_k"})]
+             ((300, 260, 900), {"path": "mfma", "tile": 3, "decomposition": "stream_k"})]
     side = torch.cuda.Stream()
     jobs = []
     for i, ((M, N, K), opts) in enumerate(cases * 2):
@@ -383,7 +411,7 @@ def test_workspace_on_many_streams(oracle_mod):
     calls on the further streams allocate their own; all run concurrently,
     unsynchronised, and every result is bit-exact."""
     M, N, K = 260, 300, 1500
-    opts = {"path": "mfma", "tile": 15, "split_k": 4, "decomposition": "tiles"}
+    opts = {"path": "mfma", "tile": 3, "split_k": 4, "decomposition": "tiles"}
     streams = [torch.cuda.Stream() for _ in range(11)]
     jobs = []
     for i, st in enumerate(streams):
@@ -405,27 +433,25 @@ def test_workspace_on_many_streams(oracle_mod):
 
 def test_large_workspace_allocated_per_call(oracle_mod):
     """A split-K workspace above the library's cached limit (1 GiB of slices
-    here) is allocated and freed with the call; checked on sampled entries,
+    here) is allocated and freed with the call; every element checked,
     twice in a row."""
     M, N, K = 4096, 4096, 8192
-    opts = {"path": "mfma", "tile": 17, "split_k": 16, "decomposition": "tiles"}
+    opts = {"path": "mfma", "tile": 1, "split_k": 16, "decomposition": "tiles"}
     assert lib.sgemm_plan_query(M, N, K, **opts)["workspace_bytes"] > (512 << 20)
     A, B = inputs(M, N, K, "integer", 70)
     Ad, Bd = to_dev(A), to_dev(B)
-    rows, cols = workloads.sample_indices(M, N, 512, seed=71)
-    ref = oracle_mod.round_to_f32(oracle_mod.sgemm_entries(A.numpy(), B.numpy(), rows, cols)[0])
+    ref = oracle_mod.round_to_f32(oracle_mod.sgemm(A.numpy(), B.numpy()))
     for r in range(2):
         say(f"large workspace call {r}")
         C = torch.full((M, N), float("nan"), device=DEV)
         lib.sgemm_ex(Ad, Bd, C, **opts)
         torch.cuda.synchronize()
-        got = C[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)].cpu().numpy()
-        assert_bit_exact(got, ref, what=f"large workspace call {r}")
+        assert_bit_exact(C.cpu().numpy(), ref, what=f"large workspace call {r}")
         del C
 
 
-@pytest.mark.parametrize("opts", [{"path": "mfma", "tile": 13, "split_k": 4, "decomposition": "tiles"},
-                                  {"path": "mfma", "tile": 15, "decomposition": "stream_k"}, {},
+@pytest.mark.parametrize("opts", [{"path": "mfma", "tile": 2, "split_k": 4, "decomposition": "tiles"},
+                                  {"path": "mfma", "tile": 3, "decomposition": "stream_k"}, {},
                                   {"path": "skinny", "decomposition": "stream_k"}],
                          ids=["split4", "streamk", "auto", "skinny-streamk"])
 def test_graph_capture_replays(oracle_mod, opts):
@@ -464,6 +490,9 @@ def test_graph_capture_replays(oracle_mod, opts):
 # --- the benchmark workloads at full size, in the benchmark's launch configuration ---------
 
 def _full_size_check(oracle_mod, w, kind, opts=None):
+    """The whole output against the whole oracle product, element by element:
+    within the normalized bound on floating-point inputs, bit-exact on
+    integer ones.  (AB)x = A(Bx) on two probe vectors is checked as well."""
     say(f"full size {w.name} inputs={kind} opts={opts}")
     A = workloads.with_ld(workloads.draw(w.M, w.K, kind, w.seed_base + 0, w.a_std if kind != "integer" else 1.0),
                           w.lda)
@@ -479,16 +508,16 @@ def _full_size_check(oracle_mod, w, kind, opts=None):
     del Ad, Bd
     Ch = C.cpu().numpy()
     del C
-    assert np.all(np.isfinite(Ch))
     An, Bn = A.numpy(), B.numpy()
-    rows, cols = workloads.sample_indices(w.M, w.N, 2048, seed=w.seed_base + 7)
-    cref, dref = oracle_mod.sgemm_entries(An, Bn, rows, cols)
-    got = Ch[rows, cols]
     if kind == "integer":
-        assert np.array_equal(got.astype(np.float64), cref), "sampled entries differ"
+        Cref = oracle_mod.sgemm(An, Bn)
+        assert_bit_exact(Ch, oracle_mod.round_to_f32(Cref), what=f"{w.name} integer, every element")
     else:
-        err = np.abs(got.astype(np.float64) - cref) / np.where(dref == 0, 1, dref)
-        assert err.max() <= 1e-5, f"sampled normalized error {err.max():.3e}"
+        Cref, D = oracle_mod.sgemm(An, Bn, with_denominator=True)
+        e = assert_within_bound(Ch, Cref, D, what=f"{w.name} {kind}, every element")
+        say(f"  max normalized error {e:.3e}")
+        del D
+    del Cref
     # (AB)x = A(Bx) over the whole output, for two vectors x
     g = np.random.default_rng(w.seed_base + 9)
     for t in range(2):

@@ -129,6 +129,35 @@ def test_associativity_float_bound(oracle_mod):
     assert np.all(np.abs(lhs - rhs) <= 1e-12 * scale)
 
 
+@pytest.mark.parametrize("M,K", [(1, 1), (7, 13), (64, 300)])
+def test_gemv_exact_integers(oracle_mod, M, K):
+    """oracle.gemv, plain and with absolute values, against exact int64
+    arithmetic: y = A x and |A| |x| (the error scale of the full-size
+    associativity check), on a row-padded A whose gap holds NaN."""
+    A = workloads.with_ld(workloads.draw(M, K, "integer", 41), K + 3).numpy()
+    x = workloads.draw(K, 1, "integer", 42).numpy()[:, 0].astype(np.int64)
+    Ai = np.asarray(A).astype(np.int64)
+    y = oracle_mod.gemv(A, x.astype(np.float64))
+    y_abs = oracle_mod.gemv(A, x.astype(np.float64), absolute=True)
+    assert np.array_equal(y, (Ai @ x).astype(np.float64))
+    assert np.array_equal(y_abs, (np.abs(Ai) @ np.abs(x)).astype(np.float64))
+
+
+def test_gemv_absolute_is_a_bound(oracle_mod):
+    """|A x| <= |A| |x| elementwise, with equality where A and x agree in sign;
+    a mixed-sign case tells the absolute form from the plain one, so a flag
+    that is ignored fails here."""
+    A = np.array([[1.0, -2.0, 3.0], [-1.0, -1.0, -1.0]], dtype=np.float32)
+    x = np.array([1.0, 1.0, -1.0])
+    assert np.array_equal(oracle_mod.gemv(A, x), np.array([-4.0, -1.0]))
+    assert np.array_equal(oracle_mod.gemv(A, x, absolute=True), np.array([6.0, 3.0]))
+    U = unif(40, 50, 43)
+    v = unif(50, 1, 44)[:, 0].astype(np.float64)
+    assert np.all(np.abs(oracle_mod.gemv(U, v)) <= oracle_mod.gemv(U, v, absolute=True))
+    P = np.abs(U)
+    assert np.array_equal(oracle_mod.gemv(P, np.abs(v)), oracle_mod.gemv(U, v, absolute=True))
+
+
 # --- closed forms -------------------------------------------------------------------
 
 @pytest.mark.parametrize("K", [1, 2, 255, 4096, 5792])

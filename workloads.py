@@ -26,7 +26,6 @@ import dataclasses
 import math
 from typing import Optional
 
-import numpy as np
 import torch
 
 
@@ -115,17 +114,3 @@ CONFIGS = {
         _make(5, "longk_512x512x65536", 512, 512, 65536, "uniform"),
     ]
 }
-
-
-def sample_indices(M: int, N: int, count: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
-    """Output positions to check on a large product: the four corners, the
-    last row and column, then uniform random positions."""
-    g = np.random.default_rng(seed)
-    fixed = [(0, 0), (0, N - 1), (M - 1, 0), (M - 1, N - 1)]
-    fixed += [(M - 1, j) for j in range(0, N, max(1, N // 16))]
-    fixed += [(i, N - 1) for i in range(0, M, max(1, M // 16))]
-    r = g.integers(0, M, size=max(0, count - len(fixed)))
-    c = g.integers(0, N, size=max(0, count - len(fixed)))
-    rows = np.concatenate([np.array([p[0] for p in fixed], dtype=np.int64), r.astype(np.int64)])
-    cols = np.concatenate([np.array([p[1] for p in fixed], dtype=np.int64), c.astype(np.int64)])
-    return rows, cols
