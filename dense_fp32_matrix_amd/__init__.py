@@ -16,7 +16,8 @@ from typing import Optional
 __all__ = [
     "SgemmError", "PATHS", "DECOMPOSITIONS", "PACK",
     "sgemm", "sgemm_ex", "sgemm_raw", "sgemm_plan_query", "sgemm_workspace_size",
-    "gemm", "gemm_raw", "gemm_plan_query", "gemm_workspace_size",
+    "gemm", "gemm_raw", "gemm_plan_query", "gemm_workspace_size", "gemm_noalloc", "gemm_noalloc_raw",
+    "NOALLOC_SCRATCH_BYTES",
     "sgemm_tile_info", "sgemm_status_string", "sgemm_version", "library_path", "load_library",
 ]
 
@@ -29,7 +30,8 @@ _PATH_NAMES = {v: k for k, v in PATHS.items()}
 
 SGEMM_OK = 0
 _STATUS = {0: "SGEMM_OK", 1: "SGEMM_ERR_INVALID_ARG", 2: "SGEMM_ERR_UNSUPPORTED", 3: "SGEMM_ERR_HIP",
-           4: "SGEMM_ERR_ALLOC"}
+           4: "SGEMM_ERR_ALLOC", 5: "SGEMM_ERR_SCRATCH_LIMIT"}
+NOALLOC_SCRATCH_BYTES = 128 << 20    # SGEMM_NOALLOC_SCRATCH_BYTES of the header
 
 
 class SgemmError(RuntimeError):
@@ -86,6 +88,8 @@ def load_library():
     lib.sgemm_gemm.restype = ctypes.c_int
     lib.sgemm_gemm_ex.argtypes = gm + [p, ctypes.POINTER(_Options)]
     lib.sgemm_gemm_ex.restype = ctypes.c_int
+    lib.sgemm_gemm_noalloc.argtypes = gm + [p, ctypes.POINTER(_Options)]
+    lib.sgemm_gemm_noalloc.restype = ctypes.c_int
     lib.sgemm_gemm_plan_query.argtypes = gm + [ctypes.POINTER(_Options), ctypes.POINTER(_Plan)]
     lib.sgemm_gemm_plan_query.restype = ctypes.c_int
     lib.sgemm_gemm_workspace_size.argtypes = [i32, i32] + [i64] * 6
@@ -263,6 +267,40 @@ def gemm(A, B, C=None, stream=None, *, trans_a=False, trans_b=False, alpha=1.0, 
                       _stream_handle(stream, A.device), opts)
     if st != SGEMM_OK:
         raise SgemmError(st, "sgemm_gemm")
+    return C
+
+
+def gemm_noalloc_raw(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0,
+                     opts: Optional[_Options] = None) -> int:
+    """sgemm_gemm_noalloc with integer device addresses; returns the status code."""
+    lib = load_library()
+    return lib.sgemm_gemm_noalloc(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                                  ctypes.byref(opts) if opts is not None else None)
+
+
+def gemm_noalloc(A, B, C, stream=None, *, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, **options):
+    """``gemm`` through sgemm_gemm_noalloc: the library allocates no device
+    memory for the call (its scratch is the static buffer of
+    NOALLOC_SCRATCH_BYTES); C must be given.  ``options`` are those of
+    ``sgemm_ex`` without a workspace."""
+    a_log = A.t() if trans_a else A
+    b_log = B.t() if trans_b else B
+    a, op_a, M, K, lda = _operand(a_log, "A")
+    b, op_b, K2, N, ldb = _operand(b_log, "B")
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: op(A) is {M}x{K}, op(B) is {K2}x{N}")
+    c, Mc, Nc, ldc = _matrix(C, "C")
+    if (Mc, Nc) != (M, N):
+        raise ValueError(f"C must be {M}x{N}, got {Mc}x{Nc}")
+    if not (A.device == B.device == C.device):
+        raise ValueError("A, B and C must be on the same device")
+    opts = _options(**options) if options else None
+    import torch
+    with torch.cuda.device(A.device):
+        st = gemm_noalloc_raw(op_a, op_b, M, N, K, float(alpha), a, lda, b, ldb, float(beta), c, ldc,
+                              _stream_handle(stream, A.device), opts)
+    if st != SGEMM_OK:
+        raise SgemmError(st, "sgemm_gemm_noalloc")
     return C
 
 

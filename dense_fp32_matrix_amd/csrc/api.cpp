@@ -205,6 +205,20 @@ Candidate streamk_candidate(int tile, bool vec, int64_t M, int64_t N, int64_t K)
     return c;
 }
 
+// Scratch bytes a decomposition needs for its partial products: the split-K
+// slices [S][M][round_up(N, 4)], or two BM x BN slots per persistent
+// workgroup when some stream-K range cuts a tile.
+size_t partials_bytes(const TileShape& t, int decomposition, int64_t splits, int64_t grid, int64_t sk_ipw,
+                      int64_t k_steps, int64_t M, int64_t N) {
+    if (decomposition == SGEMM_DECOMP_STREAM_K) {
+        const bool splits_tiles = sk_ipw % k_steps != 0 || sk_ipw < k_steps;
+        return splits_tiles ? (size_t)(2 * grid) * t.bm * t.bn * sizeof(float) : 0;
+    }
+    return splits > 1 ? (size_t)(splits * M * round_up(N, 4)) * sizeof(float) : 0;
+}
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
 // One call of the library-call form C = alpha * op(A) op(B) + beta * C.
 struct Call {
     bool ta = false, tb = false;      // A stored K x M / B stored N x K
@@ -264,7 +278,10 @@ void choose_split(int64_t tiles, int64_t K, int bk, int64_t target_wgs, int64_t 
 // k-contiguous and B k-major, or A k-major (NN, TN, TT: +0.3 to +1.4 %) and
 // the three-stage one (1) with both k-contiguous (NT: +1 %), so the
 // automatic choice takes each where it is faster.
-bool mfma_best(const sgemm_options& o, bool vec, int ops, int64_t M, int64_t N, int64_t K, Candidate* out) {
+// Candidates whose partial products need more than ws_cap bytes of scratch
+// are left out.
+bool mfma_best(const sgemm_options& o, bool vec, int ops, int64_t M, int64_t N, int64_t K, size_t ws_cap,
+               Candidate* out) {
     std::vector<int> cands;
     if (o.tile >= 0) cands.push_back(o.tile);
     else cands = {ops == 2 ? 1 : 0, 2, 3};
@@ -294,6 +311,9 @@ bool mfma_best(const sgemm_options& o, bool vec, int ops, int64_t M, int64_t N, 
         if (o.decomposition != SGEMM_DECOMP_TILES && o.split_k <= 1)
             cs.push_back(streamk_candidate(tile, vec, M, N, K));
         for (const Candidate& c : cs) {
+            if (partials_bytes(kMfmaTiles[c.tile], c.decomposition, c.splits, c.grid, c.sk_ipw, c.k_steps, M, N) >
+                ws_cap)
+                continue;
             if (!have || c.time < best.time) {
                 best = c;
                 have = true;
@@ -306,7 +326,9 @@ bool mfma_best(const sgemm_options& o, bool vec, int ops, int64_t M, int64_t N, 
 
 constexpr double kPackBw = 3e12;   // bytes/s read + written by the pack kernel
 
-sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* out) {
+// ws_cap: the most scratch the plan may use (the static buffer of
+// sgemm_gemm_noalloc; SIZE_MAX otherwise).
+sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t ws_cap, Plan* out) {
     sgemm_status st = validate(c);
     if (st != SGEMM_OK) return st;
     sgemm_options o{};
@@ -421,8 +443,9 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
     } else if (path == SGEMM_PATH_MFMA) {
         // With 4-byte lanes only the narrow tiles are built; a forced tile
         // without them can still run on packed copies.
-        const bool have = mfma_best(o, q.vector != 0, ops, M, N, K, &best);
-        if (!have && (o.vector == 1 || o.pack == 1)) return SGEMM_ERR_INVALID_ARG;
+        bool have = mfma_best(o, q.vector != 0, ops, M, N, K, ws_cap, &best);
+        const bool built = q.vector != 0 || o.tile < 0 || kMfmaTiles[o.tile].narrow;
+        if (!have && !built && (o.vector == 1 || o.pack == 1)) return SGEMM_ERR_INVALID_ARG;
         // Alternative: copy the misaligned operand(s), in their stored
         // orientation, into aligned, zero-padded workspace first and run the
         // 16-byte loaders.  A K that the KC layout would cut mid-chunk is
@@ -437,10 +460,13 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
             double bytes = 0;
             if (pack_a) bytes += 4.0 * (c.a_rows() * c.a_cols() + ar * ac);
             if (pack_b) bytes += 4.0 * (c.b_rows() * c.b_cols() + br * bc);
+            const size_t copies = (pack_a ? align256((size_t)(ar * round_up(ac, 32)) * sizeof(float)) : 0) +
+                                  (pack_b ? align256((size_t)(br * round_up(bc, 32)) * sizeof(float)) : 0);
             Candidate cand;
-            mfma_best(o, true, ops, M, N, kp, &cand);
+            const bool fits = copies <= ws_cap && mfma_best(o, true, ops, M, N, kp, ws_cap - copies, &cand);
             cand.time += bytes / kPackBw + (pack_a + pack_b) * kLaunch;
-            if (o.pack == 2 || !have || cand.time < best.time) {
+            if (fits && (o.pack == 2 || !have || cand.time < best.time)) {
+                have = true;
                 best = cand;
                 q.vector = 1;
                 q.packed = (pack_a ? 1 : 0) | (pack_b ? 2 : 0);
@@ -453,6 +479,9 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
                 p.b_ld = round_up(bc, 32);
             }
         }
+        // otherwise every plan was left out for its scratch (a plan of one
+        // tile per workgroup on unpacked operands needs none)
+        if (!have) return ws_cap == SIZE_MAX ? SGEMM_ERR_INVALID_ARG : SGEMM_ERR_SCRATCH_LIMIT;
     } else {   // VALU
         best.tile = o.tile < 0 ? 0 : o.tile;
         const TileShape& t = kValuTiles[best.tile];
@@ -491,9 +520,8 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
         q.sk_tiles = best.sk_tiles;
         q.sk_units_per_wg = best.sk_ipw;
         p.k_steps = best.k_steps;
-        const bool splits_tiles = best.sk_ipw % best.k_steps != 0 || best.sk_ipw < best.k_steps;
-        gemm_ws = splits_tiles ? (size_t)(2 * best.grid) * t.bm * t.bn * sizeof(float) : 0;
-        p.second = splits_tiles;
+        gemm_ws = partials_bytes(t, best.decomposition, 1, best.grid, best.sk_ipw, best.k_steps, M, N);
+        p.second = gemm_ws > 0;
     } else {
         if (best.splits > 65535) return SGEMM_ERR_UNSUPPORTED;
         q.split_k = (int32_t)best.splits;
@@ -501,12 +529,11 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
         q.workgroups = q.tiles_m * q.tiles_n * best.splits;
         if (best.splits > 1) {
             p.ldw = round_up(N, 4);
-            gemm_ws = (size_t)(best.splits * M * p.ldw * (int64_t)sizeof(float));
+            gemm_ws = partials_bytes(t, best.decomposition, best.splits, 0, 0, 0, M, N);
             p.second = true;
         }
     }
     // workspace: [packed A][packed B][partials], each 256-byte aligned
-    auto align256 = [](size_t b) { return (b + 255) / 256 * 256; };
     size_t off = 0;
     if (q.packed & 1) {
         p.pack_a_off = off;
@@ -518,6 +545,7 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, Plan* 
     }
     p.gemm_ws_off = off;
     q.workspace_bytes = gemm_ws > 0 ? off + gemm_ws : off;
+    if (q.workspace_bytes > ws_cap) return SGEMM_ERR_SCRATCH_LIMIT;
     q.launches = ((q.packed & 1) ? 1 : 0) + ((q.packed & 2) ? 1 : 0) + 1 + (p.second ? 1 : 0);
     *out = p;
     return SGEMM_OK;
@@ -532,16 +560,18 @@ struct PlanKey {
     int64_t M, N, K;
     int32_t flags;                 // ta | tb | reads_ab | A, B 16-byte aligned | lda, ldb % 4 == 0
     int32_t path, tile, split_k, vector, decomposition, pack;
+    size_t ws_cap;
     bool operator==(const PlanKey& o) const {
-        return std::tie(M, N, K, flags, path, tile, split_k, vector, decomposition, pack) ==
-               std::tie(o.M, o.N, o.K, o.flags, o.path, o.tile, o.split_k, o.vector, o.decomposition, o.pack);
+        return std::tie(M, N, K, flags, path, tile, split_k, vector, decomposition, pack, ws_cap) ==
+               std::tie(o.M, o.N, o.K, o.flags, o.path, o.tile, o.split_k, o.vector, o.decomposition, o.pack,
+                        o.ws_cap);
     }
 };
 struct PlanKeyHash {
     size_t operator()(const PlanKey& k) const {
         uint64_t h = 1469598103934665603ull;
         for (int64_t v : {k.M, k.N, k.K, (int64_t)k.flags, (int64_t)k.path, (int64_t)k.tile, (int64_t)k.split_k,
-                          (int64_t)k.vector, (int64_t)k.decomposition, (int64_t)k.pack})
+                          (int64_t)k.vector, (int64_t)k.decomposition, (int64_t)k.pack, (int64_t)k.ws_cap})
             h = (h ^ (uint64_t)v) * 1099511628211ull;
         return (size_t)h;
     }
@@ -550,7 +580,7 @@ constexpr size_t kPlanCacheMax = 4096;
 std::mutex g_plan_mu;
 std::unordered_map<PlanKey, Plan, PlanKeyHash> g_plans;
 
-sgemm_status make_plan(const Call& c, const sgemm_options* opts, Plan* out) {
+sgemm_status make_plan(const Call& c, const sgemm_options* opts, Plan* out, size_t ws_cap = SIZE_MAX) {
     const sgemm_status st = validate(c);
     if (st != SGEMM_OK) return st;
     if (opts != nullptr && opts->workspace != nullptr && !aligned(opts->workspace, 256)) return SGEMM_ERR_INVALID_ARG;
@@ -559,7 +589,7 @@ sgemm_status make_plan(const Call& c, const sgemm_options* opts, Plan* out) {
     const PlanKey key{c.M, c.N, c.K,
                       (c.ta ? 1 : 0) | (c.tb ? 2 : 0) | (c.reads_ab() ? 4 : 0) | (aligned(c.A, 16) ? 8 : 0) |
                           (aligned(c.B, 16) ? 16 : 0) | (c.lda % 4 == 0 ? 32 : 0) | (c.ldb % 4 == 0 ? 64 : 0),
-                      o.path, o.tile, o.split_k, o.vector, o.decomposition, o.pack};
+                      o.path, o.tile, o.split_k, o.vector, o.decomposition, o.pack, ws_cap};
     {
         std::lock_guard<std::mutex> lock(g_plan_mu);
         auto it = g_plans.find(key);
@@ -568,7 +598,7 @@ sgemm_status make_plan(const Call& c, const sgemm_options* opts, Plan* out) {
             return SGEMM_OK;
         }
     }
-    const sgemm_status s2 = make_plan_uncached(c, opts, out);
+    const sgemm_status s2 = make_plan_uncached(c, opts, ws_cap, out);
     if (s2 == SGEMM_OK) {
         std::lock_guard<std::mutex> lock(g_plan_mu);
         if (g_plans.size() >= kPlanCacheMax) g_plans.clear();
@@ -641,9 +671,12 @@ hipError_t cached_workspace(size_t bytes, hipStream_t stream, void** ws, std::un
     return hipSuccess;
 }
 
-sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_options* opts) {
+// static_ws: the no-allocation entry point's buffer of static_bytes; the
+// plan is then limited to it, and nothing is allocated.
+sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_options* opts, void* static_ws = nullptr,
+                 size_t static_bytes = 0) {
     Plan p;
-    sgemm_status st = make_plan(c, opts, &p);
+    sgemm_status st = make_plan(c, opts, &p, static_ws != nullptr ? static_bytes : SIZE_MAX);
     if (st != SGEMM_OK) return st;
     const sgemm_plan& q = p.pub;
     if (q.launches == 0) return SGEMM_OK;
@@ -657,7 +690,9 @@ sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_option
     bool owned = false;
     std::unique_lock<std::mutex> ws_lock;     // held while the cached workspace is in use
     if (q.workspace_bytes > 0) {
-        if (opts != nullptr && opts->workspace != nullptr) {
+        if (static_ws != nullptr) {
+            ws = static_ws;              // the plan fits it (make_plan's limit)
+        } else if (opts != nullptr && opts->workspace != nullptr) {
             if (opts->workspace_bytes < q.workspace_bytes) return SGEMM_ERR_ALLOC;
             ws = opts->workspace;
         } else {
@@ -752,6 +787,47 @@ sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_option
     return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch for sgemm_gemm_noalloc: one statically sized array in device
+// memory, which every device the library runs on holds (at its own address)
+// from the code object's load until the process ends.  In host code the
+// name `scratch` is only a stand-in for the symbol; the device address is
+// taken once per device with hipGetSymbolAddress (with that device current)
+// and that address is what the kernels receive.  Calls on one device share
+// the array, so calls that overlap on a device race; no part of it has to
+// start at zero, since every kernel that reads scratch reads only what an
+// earlier kernel of the same call wrote there.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = SGEMM_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};   // device address of `scratch`, per device
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device.
+sgemm_status static_scratch(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return SGEMM_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return SGEMM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return SGEMM_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SGEMM_OK;
+}
+
 Call nn_call(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb,
              const float* C, int64_t ldc) {
     Call c;
@@ -821,6 +897,22 @@ sgemm_status sgemm_gemm_ex(int32_t op_a, int32_t op_b, int64_t M, int64_t N, int
     return run(gemm_call(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), C, stream, opts);
 }
 
+sgemm_status sgemm_gemm_noalloc(int32_t op_a, int32_t op_b, int64_t M, int64_t N, int64_t K, float alpha,
+                                const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                                int64_t ldc, hipStream_t stream, const sgemm_options* opts) {
+    bool ta, tb;
+    if (!op_of(op_a, &ta) || !op_of(op_b, &tb)) return SGEMM_ERR_INVALID_ARG;
+    if (opts != nullptr && (opts->workspace != nullptr || opts->workspace_bytes != 0)) return SGEMM_ERR_INVALID_ARG;
+    const Call call = gemm_call(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    Plan p;
+    sgemm_status st = make_plan(call, opts, &p, kStaticScratchBytes);   // every check before any HIP call
+    if (st != SGEMM_OK || p.pub.launches == 0) return st;
+    void* ws = nullptr;
+    st = static_scratch(&ws);
+    if (st != SGEMM_OK) return st;
+    return run(call, C, stream, opts, ws, kStaticScratchBytes);
+}
+
 sgemm_status sgemm_gemm_plan_query(int32_t op_a, int32_t op_b, int64_t M, int64_t N, int64_t K, float alpha,
                                    const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
                                    const float* C, int64_t ldc, const sgemm_options* opts, sgemm_plan* plan) {
@@ -870,6 +962,9 @@ const char* sgemm_status_string(sgemm_status s) {
         case SGEMM_ERR_UNSUPPORTED: return "SGEMM_ERR_UNSUPPORTED: size beyond the kernels' index range";
         case SGEMM_ERR_HIP: return "SGEMM_ERR_HIP: HIP runtime or launch failure";
         case SGEMM_ERR_ALLOC: return "SGEMM_ERR_ALLOC: scratch allocation failed or workspace too small";
+        case SGEMM_ERR_SCRATCH_LIMIT:
+            return "SGEMM_ERR_SCRATCH_LIMIT: the call needs more scratch than the static buffer of "
+                   "sgemm_gemm_noalloc holds";
         default: return "unknown sgemm_status";
     }
 }

@@ -61,8 +61,10 @@ typedef enum sgemm_status {
                                    nonzero extent, C overlapping A or B, bad option */
     SGEMM_ERR_UNSUPPORTED = 2,  /* a size beyond the kernels' index range */
     SGEMM_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed */
-    SGEMM_ERR_ALLOC = 4         /* scratch allocation failed, or the caller's
+    SGEMM_ERR_ALLOC = 4,        /* scratch allocation failed, or the caller's
                                    workspace is too small */
+    SGEMM_ERR_SCRATCH_LIMIT = 5 /* sgemm_gemm_noalloc: no plan of the call fits the
+                                   static scratch buffer */
 } sgemm_status;
 
 /*
@@ -207,6 +209,35 @@ sgemm_status sgemm_gemm(int32_t op_a, int32_t op_b, int64_t M, int64_t N, int64_
 sgemm_status sgemm_gemm_ex(int32_t op_a, int32_t op_b, int64_t M, int64_t N, int64_t K, float alpha,
                            const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
                            float* C, int64_t ldc, hipStream_t stream, const sgemm_options* opts);
+
+/*
+ * sgemm_gemm_ex for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc.  It computes exactly what sgemm_gemm_ex computes with the same
+ * arguments, but allocates and frees nothing: the scratch its kernels need
+ * (packed operand copies, split-K slices, stream-K partial tiles) lives in
+ * one static device array of SGEMM_NOALLOC_SCRATCH_BYTES that each device the
+ * library runs on holds until the process ends (its address is looked up
+ * once per device, on the first call there).
+ *   - The automatic plan is the fastest one whose scratch fits the array (so
+ *     it can differ from sgemm_gemm's plan, and with it the rounding order;
+ *     results stay within the same bound).  Options that force a plan needing
+ *     more return SGEMM_ERR_SCRATCH_LIMIT, with nothing enqueued.
+ *   - opts->workspace must be NULL (and workspace_bytes 0): SGEMM_ERR_INVALID_ARG
+ *     otherwise.
+ *   - Every call on a device shares that device's array and leaves its last
+ *     contents there; nothing in it needs to start at zero.  Calls that overlap
+ *     on one device (different streams, or several host threads without
+ *     ordering) race on it: order them on one stream or synchronise.
+ * Arguments, semantics and the other errors are those of sgemm_gemm_ex.  No
+ * device memory is allocated or freed (the host-side plan cache may grow on
+ * the first call of a new shape).
+ */
+#define SGEMM_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+sgemm_status sgemm_gemm_noalloc(int32_t op_a, int32_t op_b, int64_t M, int64_t N, int64_t K, float alpha,
+                                const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                                float* C, int64_t ldc, hipStream_t stream, const sgemm_options* opts);
 
 /* The plan sgemm_gemm_ex would use.  Host only, no HIP call. */
 sgemm_status sgemm_gemm_plan_query(int32_t op_a, int32_t op_b, int64_t M, int64_t N, int64_t K, float alpha,

@@ -365,3 +365,22 @@ def test_binding_rejects_overlapping_rows():
         lay((8, 4), (1, 8), "C")                                          # C is row-major only
     with pytest.raises(ValueError):
         lay((8, 4), (2, 16), "B", allow_column_major=True)                # neither stride is 1
+
+
+def test_noalloc_checks_run_before_any_hip_call():
+    """sgemm_gemm_noalloc validates and plans on the host before touching the
+    device: invalid arguments, a caller workspace, and a forced plan whose
+    scratch exceeds the static buffer are refused with no GPU present."""
+    o = lib._options
+    assert lib.gemm_noalloc_raw(0, 0, -1, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4) == 1         # negative size
+    assert lib.gemm_noalloc_raw(2, 0, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4) == 1          # bad op flag
+    assert lib.gemm_noalloc_raw(0, 0, 64, 64, 64, 1.0, A, 64, B, 64, 0.0, C, 64,
+                                opts=o(workspace=0x7000000, workspace_bytes=1 << 20)) == 1
+    big = (0, 0, 4096, 4096, 512, 1.0, A, 512, B, 4096, 0.0, C, 4096)
+    forced = {"path": "mfma", "tile": 2, "decomposition": "tiles", "split_k": 8}
+    assert lib.gemm_plan_query(0, 0, 4096, 4096, 512, **forced)["workspace_bytes"] > lib.NOALLOC_SCRATCH_BYTES
+    assert lib.gemm_noalloc_raw(*big, opts=o(**forced)) == 5                                # SGEMM_ERR_SCRATCH_LIMIT
+    assert lib.gemm_noalloc_raw(*big, opts=o(path="skinny")) == 1                           # M > 32
+    assert "static buffer" in lib.sgemm_status_string(5)
+    # empty products enqueue nothing and need no device
+    assert lib.gemm_noalloc_raw(0, 0, 0, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4) == 0
