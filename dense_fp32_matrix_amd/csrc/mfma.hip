@@ -26,9 +26,8 @@
 // read from a k-contiguous stage as a single 16-byte LDS read.
 #include <hip/hip_runtime.h>
 
-#include <type_traits>
-
 #include "kernels.hpp"
+#include "lds_layout.hpp"
 
 namespace sgemm_impl {
 
@@ -60,14 +59,6 @@ struct MfmaCfg {
     static_assert(BK == 16 || BK == 32, "the chunk swizzle is defined for BK = 16 and 32");
     static_assert(KG % 2 == 0, "the fragment sets alternate within a K-step");
 };
-
-// Chunk-position swizzle of row r of a k-contiguous stage (BK/4 chunks of
-// 16 bytes per row): logical chunk c is stored at chunk c ^ swz(r).
-template <int BK>
-__device__ __forceinline__ int a_swizzle(int r) {
-    if constexpr (BK == 16) return ((r >> 1) ^ (r >> 3)) & 3;
-    else return (r ^ (r >> 3)) & 7;
-}
 
 // Scheduling hints for one K-loop iteration of KG groups of NM MFMAs each:
 // in every group one LDS read (the next group's fragments, NR of them) is
@@ -200,66 +191,6 @@ __device__ __forceinline__ void write_tile(const TileOut& o, const f32x16 (&acc)
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void glb_void_t;
 
-// Stage layouts of one operand.
-//  KC: R rows of BK floats (k contiguous within a row), the 16-byte chunks of
-//      row r at XOR-swizzled positions; fragments are read as 16-byte
-//      chunks.  A stored M x K and B stored N x K (transposed) use it.
-//  KM: BK rows of R floats (k-major), in blocks of 256 / R rows whose starts
-//      are GS floats apart; fragments are read one float per k row.  B
-//      stored K x N and A stored K x M (transposed) use it.
-// elem() gives, for instruction `ins` and a lane, the non-K index r and the
-// K index k of the element(s) that lane fetches; dst() the stage offset the
-// instruction writes (lane l at dst + W * l).
-template <int R, int BK, int W>
-struct KcLayout {
-    static constexpr bool KC = true;
-    static constexpr int SEG = 64 * W;                    // floats one instruction writes
-    static constexpr int FLOATS = R * BK;
-    static constexpr int INSTR = FLOATS / SEG;
-    static_assert(SEG % BK == 0, "an instruction fills whole rows");
-    static __device__ __forceinline__ void elem(int ins, int lane, int& r, int& k) {
-        const int p = ins * SEG + W * lane;
-        r = p / BK;
-        k = 4 * (((p % BK) / 4) ^ a_swizzle<BK>(r)) + p % 4;
-    }
-    static __device__ __forceinline__ int dst(int ins) { return ins * SEG; }
-    // 16-byte chunk c (k = 4c .. 4c + 3) of row r
-    static __device__ __forceinline__ int chunk(int r, int c) { return r * BK + 4 * (c ^ a_swizzle<BK>(r)); }
-};
-
-template <int R, int BK, int W>
-struct KmLayout {
-    static constexpr bool KC = false;
-    static constexpr int SEG = 64 * W;
-    static constexpr int ROWS = 256 / R;                  // k rows per 1 KB block
-    static constexpr int GS = 256 + 8 * ROWS;            // floats between blocks
-    static constexpr int SEGS = 256 / SEG;                // instructions per block
-    static constexpr int INSTR = BK / ROWS * SEGS;
-    static constexpr int FLOATS = BK / ROWS * GS;
-    static_assert(R == 64 || R == 128 || R == 256, "blocks hold one, two or four rows");
-    static_assert((4 / ROWS) * GS % 64 == 32, "lane halves of a fragment read 32 banks apart");
-    static __device__ __forceinline__ void elem(int ins, int lane, int& r, int& k) {
-        const int f = (ins % SEGS) * SEG + W * lane;       // float within the block
-        k = ins / SEGS * ROWS + f / R;
-        r = f % R;
-    }
-    static __device__ __forceinline__ int dst(int ins) { return ins / SEGS * GS + ins % SEGS * SEG; }
-    // k row k starts at this offset
-    static __device__ __forceinline__ int krow(int k) { return (k / ROWS) * GS + (k % ROWS) * R; }
-};
-
-template <bool TA, int BM, int BK, int W>
-using ALayout = std::conditional_t<TA, KmLayout<BM, BK, W>, KcLayout<BM, BK, W>>;
-template <bool TB, int BN, int BK, int W>
-using BLayout = std::conditional_t<TB, KcLayout<BN, BK, W>, KmLayout<BN, BK, W>>;
-
-// Floats per stage of the direct-to-LDS layout: A region, then B region (the
-// same for both lane widths).
-template <int OPS, int BM, int BN, int BK>
-struct DtlStageFloats {
-    static constexpr int value = ALayout<(OPS & 1) != 0, BM, BK, 4>::FLOATS + BLayout<(OPS & 2) != 0, BN, BK, 4>::FLOATS;
-};
-
 // The direct loads of one operand that one wave issues per K-step: PER
 // instructions, ins = i * waves + wave.  Each keeps a running per-lane
 // source pointer that one issue advances by one K-step (steps are issued in
@@ -282,8 +213,7 @@ struct DtlLoads {
         for (int i = 0; i < PER; ++i) {
             int r, k;
             L::elem(i * waves + wave, lane, r, k);
-            constexpr int lanew = L::SEG / 64;
-            const int rr = min(r0 + r, L::KC ? lim - 1 : (lim - 1) & ~(lanew - 1));
+            const int rr = clamp_index<L>(r0 + r, lim);
             ptr[i] = X + (L::KC ? (int64_t)rr * ld + kb + k : (int64_t)(kb + k) * ld + rr);
             kk[i] = k;
         }
