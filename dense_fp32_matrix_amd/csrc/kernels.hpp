@@ -5,6 +5,8 @@
 #include <cstdint>
 #include <hip/hip_runtime.h>
 
+#include "tile_order.hpp"
+
 namespace sgemm_impl {
 
 // One launch of a tiled product kernel.  The kernel computes, for every
@@ -43,28 +45,6 @@ __device__ __forceinline__ void store_scaled(float* p, float v, float alpha, flo
     v = alpha * v;
     if (beta != 0.f) v = __builtin_fmaf(beta, *p, v);
     *p = v;
-}
-
-// Workgroup -> output tile.  Consecutive workgroup ids are dispatched
-// round-robin over the chip's 8 XCDs (each with its own L2), so id b is first
-// renumbered so that every XCD receives one contiguous range of logical
-// tiles; logical tiles are then walked in groups of group_m tile rows,
-// column by column, so the tiles one XCD holds at a time share rows of A
-// and columns of B.
-__host__ __device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int group_m, int* tm, int* tn) {
-    const int total = tiles_m * tiles_n;
-    const int xcd = bid % 8;
-    const int local = bid / 8;
-    const int per = total / 8;
-    const int rem = total % 8;
-    const int t = xcd * per + (xcd < rem ? xcd : rem) + local;
-    const int span = group_m * tiles_n;
-    const int group = t / span;
-    const int first_m = group * group_m;
-    const int gm = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
-    const int within = t - group * span;
-    *tm = first_m + within % gm;
-    *tn = within / gm;
 }
 
 // Tile shapes of each path.  The kernels are instantiated for exactly these;

@@ -20,6 +20,7 @@
 #include <vector>
 
 #include "lds_layout.hpp"
+#include "tile_order.hpp"
 
 using namespace sgemm_impl;
 
@@ -154,7 +155,29 @@ void dump_all_ops(int tile) {
     dump_tile<BM, BN, BK, WGM, WGN, 3>(tile);
 }
 
+// Tile order: for every grid of tiles (and the raster group heights the
+// dispatcher uses), workgroup ids 0 .. tiles - 1 map one to one onto the
+// output tiles.
+void check_tile_order() {
+    for (int tm_n = 1; tm_n <= 48; ++tm_n)
+        for (int tn_n = 1; tn_n <= 48; ++tn_n)
+            for (int gm : {1, tm_n < 8 ? tm_n : 8}) {
+                std::vector<int> seen(tm_n * tn_n, 0);
+                for (int b = 0; b < tm_n * tn_n; ++b) {
+                    int tm, tn;
+                    tile_coords(b, tm_n, tn_n, gm, &tm, &tn);
+                    if (tm < 0 || tm >= tm_n || tn < 0 || tn >= tn_n || seen[tm * tn_n + tn]++) {
+                        std::printf("FAIL tile order %d x %d group %d: id %d -> (%d, %d)\n", tm_n, tn_n, gm, b, tm, tn);
+                        ++failures;
+                        return;
+                    }
+                }
+            }
+    std::printf("ok tile order\n");
+}
+
 int main() {
+    check_tile_order();
     check_rbk<256, 16>();
     check_rbk<128, 16>();
     check_rbk<64, 32>();

@@ -74,8 +74,9 @@ def test_layouts_cover_each_element_once(layout_output):
     fails = [ln for ln in lines if ln.startswith("FAIL")]
     oks = [ln for ln in lines if ln.startswith("ok")]
     assert rc == 0 and not fails, fails
-    # KC and KM, two lane widths, five (R, BK) shapes, loader coverage and edge clamps
-    assert len(oks) == 40
+    # KC and KM, two lane widths, five (R, BK) shapes, loader coverage and
+    # edge clamps, and the tile order
+    assert len(oks) == 41 and "ok tile order" in oks
 
 
 def test_bank_model_reproduces_probe_patterns():
