@@ -10,7 +10,9 @@ roofline of the dominant kernel (its time per step from two HIP events on the
 launch stream around the timed steps; for a plan of one launch per step that
 is the kernel's own launch time plus the gap to the next launch, for a plan of
 several launches it covers all of them), against the FP32 matrix-core peak,
-and the host oracle's throughput on a bounded sample of the same workload.
+the median and minimum of launches timed one by one after a cache flush
+(`flushed`), and the host oracle's throughput on a bounded sample of the same
+workload and on the 256^3 workload (all host threads and one thread).
 """
 import argparse
 import hashlib
@@ -43,10 +45,14 @@ def parse():
     ap.add_argument("--split-k", type=int, default=0)
     ap.add_argument("--decomposition", default="auto")
     ap.add_argument("--pack", default="auto", choices=["auto", "never", "always"])
+    ap.add_argument("--tile-order", default="xcd", choices=["xcd", "plain"],
+                    help="matrix-core tile order: XCD-aware (default) or plain row-major, for comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time of the oracle sample (0 = skip the CPU baseline)")
     ap.add_argument("--flush-mib", type=int, default=1024,
-                    help="size of the cache-flush buffer for the flushed per-launch median")
+                    help="size of the buffer read (or written) before each flushed launch")
+    ap.add_argument("--flush-launches", type=int, default=50,
+                    help="launches timed one by one after a cache flush (0 = none)")
     ap.add_argument("--probe-seconds", type=float, default=1.5,
                     help="untimed steps before the timed region while rocm-smi samples the clocks (0 = none)")
     return ap.parse_args()
@@ -97,6 +103,27 @@ def sample_clocks(stop, out):
             out["power_w"].append(float(m.group(1)))
 
 
+def cpu_oracle_small(threads_all):
+    """The oracle on the 256^3 workload: median of 3 runs on all host threads
+    and on one thread (TFLOP/s)."""
+    import oracle
+    import workloads
+    w = workloads.CONFIGS["sgemm_256"]
+    An, Bn = w.a().numpy(), w.b().numpy()
+    out = {}
+    for threads in (threads_all, 1):
+        oracle.set_num_threads(threads)
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.sgemm(An, Bn)
+            ts.append(time.perf_counter() - t0)
+        out[f"threads_{threads}"] = {"value": 2 * w.M * w.N * w.K / statistics.median(ts) / 1e12,
+                                     "unit": "TFLOP/s", "ms_median": statistics.median(ts) * 1e3}
+    oracle.set_num_threads(threads_all)
+    return {"workload": w.name, "kind": "oracle", **out}
+
+
 def cpu_baseline(w, A, B, target_s):
     """The host oracle on the first R rows of the workload (R chosen so the
     timed run takes about target_s seconds), scaled to TFLOP/s."""
@@ -141,9 +168,10 @@ def main():
     B = B_host.to(dev)
     C = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
     opts = {}
-    if args.path != "auto" or args.tile >= 0 or args.split_k or args.decomposition != "auto" or args.pack != "auto":
+    if (args.path != "auto" or args.tile >= 0 or args.split_k or args.decomposition != "auto" or args.pack != "auto"
+            or args.tile_order != "xcd"):
         opts = {"path": args.path, "tile": args.tile, "split_k": args.split_k,
-                "decomposition": args.decomposition, "pack": args.pack}
+                "decomposition": args.decomposition, "pack": args.pack, "tile_order": args.tile_order}
     plan = lib.sgemm_plan_query(w.M, w.N, w.K, A.data_ptr(), w.lda, B.data_ptr(), w.ldb, C.data_ptr(), w.N,
                                 **opts)
 
@@ -206,25 +234,43 @@ def main():
     flops, alg_bytes = algorithmic(w)
     value = flops * args.steps / wall / 1e12
 
-    # flushed per-launch median: overwrite a buffer larger than L2 + MALL before each launch
-    flush = torch.empty(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
-    fl = []
-    for _ in range(10):
-        flush.fill_(1.0)
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record(stream)
-        step()
-        e.record(stream)
-        torch.cuda.synchronize()
-        fl.append(s.elapsed_time(e))
-    del flush
+    # Launches from cold caches: before each, read (or write) a buffer larger
+    # than the L2s and the 256 MB MALL together, so the operands come from HBM.
+    # Reading leaves the caches holding clean lines; writing (the pages'
+    # flush) leaves up to 256 MB of dirty lines whose write-back competes
+    # with the launch's reads, so that figure is reported beside the other.
+    def cold_launches(mode):
+        ts = []
+        for _ in range(args.flush_launches):
+            if mode == "read":
+                flush.sum()
+            else:
+                flush.fill_(1.0)
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            step()
+            e.record(stream)
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e))
+        return ts
+
+    flushed = None
+    if args.flush_launches > 0:
+        flush = torch.ones(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        fr = cold_launches("read")
+        fw = cold_launches("write")
+        del flush
+        flushed = {"flush": f"{args.flush_mib} MiB read before each launch", "launches": len(fr),
+                   "ms_median": statistics.median(fr), "ms_min": min(fr),
+                   "write_flush_ms_median": statistics.median(fw), "write_flush_ms_min": min(fw)}
 
     kernel_ms = event_ms_per_step
     main_kernel = {1: "naive_gemm_kernel", 2: "valu_gemm_kernel", 3: "mfma_gemm_kernel",
                    4: "skinny_gemm_kernel"}.get(plan["path"], "?")
     src = {1: "simple.hip", 2: "valu.hip", 3: "mfma.hip", 4: "skinny.hip"}.get(plan["path"], "mfma.hip")
-    digest = source_digest([f"dense_fp32_matrix_amd/csrc/{src}", "dense_fp32_matrix_amd/csrc/kernels.hpp"])
+    digest = source_digest([f"dense_fp32_matrix_amd/csrc/{src}", "dense_fp32_matrix_amd/csrc/kernels.hpp",
+                            "dense_fp32_matrix_amd/csrc/lds_layout.hpp", "dense_fp32_matrix_amd/csrc/tile_order.hpp"])
     key = (f"{main_kernel}:{w.name}:tile{plan['tile']}:{plan['decomposition_name']}:split{plan['split_k']}"
            f":vec{plan['vector']}:pack{plan['packed']}")
     hbm_bound = w.M <= 16
@@ -242,8 +288,21 @@ def main():
     roof["launches_per_step"] = plan["launches"]
 
     cpu = None
+    cpu_small = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, A_host, B_host, args.cpu_seconds)
+        cpu_small = cpu_oracle_small(cpu["cores"])
+    if flushed is not None:
+        # the same roofline as the warm figure, on the flushed launch median (the whole call)
+        fm = flushed["ms_median"] * 1e-3
+        if hbm_bound:
+            flushed["achieved"] = alg_bytes / fm / 1e9
+            flushed["unit"] = "GB/s"
+            flushed["frac"] = flushed["achieved"] / PEAK_HBM_GBS
+        else:
+            flushed["achieved"] = flops / fm / 1e12
+            flushed["unit"] = "TFLOP/s"
+            flushed["frac"] = flushed["achieved"] / PEAK_FP32_TFLOPS
 
     out = {
         "metric": METRIC,
@@ -263,12 +322,13 @@ def main():
                    "inputs": f"A~{w.a_kind}, B~{w.b_kind}", "path": plan["path_name"], "tile": plan["tile"],
                    "bm": plan["bm"], "bn": plan["bn"], "bk": plan["bk"], "split_k": plan["split_k"],
                    "decomposition": plan["decomposition_name"],
-                   "vector_loads": bool(plan["vector"]), "packed": plan["packed"], "workgroups": plan["workgroups"]},
+                   "vector_loads": bool(plan["vector"]), "packed": plan["packed"], "workgroups": plan["workgroups"],
+                   "tile_order": args.tile_order},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "cpu_oracle_256": cpu_small,
         "clocks": clocks,
-        "flushed_launch_ms_median": statistics.median(fl),
-        "flushed_tflops": flops / (statistics.median(fl) * 1e-3) / 1e12,
+        "flushed": flushed,
     }
     print(json.dumps(out), flush=True)
 

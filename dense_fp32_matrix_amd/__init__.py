@@ -14,7 +14,7 @@ import os
 from typing import Optional
 
 __all__ = [
-    "SgemmError", "PATHS", "DECOMPOSITIONS", "PACK",
+    "SgemmError", "PATHS", "DECOMPOSITIONS", "PACK", "TILE_ORDERS",
     "sgemm", "sgemm_ex", "sgemm_raw", "sgemm_plan_query", "sgemm_workspace_size",
     "gemm", "gemm_raw", "gemm_plan_query", "gemm_workspace_size", "gemm_noalloc", "gemm_noalloc_raw",
     "NOALLOC_SCRATCH_BYTES",
@@ -47,7 +47,7 @@ _DECOMP_NAMES = {v: k for k, v in DECOMPOSITIONS.items()}
 class _Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("tile", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("vector", ctypes.c_int32), ("decomposition", ctypes.c_int32), ("pack", ctypes.c_int32),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("tile_order", ctypes.c_int32)]
 
 
 class _Plan(ctypes.Structure):
@@ -108,9 +108,13 @@ def load_library():
 PACK = {"auto": 0, "never": 1, "always": 2}
 
 
+TILE_ORDERS = {"xcd": 0, "plain": 1}
+
+
 def _options(path="auto", tile=-1, split_k=0, vector=0, decomposition="auto", workspace=None,
-             workspace_bytes=0, pack="auto") -> _Options:
+             workspace_bytes=0, pack="auto", tile_order="xcd") -> _Options:
     o = _Options()
+    o.tile_order = TILE_ORDERS[tile_order] if isinstance(tile_order, str) else int(tile_order)
     o.pack = PACK[pack] if isinstance(pack, str) else int(pack)
     o.path = PATHS[path] if isinstance(path, str) else int(path)
     o.tile = int(tile)
@@ -210,12 +214,13 @@ def sgemm(A, B, C=None, stream=None):
 
 
 def sgemm_ex(A, B, C=None, stream=None, *, path="auto", tile=-1, split_k=0, vector=0, decomposition="auto",
-             workspace=None, pack="auto"):
+             workspace=None, pack="auto", tile_order="xcd"):
     """``sgemm`` with explicit options: ``path`` in PATHS, ``tile`` index, ``split_k``
     slices, ``vector=1`` to force 4-byte loads, ``decomposition`` in DECOMPOSITIONS,
     ``pack`` in PACK (aligned copies of misaligned operands), optional ``workspace``
-    tensor."""
-    return _call(A, B, C, stream, _options(path, tile, split_k, vector, decomposition, workspace, pack=pack))
+    tensor, ``tile_order`` in TILE_ORDERS."""
+    return _call(A, B, C, stream, _options(path, tile, split_k, vector, decomposition, workspace, pack=pack,
+                                           tile_order=tile_order))
 
 
 def gemm_raw(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0,

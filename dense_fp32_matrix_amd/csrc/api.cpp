@@ -95,10 +95,6 @@ constexpr double kPartialBw = 4e12;          // bytes/s for split-K partial slic
 constexpr double kStreamKBw = 1e13;          // bytes/s for stream-K partial tiles (written and read back
                                              // by neighbouring workgroups, cache resident)
 constexpr double kLaunch = 8e-6;             // one more dependent kernel launch
-constexpr double kSkinnyCuBw = 31e9;         // bytes/s one CU's skinny workgroup streams from B (one row
-                                             // block; two row blocks, with twice the MFMAs per byte and
-                                             // half the loads in flight, at 20e9)
-constexpr double kSkinnyHbmBw = 5.3e12;      // bytes/s the whole chip streams B at
 constexpr double kTileVisit = 2e-6;          // filling and draining one tile's pipeline, and its epilogue
 
 // Share of the CU's peak one tile shape sustains when its CU is full, with
@@ -337,6 +333,7 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
     if (o.split_k < 0 || o.vector < 0 || o.vector > 1) return SGEMM_ERR_INVALID_ARG;
     if (o.decomposition < SGEMM_DECOMP_AUTO || o.decomposition > SGEMM_DECOMP_STREAM_K) return SGEMM_ERR_INVALID_ARG;
     if (o.pack < 0 || o.pack > 2) return SGEMM_ERR_INVALID_ARG;
+    if (o.tile_order < 0 || o.tile_order > 1) return SGEMM_ERR_INVALID_ARG;
     if (o.workspace != nullptr && !aligned(o.workspace, 256)) return SGEMM_ERR_INVALID_ARG;
     const int64_t M = c.M, N = c.N, K = c.K;
     const bool trans = c.ta || c.tb;
@@ -387,16 +384,19 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
         best.tile = 0;
         best.k_chunk = K;
     } else if (path == SGEMM_PATH_SKINNY) {
-        // A workgroup streams its slice of B at a rate that one CU caps, so
-        // the skinny tiles run one workgroup per CU.  Either K is split
-        // uniformly across workgroups as far as they still fit one per CU (a
-        // second workgroup on some CUs makes those the tail), or stream-K
-        // shares the (strip, 64-deep K-step) units out evenly over one
-        // workgroup per CU and a fix-up sums the strips that two workgroups
-        // share.  Both are floored by the chip's streaming rate: with one row
-        // block 172 strips already reach it, and stream-K pays where the CUs,
-        // not HBM, are the limit (two row blocks, long K) or where the uniform
-        // split needs 4 or more slices.
+        // The kernel streams B fastest when every CU holds one workgroup from
+        // start to end.  A uniform K split into S slices of at least four
+        // 64-deep steps gives tiles x S workgroups; where that fills the CUs
+        // in whole rounds with at most a quarter of a round idle (64 strips x
+        // 4, 32 x 8, 200 or 224 x 1) the split wins, and the slices are
+        // summed by the split-K reduction.  Where no split does (172 strips:
+        // 172 or 344 workgroups; 344 strips), stream-K shares the (strip,
+        // K-step) units out evenly over two workgroups per CU (one with two
+        // row blocks, whose A fragments and MFMAs double) and the fix-up sums
+        // the shared strips.  Measured cold (B read from HBM) on 18 shapes of
+        // 1-32 rows, 256-22016 columns and 4096-65536 deep, the rule picks
+        // the fastest plan or one within 3 %, except 4 strips 65536 deep (64
+        // slices, 9 % behind stream-K).
         best.tile = o.tile >= 0 ? o.tile : (M <= 16 ? 0 : 1);
         const TileShape& t = kSkinnyTiles[best.tile];
         if (M > t.bm) return SGEMM_ERR_INVALID_ARG;     // the tile holds at most bm rows of A
@@ -412,33 +412,21 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
         const int64_t k_chunk = round_up(cdiv(K, splits), t.bk);
         best.splits = cdiv(K, k_chunk);
         best.k_chunk = k_chunk;
+        const int64_t wgs = tiles * best.splits;
+        const bool whole_rounds = 4 * wgs >= 3 * round_up(wgs, kNumCUs);
         // stream-K units are the kernel's 64-deep K-steps
         const bool sk_ok = o.split_k <= 1 && o.decomposition != SGEMM_DECOMP_TILES;
-        if (sk_ok) {
+        if (sk_ok && (o.decomposition == SGEMM_DECOMP_STREAM_K || !whole_rounds)) {
             const int64_t k_steps = cdiv(K, 64);
             const int64_t units = tiles * k_steps;
-            const int64_t ipw = cdiv(units, kNumCUs);
-            const double cu_bw = t.bm > 16 ? 20e9 : kSkinnyCuBw;
-            const double per_unit = 64.0 * t.bn * 4 / cu_bw;           // B bytes of a unit at one CU's rate
-            const double floor = 4.0 * ((double)M * K + (double)K * N + (double)M * N) / kSkinnyHbmBw;
-            const int64_t wgs = tiles * best.splits;
-            const double t_tiles = std::max(floor, (double)cdiv(wgs, kNumCUs) * (k_chunk / 64.0) * per_unit) +
-                                   (best.splits > 1 ? kLaunch : 0.0);
-            const double t_sk = std::max(floor, ipw * per_unit) + kLaunch;
-            // with 4 or more uniform slices the two plans stream the same
-            // shares; the stream-K fix-up then measured 2-12 % faster than the
-            // split-K reduction of the slices, so stream-K takes the tie there
-            const bool sk_wins = best.splits >= 4 ? t_sk <= t_tiles : t_sk < 0.95 * t_tiles;
-            if (o.decomposition == SGEMM_DECOMP_STREAM_K || sk_wins) {
-                best.decomposition = SGEMM_DECOMP_STREAM_K;
-                best.splits = 1;
-                best.k_chunk = K;
-                best.grid = std::min<int64_t>(kNumCUs, units);
-                best.k_steps = k_steps;
-                best.sk_tiles = tiles;
-                best.dp_tiles = 0;
-                best.sk_ipw = cdiv(units, best.grid);
-            }
+            best.decomposition = SGEMM_DECOMP_STREAM_K;
+            best.splits = 1;
+            best.k_chunk = K;
+            best.grid = std::min<int64_t>(kNumCUs * (t.bm > 16 ? 1 : 2), units);
+            best.k_steps = k_steps;
+            best.sk_tiles = tiles;
+            best.dp_tiles = 0;
+            best.sk_ipw = cdiv(units, best.grid);
         }
     } else if (path == SGEMM_PATH_MFMA) {
         // With 4-byte lanes only the narrow tiles are built; a forced tile
@@ -749,7 +737,7 @@ sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_option
     g.tiles_n = (int32_t)q.tiles_n;
     // 8 tile rows per raster group: the workgroups one XCD holds at a time
     // then cover a roughly square block of tiles
-    g.group_m = (int32_t)std::min<int64_t>(q.tiles_m, 8);
+    g.group_m = (opts != nullptr && opts->tile_order == 1) ? 0 : (int32_t)std::min<int64_t>(q.tiles_m, 8);
     g.C = C;
     g.ldc = c.ldc;
     if (q.decomposition == SGEMM_DECOMP_STREAM_K) {

@@ -28,8 +28,8 @@ struct GemmArgs {
     int64_t lda, ldb, ldc;
     int64_t c_slice;    // elements between consecutive slices' outputs
     int32_t tiles_m, tiles_n;
-    int32_t group_m;    // tile rows per raster group (tile-order swizzle), >= 1
-    // stream-K decomposition (MFMA path only; sk_iters == 0 disables it)
+    int32_t group_m;    // tile rows per raster group of the XCD-aware order, or 0 for row-major order
+    // stream-K decomposition (MFMA and skinny paths; sk_iters == 0 disables it)
     int32_t sk_grid;    // persistent workgroups
     int32_t dp_tiles;   // tiles computed whole, before the stream-K tiles
     int32_t k_steps;    // K-steps per tile, ceil(K / BK)

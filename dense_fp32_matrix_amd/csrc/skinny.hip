@@ -213,7 +213,7 @@ void skinny_gemm_kernel(GemmArgs g) {
             const int q0 = (int)(it - (int64_t)j * g.k_steps);
             const int q1 = (int)min<int64_t>(g.k_steps, q0 + (it_end - it));
             int tm, tn;
-            tile_coords(j, 1, g.tiles_n, 1, &tm, &tn);
+            tile_coords(j, 1, g.tiles_n, g.group_m, &tm, &tn);
             n_w = tn * 64;
             kb = q0 * kStageK;
             ke = min(g.K, q1 * kStageK);

@@ -15,8 +15,14 @@ namespace sgemm_impl {
 // renumbered so that every XCD receives one contiguous range of logical
 // tiles; logical tiles are then walked in groups of group_m tile rows,
 // column by column, so the tiles one XCD holds at a time share rows of A
-// and columns of B.
+// and columns of B.  group_m == 0 selects the plain row-major order instead
+// (tile b is row b / tiles_n, column b % tiles_n), for comparison.
 SGEMM_TILE_HD void tile_coords(int bid, int tiles_m, int tiles_n, int group_m, int* tm, int* tn) {
+    if (group_m == 0) {
+        *tm = bid / tiles_n;
+        *tn = bid - *tm * tiles_n;
+        return;
+    }
     const int total = tiles_m * tiles_n;
     const int xcd = bid % 8;
     const int local = bid / 8;

@@ -125,6 +125,12 @@ typedef enum sgemm_decomposition {
  *                   operands and split-K or stream-K partials, or NULL to let the
  *                   library provide it (see "Memory and streams").  The caller keeps
  *                   it alive until the work completes.
+ *   tile_order    : order in which workgroups take the matrix-core path's output
+ *                   tiles: 0 = XCD-aware (each of the 8 XCDs, with its own L2, takes
+ *                   one contiguous range of tiles, walked in groups of 8 tile rows;
+ *                   the rasterisation of "如何让计算受限问题真正达到计算受限" section
+ *                   5.2), 1 = plain row-major (for comparison).  Results are the
+ *                   same bits either way.
  */
 typedef struct sgemm_options {
     int32_t path;
@@ -135,6 +141,7 @@ typedef struct sgemm_options {
     int32_t pack;
     void* workspace;
     size_t workspace_bytes;
+    int32_t tile_order;
 } sgemm_options;
 
 /* sgemm with explicit options (tests and benchmarks).  opts may be NULL. */
@@ -157,7 +164,8 @@ typedef struct sgemm_plan {
     int64_t k_chunk;         /* K elements per slice */
     int64_t workgroups;      /* workgroups of the main kernel */
     size_t workspace_bytes;  /* split-K / stream-K scratch (0 if none) */
-    int32_t launches;        /* kernels enqueued by the call (0, 1 or 2) */
+    int32_t launches;        /* kernels enqueued by the call (0 to 4: packing copies, the matrix
+                                kernel, a split-K reduction or stream-K fix-up) */
     int32_t decomposition;   /* sgemm_decomposition actually used */
     int64_t dp_tiles;        /* stream-K: tiles computed whole first */
     int64_t sk_tiles;        /* stream-K: tiles whose K-steps are shared out */

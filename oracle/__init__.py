@@ -35,6 +35,8 @@ def _load():
             _build.build()
         lib = ctypes.CDLL(_LIB_PATH)
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         lib.oracle_sgemm.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64]
         lib.oracle_sgemm.restype = ctypes.c_int
         lib.oracle_sgemm_entries.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64,
@@ -73,6 +75,11 @@ def _ptr(a):
 def num_threads() -> int:
     """OpenMP threads the oracle runs on."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the following calls (results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def sgemm(A, B, with_denominator: bool = False):

@@ -43,6 +43,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads the following calls use (n >= 1); results do not depend on it. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Full product.  C (M x N, leading dimension ldc) receives the fp64 sums.
  * D, when not NULL, receives sum_k |A||B| with leading dimension ldd.

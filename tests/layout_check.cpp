@@ -161,7 +161,7 @@ void dump_all_ops(int tile) {
 void check_tile_order() {
     for (int tm_n = 1; tm_n <= 48; ++tm_n)
         for (int tn_n = 1; tn_n <= 48; ++tn_n)
-            for (int gm : {1, tm_n < 8 ? tm_n : 8}) {
+            for (int gm : {0, 1, tm_n < 8 ? tm_n : 8}) {
                 std::vector<int> seen(tm_n * tn_n, 0);
                 for (int b = 0; b < tm_n * tn_n; ++b) {
                     int tm, tn;

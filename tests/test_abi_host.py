@@ -140,6 +140,7 @@ def test_bad_options_rejected():
     assert lib.sgemm_raw(*base, opts=lib._options(path="naive", split_k=2)) == 1
     assert lib.sgemm_raw(*base, opts=lib._options(workspace=A + 16, workspace_bytes=1 << 20)) == 1
     assert lib.sgemm_raw(*base, opts=lib._options(pack=-1)) == 1
+    assert lib.sgemm_raw(*base, opts=lib._options(tile_order=2)) == 1
 
 
 def test_wide_tiles_have_no_narrow_lanes():
@@ -239,14 +240,14 @@ def test_packing_plans():
 def test_default_plans_fill_the_chip():
     """Every matrix-core benchmark shape gets at least one workgroup per CU
     (256), with split-K or stream-K where the output alone has too few tiles;
-    the skinny streaming kernel runs at most one workgroup per CU on more
-    than half of the CUs (its 64-column strips, times the K slices)."""
+    the skinny streaming kernel fills the CUs: K slices in whole rounds of
+    one workgroup per CU, or stream-K over two workgroups per CU."""
     shapes = [(4096, 4096, 4096), (4097, 3001, 2049), (8192, 11008, 4096), (16, 11008, 4096),
               (512, 512, 65536)]
     for M, N, K in shapes:
         p = lib.sgemm_plan_query(M, N, K, lda=K, ldb=N, ldc=N)
         if p["path_name"] == "skinny":
-            assert 128 < p["workgroups"] <= 256, (M, N, K, p)
+            assert p["workgroups"] in ((256, 512) if p["decomposition_name"] == "stream_k" else (256,)), (M, N, K, p)
         else:
             assert p["workgroups"] >= 256, (M, N, K, p)
         Kg = p["k_padded"]
@@ -324,21 +325,23 @@ def test_plan_cache_keys():
     assert lib.gemm_plan_query("N", "N", M, N, K) == first
 
 
-def test_skinny_stream_k_takes_ties_at_four_slices():
-    """The skinny planner's choice between uniform K slices and stream-K:
-    where the uniform plan needs 4 or more slices the two stream equal
-    shares and stream-K is chosen; with 172 strips and no split (one
-    workgroup per strip), or 2 slices, the uniform plan stays."""
-    for M, N, K in [(16, 256, 65536), (4, 1024, 16384), (16, 2048, 8192), (32, 4096, 4096), (16, 4096, 11008)]:
-        p = lib.sgemm_plan_query(M, N, K)
-        assert p["path_name"] == "skinny" and p["decomposition_name"] == "stream_k", (M, N, K, p)
-        assert p["split_k"] == 1 and p["workgroups"] == 256
-        tiles = lib.sgemm_plan_query(M, N, K, decomposition="tiles")
-        assert tiles["split_k"] >= 4, (M, N, K, tiles)
-    for M, N, K, split in [(16, 11008, 4096, 1), (8, 8192, 8192, 2)]:
+def test_skinny_plan_rule():
+    """The skinny planner: a uniform K split when strips x slices fill the
+    256 CUs in whole rounds with at most a quarter of a round idle, else
+    stream-K over two workgroups per CU (one with two row blocks)."""
+    for M, N, K, split in [(16, 4096, 4096, 4), (1, 4096, 11008, 4), (32, 4096, 11008, 4), (16, 2048, 8192, 8),
+                           (16, 8192, 4096, 2), (16, 12800, 4096, 1), (16, 14336, 4096, 1), (4, 1024, 16384, 16),
+                           (16, 256, 65536, 64)]:
         p = lib.sgemm_plan_query(M, N, K)
         assert p["path_name"] == "skinny" and p["decomposition_name"] == "tiles", (M, N, K, p)
-        assert p["split_k"] == split
+        assert p["split_k"] == split and p["workgroups"] == -(-N // 64) * split, (M, N, K, p)
+    for M, N, K, grid in [(16, 11008, 4096, 512), (8, 11008, 4096, 512), (16, 11008, 8192, 512),
+                          (32, 11008, 4096, 256), (16, 22016, 4096, 512), (16, 256, 128, 8)]:
+        p = lib.sgemm_plan_query(M, N, K)
+        assert p["path_name"] == "skinny" and p["decomposition_name"] == "stream_k", (M, N, K, p)
+        assert p["split_k"] == 1 and p["workgroups"] == grid, (M, N, K, p)
+    # slices keep at least four 64-deep steps: 4 strips x 2 slices of 256 fill nothing, stream-K it is
+    assert lib.sgemm_plan_query(16, 256, 512)["decomposition_name"] == "stream_k"
 
 
 def test_binding_rejects_overlapping_rows():

@@ -139,16 +139,34 @@ def test_skinny_stream_k(oracle_mod, shape, vector):
     K-step) units, partial strips summed by the fix-up kernel)."""
     M, N, K = shape
     plan = lib.sgemm_plan_query(M, N, K, path="skinny", decomposition="stream_k", vector=vector)
-    assert plan["decomposition_name"] == "stream_k" and plan["workgroups"] <= 256
+    assert plan["decomposition_name"] == "stream_k" and plan["workgroups"] <= 512   # at most the workgroups the chip holds at once
     check_case(oracle_mod, M, N, K, f"skinny stream-K v{vector}", path="skinny", decomposition="stream_k",
                vector=vector)
 
 
-@pytest.mark.parametrize("tile", [0, 1])
+@pytest.mark.parametrize("tile", list(range(lib.sgemm_tile_info("skinny", 0)["count"])))
 def test_skinny_tiles(oracle_mod, tile):
     """Every skinny tile on the rows it holds (16, or 32 with two row blocks)."""
     M = lib.sgemm_tile_info("skinny", tile)["bm"]
-    check_case(oracle_mod, M, 517, 2100, f"skinny tile {tile}", path="skinny", tile=tile, split_k=2)
+    check_case(oracle_mod, M, 516, 2100, f"skinny tile {tile}", path="skinny", tile=tile, split_k=2)
+
+
+SKINNY_EDGE_SHAPES = [(1, 1000, 200), (16, 64, 64), (5, 300, 1000), (16, 1000, 4100), (9, 11008, 512),
+                      (16, 3000, 1000), (17, 300, 1000), (32, 1000, 4100), (24, 68, 132), (16, 12800, 128),
+                      (32, 8, 4), (3, 4, 8)]
+
+
+@pytest.mark.parametrize("decomposition,split", [("stream_k", 0), ("tiles", 1), ("tiles", 3)])
+@pytest.mark.parametrize("shape", SKINNY_EDGE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_skinny_edges(oracle_mod, shape, decomposition, split):
+    """The skinny kernel in both decompositions on ragged shapes: stream-K
+    ranges shorter than a strip and crossing strip boundaries, K tails inside
+    a 64-deep unit, A rows past M and strips past N reading zeros."""
+    M, N, K = shape
+    opts = {"path": "skinny", "decomposition": decomposition}
+    if split:
+        opts["split_k"] = split
+    check_case(oracle_mod, M, N, K, f"skinny {opts}", **opts)
 
 
 @pytest.mark.parametrize("path,tile", [("mfma", 0), ("mfma", 1), ("mfma", 2), ("mfma", 3), ("valu", 0)])
@@ -191,6 +209,28 @@ def test_stream_k_after_data_parallel_tiles(oracle_mod, tile):
                          ids=lambda s: "x".join(map(str, s)))
 def test_default_plan(oracle_mod, shape):
     check_case(oracle_mod, *shape, "auto")
+
+
+@pytest.mark.parametrize("opts", [{"path": "mfma", "tile": 0, "decomposition": "tiles"},
+                                  {"path": "mfma", "tile": 0, "decomposition": "stream_k"},
+                                  {"path": "mfma", "tile": 2, "decomposition": "stream_k"},
+                                  {"path": "mfma", "tile": 3, "decomposition": "tiles", "split_k": 3}],
+                         ids=["tile0", "tile0-streamk", "tile2-streamk", "tile3-split3"])
+def test_tile_order(oracle_mod, opts):
+    """The plain row-major tile order (kept for comparing against the
+    XCD-aware one).  With one tile per workgroup every tile is computed the
+    same way in either order: identical bits.  Stream-K cuts the K-steps of
+    the tiles in order, so there the order decides which tiles are split
+    where: both results are checked against the oracle instead."""
+    M, N, K = 1300, 1100, 700
+    say(f"tile order {opts}")
+    A, B = inputs(M, N, K, "uniform", 21)
+    C1 = run(A, B, **opts).cpu()
+    C2 = run(A, B, tile_order="plain", **opts).cpu()
+    if opts["decomposition"] != "stream_k":
+        assert torch.equal(C1.view(torch.int32), C2.view(torch.int32))
+    else:
+        check_case(oracle_mod, M, N, K, "plain order", tile_order="plain", **opts)
 
 
 # --- layouts: leading dimensions with NaN padding, misaligned bases -------------------------
@@ -545,9 +585,9 @@ def test_full_size_workload(oracle_mod, name):
 
 @pytest.mark.parametrize("kind", ["normal", "integer"])
 def test_full_size_skinny_stream_k(oracle_mod, kind):
-    """The skinny workload at full size through the skinny stream-K plan (the
-    default plan streams it on 172 CUs instead; this one spreads it over all
-    256 and sums the shared strips in the fix-up)."""
+    """The skinny workload at full size through the skinny stream-K plan (a
+    persistent grid of every resident workgroup, the shared strips summed in
+    workgroup order), every element checked."""
     w = workloads.CONFIGS["linear_skinny_16x4096x11008"]
     _full_size_check(oracle_mod, w, kind, {"path": "skinny", "decomposition": "stream_k"})
 

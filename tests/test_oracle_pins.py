@@ -251,6 +251,15 @@ def test_threads_do_not_change_results(oracle_mod):
     C = oracle_mod.sgemm(A, B)
     for i in range(M):
         assert np.array_equal(oracle_mod.sgemm(A[i:i + 1], B)[0], C[i])
+    # and with one thread or three
+    n = oracle_mod.num_threads()
+    try:
+        for t in (1, 3):
+            oracle_mod.set_num_threads(t)
+            assert oracle_mod.num_threads() == t
+            assert np.array_equal(oracle_mod.sgemm(A, B), C)
+    finally:
+        oracle_mod.set_num_threads(n)
 
 
 # --- the library-call form: alpha * op(A) op(B) + beta * C ------------------------------
