@@ -239,7 +239,7 @@ def main():
     # Reading leaves the caches holding clean lines; writing (the pages'
     # flush) leaves up to 256 MB of dirty lines whose write-back competes
     # with the launch's reads, so that figure is reported beside the other.
-    def cold_launches(mode):
+    def cold_launches(mode, fn=step):
         ts = []
         for _ in range(args.flush_launches):
             if mode == "read":
@@ -249,17 +249,47 @@ def main():
             s = torch.cuda.Event(enable_timing=True)
             e = torch.cuda.Event(enable_timing=True)
             s.record(stream)
-            step()
+            fn()
             e.record(stream)
             torch.cuda.synchronize()
             ts.append(s.elapsed_time(e))
         return ts
+
+    # Where the product is bound by reading B once (M <= 16), the library's
+    # read-rate probe reads the same B -- the same bytes, from the same cache
+    # state -- warm (back-to-back) and after the same flush: the attainable
+    # rate the call is compared with, beside the data-sheet peak.
+    hbm_bound = w.M <= 16
+    b_flat = B.reshape(-1) if hbm_bound and B.is_contiguous() and B.numel() % 4 == 0 else None
+    probe = None
+    if b_flat is not None:
+        part = torch.empty(lib.READ_PROBE_PARTIALS, dtype=torch.float32, device=dev)
+
+        def read_b():
+            lib.read_probe(b_flat, part)
+
+        for _ in range(args.warmup):
+            read_b()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            read_b()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        read_ms = ev0.elapsed_time(ev1) / args.steps
+        b_bytes = 4 * b_flat.numel()
+        probe = {"what": f"sgemm_read_probe over B ({w.K} x {w.N} fp32, {b_bytes} bytes), read once",
+                 "warm_ms": read_ms, "warm_gbs": b_bytes / (read_ms * 1e-3) / 1e9}
 
     flushed = None
     if args.flush_launches > 0:
         flush = torch.ones(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
         fr = cold_launches("read")
         fw = cold_launches("write")
+        if probe is not None:
+            pr = cold_launches("read", read_b)
+            probe["flushed_ms_median"] = statistics.median(pr)
+            probe["flushed_gbs"] = 4 * b_flat.numel() / (probe["flushed_ms_median"] * 1e-3) / 1e9
         del flush
         flushed = {"flush": f"{args.flush_mib} MiB read before each launch", "launches": len(fr),
                    "ms_median": statistics.median(fr), "ms_min": min(fr),
@@ -273,7 +303,6 @@ def main():
                             "dense_fp32_matrix_amd/csrc/lds_layout.hpp", "dense_fp32_matrix_amd/csrc/tile_order.hpp"])
     key = (f"{main_kernel}:{w.name}:tile{plan['tile']}:{plan['decomposition_name']}:split{plan['split_k']}"
            f":vec{plan['vector']}:pack{plan['packed']}")
-    hbm_bound = w.M <= 16
     if hbm_bound:
         achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -286,6 +315,9 @@ def main():
     roof["kernel"] = main_kernel
     roof["launch_ms"] = kernel_ms
     roof["launches_per_step"] = plan["launches"]
+    if probe is not None:
+        probe["call_vs_read_warm"] = probe["warm_ms"] / kernel_ms
+        roof["read_probe"] = probe
 
     cpu = None
     cpu_small = None
@@ -299,6 +331,9 @@ def main():
             flushed["achieved"] = alg_bytes / fm / 1e9
             flushed["unit"] = "GB/s"
             flushed["frac"] = flushed["achieved"] / PEAK_HBM_GBS
+            if probe is not None and "flushed_ms_median" in probe:
+                # the probe's time for B over the call's time for A, B and C
+                flushed["vs_read_probe"] = probe["flushed_ms_median"] / flushed["ms_median"]
         else:
             flushed["achieved"] = flops / fm / 1e12
             flushed["unit"] = "TFLOP/s"

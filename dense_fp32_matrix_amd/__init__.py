@@ -17,7 +17,7 @@ __all__ = [
     "SgemmError", "PATHS", "DECOMPOSITIONS", "PACK", "TILE_ORDERS",
     "sgemm", "sgemm_ex", "sgemm_raw", "sgemm_plan_query", "sgemm_workspace_size",
     "gemm", "gemm_raw", "gemm_plan_query", "gemm_workspace_size", "gemm_noalloc", "gemm_noalloc_raw",
-    "NOALLOC_SCRATCH_BYTES",
+    "NOALLOC_SCRATCH_BYTES", "read_probe", "read_probe_raw", "READ_PROBE_PARTIALS",
     "sgemm_tile_info", "sgemm_status_string", "sgemm_version", "library_path", "load_library",
 ]
 
@@ -99,6 +99,8 @@ def load_library():
     lib.sgemm_tile_info.restype = ctypes.c_int
     lib.sgemm_status_string.argtypes = [ctypes.c_int]
     lib.sgemm_status_string.restype = ctypes.c_char_p
+    lib.sgemm_read_probe.argtypes = [p, i64, p, p]
+    lib.sgemm_read_probe.restype = ctypes.c_int
     lib.sgemm_version.argtypes = []
     lib.sgemm_version.restype = ctypes.c_char_p
     _lib = lib
@@ -273,6 +275,34 @@ def gemm(A, B, C=None, stream=None, *, trans_a=False, trans_b=False, alpha=1.0, 
     if st != SGEMM_OK:
         raise SgemmError(st, "sgemm_gemm")
     return C
+
+
+READ_PROBE_PARTIALS = 1024
+
+
+def read_probe_raw(x, n, partial, stream=0) -> int:
+    """sgemm_read_probe with integer device addresses; returns the status code."""
+    return load_library().sgemm_read_probe(x, n, partial, stream)
+
+
+def read_probe(x, partial=None, stream=None):
+    """Read the float32 tensor x (contiguous) once on the GPU: the read-rate
+    probe.  Returns the READ_PROBE_PARTIALS per-workgroup sums."""
+    import torch
+    for t, name in ((x, "x"), (partial, "partial")):
+        if t is not None and (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda
+                              or not t.is_contiguous()):
+            raise TypeError(f"{name} must be a contiguous float32 GPU tensor")
+    if partial is None:
+        partial = torch.empty(READ_PROBE_PARTIALS, dtype=torch.float32, device=x.device)
+    if partial.numel() < READ_PROBE_PARTIALS or partial.device != x.device:
+        raise ValueError(f"partial must hold {READ_PROBE_PARTIALS} floats on x's device")
+    with torch.cuda.device(x.device):
+        st = read_probe_raw(x.data_ptr() if x.numel() else None, x.numel(), partial.data_ptr(),
+                            _stream_handle(stream, x.device))
+    if st != SGEMM_OK:
+        raise SgemmError(st, "sgemm_read_probe")
+    return partial
 
 
 def gemm_noalloc_raw(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0,

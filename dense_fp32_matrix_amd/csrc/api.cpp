@@ -943,6 +943,13 @@ sgemm_status sgemm_tile_info(int32_t path, int32_t tile, int32_t* count, int32_t
     return SGEMM_OK;
 }
 
+sgemm_status sgemm_read_probe(const float* x, int64_t n, float* partial, hipStream_t stream) {
+    static_assert(kReadGrid == SGEMM_READ_PROBE_PARTIALS, "the header states the probe's partial count");
+    if (n < 0 || n % 4 != 0 || partial == nullptr || (n > 0 && x == nullptr) || !aligned(x, 16))
+        return SGEMM_ERR_INVALID_ARG;
+    return launch_read_probe(x, n, partial, stream) == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
+}
+
 const char* sgemm_status_string(sgemm_status s) {
     switch (s) {
         case SGEMM_OK: return "SGEMM_OK";

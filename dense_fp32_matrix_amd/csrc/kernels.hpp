@@ -110,6 +110,10 @@ hipError_t launch_streamk_fixup(const GemmArgs& g, int bm, int bn, int sk_tiles,
 // C[i][j] = +0.0 for i < M, j < N (the empty sum, K == 0).
 // C = beta * C (C not read when beta == 0): the whole product when alpha == 0 or K == 0.
 hipError_t launch_scale(float* C, int64_t ldc, int32_t M, int32_t N, float beta, hipStream_t stream);
+// The read-rate probe: reads x[0 .. n) once (n % 4 == 0, x 16-byte aligned)
+// and writes kReadGrid per-workgroup sums to partial.
+constexpr int kReadGrid = 1024;
+hipError_t launch_read_probe(const float* x, int64_t n, float* partial, hipStream_t stream);
 
 // dst (rows_p x cols_p, leading dimension ldd >= cols_p, both multiples of 4,
 // 16-byte aligned) = src (rows x cols, leading dimension ld) zero-padded.

@@ -1,6 +1,6 @@
 // Small kernels: the one-thread-per-output product, the split-K reduction,
-// the stream-K fix-up, operand packing and the C = beta * C scaling used
-// when alpha == 0 or K == 0.
+// the stream-K fix-up, operand packing, the C = beta * C scaling used when
+// alpha == 0 or K == 0, and the read-rate probe.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -174,6 +174,38 @@ void streamk_fixup_kernel(GemmArgs g, int bm, int bn) {
     }
 }
 
+// Read-rate probe, the yardstick of the streaming (skinny) path: the rate
+// at which the chip reads a buffer it uses once, measured rather than taken
+// from the data sheet (the "realistic machine model" of the GEMV example in
+// "如何让计算受限问题真正达到计算受限", section 7).  x[0 .. 4 n4) is read once
+// with 16-byte loads, grid-stride in 16-byte groups (a wave's load covers
+// 1 KB), kReadU loads in flight per lane; each workgroup writes its sum to
+// partial[blockIdx.x], so no load is dead.  kReadGrid workgroups (4 per CU)
+// and 4 loads in flight measured the fastest of 1024-4096 workgroups and
+// 4-8 loads on a 180 MB buffer, warm and after a flush.
+constexpr int kReadU = 4;
+
+__global__ __launch_bounds__(256)
+void read_probe_kernel(const f32x4* __restrict__ x, int64_t n4, float* __restrict__ partial) {
+    __shared__ float red[4];
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (; i + (kReadU - 1) * stride < n4; i += kReadU * stride) {
+        f32x4 v[kReadU];
+#pragma unroll
+        for (int u = 0; u < kReadU; ++u) v[u] = x[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kReadU; ++u) acc += v[u];
+    }
+    for (; i < n4; i += stride) acc += x[i];
+    float s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_down(s, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) partial[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 unsigned grid_for(int64_t items, int64_t per_block) {
     int64_t blocks = (items + per_block - 1) / per_block;
     if (blocks > 256 * 16) blocks = 256 * 16;   // grid-stride beyond 16 workgroups per CU
@@ -226,6 +258,13 @@ hipError_t launch_pack(const float* src, int64_t ld, int32_t rows, int32_t cols,
 
 hipError_t launch_scale(float* C, int64_t ldc, int32_t M, int32_t N, float beta, hipStream_t stream) {
     hipLaunchKernelGGL(scale_kernel, dim3(grid_for((int64_t)M * N, 256)), dim3(256), 0, stream, C, ldc, M, N, beta);
+    return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const float* x, int64_t n, float* partial, hipStream_t stream) {
+    if (n < 0 || n % 4 != 0 || reinterpret_cast<uintptr_t>(x) % 16 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(read_probe_kernel, dim3(kReadGrid), dim3(256), 0, stream, reinterpret_cast<const f32x4*>(x),
+                       n / 4, partial);
     return hipGetLastError();
 }
 

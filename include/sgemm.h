@@ -270,6 +270,19 @@ size_t sgemm_workspace_size(int64_t M, int64_t N, int64_t K,
 sgemm_status sgemm_tile_info(int32_t path, int32_t tile, int32_t* count,
                              int32_t* bm, int32_t* bn, int32_t* bk, int32_t* threads);
 
+/* Measurement helper, outside the product path: reads the n floats at x
+ * once and writes SGEMM_READ_PROBE_PARTIALS per-workgroup sums to partial,
+ * enqueued on `stream`.  Timing it gives the rate at which the chip streams
+ * a buffer it reads once -- the measured machine model against which a
+ * bandwidth-bound product (the skinny path, which reads B once) is judged,
+ * as the GEMV example of "如何让计算受限问题真正达到计算受限", section 7,
+ * weighs a kernel against the attainable, not the data-sheet, bandwidth.
+ * x: device, 16-byte aligned, n >= 0 and a multiple of 4 (SGEMM_ERR_INVALID_ARG
+ * otherwise, nothing enqueued); partial: device, SGEMM_READ_PROBE_PARTIALS
+ * floats, caller-owned.  Nothing is allocated. */
+#define SGEMM_READ_PROBE_PARTIALS 1024
+sgemm_status sgemm_read_probe(const float* x, int64_t n, float* partial, hipStream_t stream);
+
 /* Static string naming a status code. */
 const char* sgemm_status_string(sgemm_status status);
 

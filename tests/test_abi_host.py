@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"sgemm", "sgemm_ex", "sgemm_plan_query", "sgemm_workspace_size", "sgemm_tile_info",
-            "sgemm_status_string", "sgemm_version"} <= set(names)
+            "sgemm_status_string", "sgemm_version", "sgemm_read_probe"} <= set(names)
     so = ctypes.CDLL(lib.library_path())
     for n in names:
         assert hasattr(so, n), n
@@ -387,3 +387,16 @@ def test_noalloc_checks_run_before_any_hip_call():
     assert "static buffer" in lib.sgemm_status_string(5)
     # empty products enqueue nothing and need no device
     assert lib.gemm_noalloc_raw(0, 0, 0, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4) == 0
+
+
+def test_read_probe_rejects_bad_arguments():
+    """The read-rate probe validates on the host before any HIP call: n a
+    multiple of 4, x 16-byte aligned, a partial buffer given."""
+    so = lib.load_library()
+    assert lib.READ_PROBE_PARTIALS == 1024
+    assert lib.read_probe_raw(0x1000, 6, 0x2000) == 1          # n % 4
+    assert lib.read_probe_raw(0x1004, 8, 0x2000) == 1          # misaligned x
+    assert lib.read_probe_raw(0x1000, -4, 0x2000) == 1         # negative n
+    assert lib.read_probe_raw(0x1000, 8, None) == 1            # no partial buffer
+    assert lib.read_probe_raw(None, 8, 0x2000) == 1            # no x
+    assert so.sgemm_read_probe is not None

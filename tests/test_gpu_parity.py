@@ -596,3 +596,19 @@ def test_full_size_skinny_stream_k(oracle_mod, kind):
 def test_full_size_workload_integer(oracle_mod, name):
     w = workloads.CONFIGS[name]
     _full_size_check(oracle_mod, w, "integer")
+
+
+@pytest.mark.parametrize("n", [0, 4, 1 << 20, (1 << 20) + 4 * 1021, 3 * 1024 * 1024 + 8])
+def test_read_probe(n):
+    """The read-rate probe reads every element once: on small integers its
+    per-workgroup sums are exact, and together they give the buffer's sum
+    (ragged tails past the grid stride and past the unrolled loads
+    included)."""
+    say(f"read probe n={n}")
+    g = torch.Generator().manual_seed(n + 3)
+    x = torch.randint(0, 3, (n,), generator=g, dtype=torch.int32).to(torch.float32)
+    part = lib.read_probe(x.to(DEV))
+    torch.cuda.synchronize()
+    p = part.cpu().to(torch.float64)
+    assert part.numel() == lib.READ_PROBE_PARTIALS
+    assert torch.equal(p, p.round()) and int(p.sum().item()) == int(x.to(torch.int64).sum().item())
