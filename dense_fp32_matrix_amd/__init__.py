@@ -6,6 +6,10 @@ gfx950 kernels.  The functions carry the C interface's names
 (``include/sgemm.h``); tensors are torch CUDA (HIP) float32 matrices with unit
 column stride, and the row stride is passed as the leading dimension.  If the
 library has not been built, every call raises; there is no fallback.
+
+SGEMM_LIBRARY, when set, names the library file to load instead of the
+in-tree ``libsgemm.so`` -- used to run the same tests on the LDS-poison build
+(``libsgemm_ldspoison.so``, see ``build.py``).
 """
 from __future__ import annotations
 
@@ -22,7 +26,7 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libsgemm.so")
+_LIB_PATH = os.environ.get("SGEMM_LIBRARY") or os.path.join(_HERE, "libsgemm.so")
 _lib = None
 
 PATHS = {"auto": 0, "naive": 1, "valu": 2, "mfma": 3, "skinny": 4}

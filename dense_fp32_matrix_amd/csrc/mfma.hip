@@ -262,6 +262,26 @@ __device__ __forceinline__ void dma_lanes(const float* src, const float* lds) {
         asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(base));
 }
 
+// Race check (built with SGEMM_LDS_POISON=1, never in the product library):
+// before each refill of a stage, every wave writes NaN into exactly the LDS
+// bytes its own direct loads of that refill will fill, and waits for those
+// writes, so that the loads land on top of them.  A wave that still read the
+// stage after the barrier that freed it, or read a refill before its loads
+// had landed, would see NaN, which the parity tests catch.
+#ifndef SGEMM_LDS_POISON
+#define SGEMM_LDS_POISON 0
+#endif
+constexpr bool kLdsPoison = SGEMM_LDS_POISON != 0;
+
+template <int W>
+__device__ __forceinline__ void poison_lanes(float* lds, int lane) {
+    const float nan = __builtin_nanf("");
+    if constexpr (W == 4)
+        *reinterpret_cast<f32x4*>(lds + 4 * lane) = f32x4{nan, nan, nan, nan};
+    else
+        lds[lane] = nan;
+}
+
 template <int BM, int BN, int BK, int WGM, int WGN, int DS, int W, int OPS, bool PRIO>
 __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, float* st1, float* st2, float* st3,
                                               int tm, int tn, int kb, int ke, const TileOut& o) {
@@ -300,6 +320,13 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
     auto issue = [&](int step, float* st, auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
         const int k0 = kb + step * BK;
+        if constexpr (kLdsPoison) {
+#pragma unroll
+            for (int i = 0; i < A_PER; ++i) poison_lanes<W>(st + LA::dst(i * WAVES + wave), lane);
+#pragma unroll
+            for (int i = 0; i < B_PER; ++i) poison_lanes<W>(st + LA::FLOATS + LB::dst(i * WAVES + wave), lane);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
 #pragma unroll
         for (int i = 0; i < A_PER; ++i)
             dma_lanes<W>(FULL ? la.ptr[i] : la.checked(i, k0, ke), st + LA::dst(i * WAVES + wave));
