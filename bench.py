@@ -318,6 +318,26 @@ def main():
     if probe is not None:
         probe["call_vs_read_warm"] = probe["warm_ms"] / kernel_ms
         roof["read_probe"] = probe
+    if roof["bound"] == "alu":
+        # the VALU path's ceiling measured, beside the data-sheet figure: the
+        # library's FMA-rate probe (scalar v_fmac_f32, 16 chains per lane,
+        # 32 workgroups per CU)
+        fma_wgs, fma_iters = 8192, 1000
+        fma_out = torch.empty(fma_wgs * 256, dtype=torch.float32, device=dev)
+        lib.fma_probe(fma_iters, fma_wgs, fma_out)
+        fts = []
+        for _ in range(5):
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            lib.fma_probe(fma_iters, fma_wgs, fma_out)
+            s1.record(stream)
+            torch.cuda.synchronize()
+            fts.append(s0.elapsed_time(s1))
+        fma_flops = 2.0 * fma_wgs * 256 * fma_iters * lib.FMA_PROBE_FMAS_PER_ITER
+        ceiling = fma_flops / (statistics.median(fts) * 1e-3) / 1e12
+        roof["fma_probe"] = {"what": "sgemm_fma_probe: scalar FP32 FMA rate, 8192 x 256 lanes x 128000 FMAs",
+                             "tflops": ceiling, "frac_of_probe": achieved / ceiling}
 
     cpu = None
     cpu_small = None

@@ -22,6 +22,7 @@ __all__ = [
     "sgemm", "sgemm_ex", "sgemm_raw", "sgemm_plan_query", "sgemm_workspace_size",
     "gemm", "gemm_raw", "gemm_plan_query", "gemm_workspace_size", "gemm_noalloc", "gemm_noalloc_raw",
     "NOALLOC_SCRATCH_BYTES", "read_probe", "read_probe_raw", "READ_PROBE_PARTIALS",
+    "fma_probe", "FMA_PROBE_FMAS_PER_ITER",
     "sgemm_tile_info", "sgemm_status_string", "sgemm_version", "library_path", "load_library",
 ]
 
@@ -103,6 +104,8 @@ def load_library():
     lib.sgemm_tile_info.restype = ctypes.c_int
     lib.sgemm_status_string.argtypes = [ctypes.c_int]
     lib.sgemm_status_string.restype = ctypes.c_char_p
+    lib.sgemm_fma_probe.argtypes = [i32, i32, p, p]
+    lib.sgemm_fma_probe.restype = ctypes.c_int
     lib.sgemm_read_probe.argtypes = [p, i64, p, p]
     lib.sgemm_read_probe.restype = ctypes.c_int
     lib.sgemm_version.argtypes = []
@@ -307,6 +310,28 @@ def read_probe(x, partial=None, stream=None):
     if st != SGEMM_OK:
         raise SgemmError(st, "sgemm_read_probe")
     return partial
+
+
+FMA_PROBE_FMAS_PER_ITER = 128
+
+
+def fma_probe(iters, workgroups, out=None, stream=None):
+    """The FMA-rate probe on the current device: workgroups x 256 lanes, each
+    FMA_PROBE_FMAS_PER_ITER x iters scalar FP32 FMAs.  Returns the per-lane
+    results (workgroups x 256 floats)."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device())
+    if out is None:
+        out = torch.empty(int(workgroups) * 256, dtype=torch.float32, device=dev)
+    if (out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous()
+            or out.numel() < int(workgroups) * 256):
+        raise ValueError("out must be a contiguous float32 GPU tensor of workgroups x 256 floats")
+    with torch.cuda.device(out.device):
+        st = load_library().sgemm_fma_probe(int(iters), int(workgroups), out.data_ptr(),
+                                            _stream_handle(stream, out.device))
+    if st != SGEMM_OK:
+        raise SgemmError(st, "sgemm_fma_probe")
+    return out
 
 
 def gemm_noalloc_raw(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0,

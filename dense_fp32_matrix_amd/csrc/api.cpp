@@ -950,6 +950,12 @@ sgemm_status sgemm_read_probe(const float* x, int64_t n, float* partial, hipStre
     return launch_read_probe(x, n, partial, stream) == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
 }
 
+sgemm_status sgemm_fma_probe(int32_t iters, int32_t workgroups, float* out, hipStream_t stream) {
+    static_assert(kFmaPerLanePerIter == SGEMM_FMA_PROBE_FMAS_PER_ITER, "the header states the probe's FMA count");
+    if (iters < 0 || workgroups < 1 || out == nullptr) return SGEMM_ERR_INVALID_ARG;
+    return launch_fma_probe(iters, workgroups, out, stream) == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
+}
+
 const char* sgemm_status_string(sgemm_status s) {
     switch (s) {
         case SGEMM_OK: return "SGEMM_OK";

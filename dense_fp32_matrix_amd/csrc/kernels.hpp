@@ -114,6 +114,10 @@ hipError_t launch_scale(float* C, int64_t ldc, int32_t M, int32_t N, float beta,
 // and writes kReadGrid per-workgroup sums to partial.
 constexpr int kReadGrid = 1024;
 hipError_t launch_read_probe(const float* x, int64_t n, float* partial, hipStream_t stream);
+// The FMA-rate probe: `workgroups` x 256 lanes, each 16 x 8 x iters scalar
+// FP32 FMAs; one float per lane to out.
+constexpr int kFmaPerLanePerIter = 16 * 8;
+hipError_t launch_fma_probe(int iters, int workgroups, float* out, hipStream_t stream);
 
 // dst (rows_p x cols_p, leading dimension ldd >= cols_p, both multiples of 4,
 // 16-byte aligned) = src (rows x cols, leading dimension ld) zero-padded.

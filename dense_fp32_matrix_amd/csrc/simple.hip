@@ -1,6 +1,6 @@
 // Small kernels: the one-thread-per-output product, the split-K reduction,
 // the stream-K fix-up, operand packing, the C = beta * C scaling used when
-// alpha == 0 or K == 0, and the read-rate probe.
+// alpha == 0 or K == 0, and the read-rate and FMA-rate probes.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -206,6 +206,33 @@ void read_probe_kernel(const f32x4* __restrict__ x, int64_t n4, float* __restric
     if (threadIdx.x == 0) partial[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+// FMA-rate probe, the yardstick of the VALU path: each lane runs kFmaChains
+// independent chains acc = x * y + acc of `iters` x 8 scalar FP32 FMAs
+// (v_fmac_f32; packed FP32 is off in this build, as for the VALU kernel),
+// x and y lane-dependent so nothing folds, and writes the chains' sum, so no
+// FMA is dead.  With kFmaChains chains per lane and several waves per SIMD,
+// issue, not the FMA latency, is the limit.
+constexpr int kFmaChains = 16;
+
+__global__ __launch_bounds__(256)
+void fma_probe_kernel(int iters, float* __restrict__ out) {
+    const float x = 1.0f + 1e-7f * (float)threadIdx.x;
+    const float y = 1.0f - 1e-7f * (float)blockIdx.x;
+    float acc[kFmaChains];
+#pragma unroll
+    for (int c = 0; c < kFmaChains; ++c) acc[c] = (float)c;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int c = 0; c < kFmaChains; ++c) acc[c] = __builtin_fmaf(x, y, acc[c]);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < kFmaChains; ++c) s += acc[c];
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 unsigned grid_for(int64_t items, int64_t per_block) {
     int64_t blocks = (items + per_block - 1) / per_block;
     if (blocks > 256 * 16) blocks = 256 * 16;   // grid-stride beyond 16 workgroups per CU
@@ -258,6 +285,12 @@ hipError_t launch_pack(const float* src, int64_t ld, int32_t rows, int32_t cols,
 
 hipError_t launch_scale(float* C, int64_t ldc, int32_t M, int32_t N, float beta, hipStream_t stream) {
     hipLaunchKernelGGL(scale_kernel, dim3(grid_for((int64_t)M * N, 256)), dim3(256), 0, stream, C, ldc, M, N, beta);
+    return hipGetLastError();
+}
+
+hipError_t launch_fma_probe(int iters, int workgroups, float* out, hipStream_t stream) {
+    if (iters < 0 || workgroups < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fma_probe_kernel, dim3((unsigned)workgroups), dim3(256), 0, stream, iters, out);
     return hipGetLastError();
 }
 

@@ -283,6 +283,18 @@ sgemm_status sgemm_tile_info(int32_t path, int32_t tile, int32_t* count,
 #define SGEMM_READ_PROBE_PARTIALS 1024
 sgemm_status sgemm_read_probe(const float* x, int64_t n, float* partial, hipStream_t stream);
 
+/* Measurement helper, outside the product path: the rate of scalar FP32
+ * fused multiply-adds (v_fmac_f32, no packed FP32), the ceiling of the VALU
+ * path's rank-1 updates ("GEMM from naive to tiled", section 五: the inner
+ * loop is nothing but such FMAs).  Enqueues `workgroups` x 256 lanes, each
+ * running 16 independent chains of SGEMM_FMA_PROBE_FMAS_PER_ITER x iters
+ * FMAs in total, and writing one float per lane to out (device, caller-owned,
+ * workgroups x 256 floats).  FLOPs = 2 x 256 x workgroups x iters x
+ * SGEMM_FMA_PROBE_FMAS_PER_ITER.  SGEMM_ERR_INVALID_ARG for iters < 0,
+ * workgroups < 1 or a null out; nothing is allocated. */
+#define SGEMM_FMA_PROBE_FMAS_PER_ITER 128
+sgemm_status sgemm_fma_probe(int32_t iters, int32_t workgroups, float* out, hipStream_t stream);
+
 /* Static string naming a status code. */
 const char* sgemm_status_string(sgemm_status status);
 

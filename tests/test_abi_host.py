@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"sgemm", "sgemm_ex", "sgemm_plan_query", "sgemm_workspace_size", "sgemm_tile_info",
-            "sgemm_status_string", "sgemm_version", "sgemm_read_probe"} <= set(names)
+            "sgemm_status_string", "sgemm_version", "sgemm_read_probe", "sgemm_fma_probe"} <= set(names)
     so = ctypes.CDLL(lib.library_path())
     for n in names:
         assert hasattr(so, n), n
@@ -400,3 +400,11 @@ def test_read_probe_rejects_bad_arguments():
     assert lib.read_probe_raw(0x1000, 8, None) == 1            # no partial buffer
     assert lib.read_probe_raw(None, 8, 0x2000) == 1            # no x
     assert so.sgemm_read_probe is not None
+
+
+def test_fma_probe_rejects_bad_arguments():
+    so = lib.load_library()
+    assert lib.FMA_PROBE_FMAS_PER_ITER == 128
+    assert so.sgemm_fma_probe(-1, 4, 0x1000, None) == 1
+    assert so.sgemm_fma_probe(4, 0, 0x1000, None) == 1
+    assert so.sgemm_fma_probe(4, 4, None, None) == 1

@@ -612,3 +612,20 @@ def test_read_probe(n):
     p = part.cpu().to(torch.float64)
     assert part.numel() == lib.READ_PROBE_PARTIALS
     assert torch.equal(p, p.round()) and int(p.sum().item()) == int(x.to(torch.int64).sum().item())
+
+
+def test_fma_probe_values():
+    """The FMA-rate probe computes what it claims: with no iterations each lane
+    holds the sum of its chains' starting values (0 + 1 + ... + 15); with i
+    iterations each of the 16 chains gained 8 i products x * y."""
+    say("fma probe")
+    out0 = lib.fma_probe(0, 2)
+    out3 = lib.fma_probe(3, 2)
+    torch.cuda.synchronize()
+    assert torch.all(out0.cpu() == 120.0)
+    lane = torch.arange(512) % 256
+    wg = torch.arange(512) // 256
+    x = (1.0 + 1e-7 * lane.double())
+    y = (1.0 - 1e-7 * wg.double())
+    expect = 120.0 + 16 * 8 * 3 * x * y
+    assert torch.allclose(out3.cpu().double(), expect, rtol=1e-5, atol=0)
