@@ -452,7 +452,7 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
                                   (pack_b ? align256((size_t)(br * round_up(bc, 32)) * sizeof(float)) : 0);
             Candidate cand;
             const bool fits = copies <= ws_cap && mfma_best(o, true, ops, M, N, kp, ws_cap - copies, &cand);
-            cand.time += bytes / kPackBw + (pack_a + pack_b) * kLaunch;
+            cand.time += bytes / kPackBw + kLaunch;
             if (fits && (o.pack == 2 || !have || cand.time < best.time)) {
                 have = true;
                 best = cand;
@@ -534,7 +534,7 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
     p.gemm_ws_off = off;
     q.workspace_bytes = gemm_ws > 0 ? off + gemm_ws : off;
     if (q.workspace_bytes > ws_cap) return SGEMM_ERR_SCRATCH_LIMIT;
-    q.launches = ((q.packed & 1) ? 1 : 0) + ((q.packed & 2) ? 1 : 0) + 1 + (p.second ? 1 : 0);
+    q.launches = (q.packed != 0 ? 1 : 0) + 1 + (p.second ? 1 : 0);   // both operands pack in one launch
     *out = p;
     return SGEMM_OK;
 }
@@ -703,20 +703,22 @@ sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_option
     int64_t lda = c.lda, ldb = c.ldb;
     char* const wsb = static_cast<char*>(ws);
     hipError_t e = hipSuccess;
+    PackJobs jobs{};
     if (q.packed & 1) {
         float* Ap = reinterpret_cast<float*>(wsb + p.pack_a_off);
-        e = launch_pack(A, lda, (int32_t)c.a_rows(), (int32_t)c.a_cols(), Ap, p.a_ld, (int32_t)p.a_rows,
-                        (int32_t)p.a_cols, stream);
+        jobs.job[jobs.count++] = PackJob{A, lda, (int32_t)c.a_rows(), (int32_t)c.a_cols(), Ap, p.a_ld,
+                                         (int32_t)p.a_rows, (int32_t)p.a_cols};
         A = Ap;
         lda = p.a_ld;
     }
-    if (e == hipSuccess && (q.packed & 2)) {
+    if (q.packed & 2) {
         float* Bp = reinterpret_cast<float*>(wsb + p.pack_b_off);
-        e = launch_pack(B, ldb, (int32_t)c.b_rows(), (int32_t)c.b_cols(), Bp, p.b_ld, (int32_t)p.b_rows,
-                        (int32_t)p.b_cols, stream);
+        jobs.job[jobs.count++] = PackJob{B, ldb, (int32_t)c.b_rows(), (int32_t)c.b_cols(), Bp, p.b_ld,
+                                         (int32_t)p.b_rows, (int32_t)p.b_cols};
         B = Bp;
         ldb = p.b_ld;
     }
+    if (jobs.count > 0) e = launch_pack(jobs, stream);
     void* const gws = q.workspace_bytes > p.gemm_ws_off ? static_cast<void*>(wsb + p.gemm_ws_off) : nullptr;
 
     GemmArgs g;

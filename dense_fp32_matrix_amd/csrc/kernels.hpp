@@ -121,8 +121,21 @@ hipError_t launch_fma_probe(int iters, int workgroups, float* out, hipStream_t s
 
 // dst (rows_p x cols_p, leading dimension ldd >= cols_p, both multiples of 4,
 // 16-byte aligned) = src (rows x cols, leading dimension ld) zero-padded.
-hipError_t launch_pack(const float* src, int64_t ld, int32_t rows, int32_t cols, float* dst, int64_t ldd,
-                       int32_t rows_p, int32_t cols_p, hipStream_t stream);
+// One operand to pack: rows x cols at src (leading dimension ld) into the
+// zero-padded rows_p x cols_p copy at dst (leading dimension ldd).
+struct PackJob {
+    const float* src;
+    int64_t ld;
+    int32_t rows, cols;
+    float* dst;
+    int64_t ldd;
+    int32_t rows_p, cols_p;
+};
+struct PackJobs {
+    PackJob job[2];
+    int32_t count;   // 1 or 2, packed in one launch
+};
+hipError_t launch_pack(const PackJobs& jobs, hipStream_t stream);
 
 // Sixteen zero bytes in device memory, defined once per kernel source.  A
 // masked-off load (outside the matrix, or past the end of a K slice) reads

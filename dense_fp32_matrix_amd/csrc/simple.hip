@@ -85,24 +85,25 @@ void scale_kernel(float* __restrict__ C, int64_t ldc, int32_t M, int32_t N, floa
 // from cols_p to ldd are left alone, nothing reads them), with zeros in the
 // padding rows and columns.  The copy is exact, and the zeros only add +0
 // terms to the product, so the matrix kernel's 16-byte loaders can then run
-// on operands that were not aligned.  One thread writes one 16-byte group of
-// a row; blockIdx.y strides over the rows.
+// on operands that were not aligned.  One launch packs both operands when
+// both need it (blockIdx.z picks the job).  One thread writes one 16-byte
+// group of a row; blockIdx.y strides over the rows.
 __global__ __launch_bounds__(256)
-void pack_kernel(const float* __restrict__ src, int64_t ld, int32_t rows, int32_t cols,
-                 float* __restrict__ dst, int64_t ldd, int32_t rows_p, int32_t cols_p) {
+void pack_kernel(PackJobs jobs) {
+    const PackJob& j = jobs.job[blockIdx.z];
     const int32_t c4 = (int32_t)blockIdx.x * 256 + (int32_t)threadIdx.x;
-    if (4 * c4 >= cols_p) return;
-    for (int32_t r = blockIdx.y; r < rows_p; r += gridDim.y) {
+    if (4 * c4 >= j.cols_p) return;
+    for (int32_t r = blockIdx.y; r < j.rows_p; r += gridDim.y) {
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < rows) {
-            const float* s = src + (int64_t)r * ld + 4 * c4;
-            const int32_t left = cols - 4 * c4;
+        if (r < j.rows) {
+            const float* s = j.src + (int64_t)r * j.ld + 4 * c4;
+            const int32_t left = j.cols - 4 * c4;
             if (left > 0) v.x = s[0];
             if (left > 1) v.y = s[1];
             if (left > 2) v.z = s[2];
             if (left > 3) v.w = s[3];
         }
-        *reinterpret_cast<float4*>(dst + (int64_t)r * ldd + 4 * c4) = v;
+        *reinterpret_cast<float4*>(j.dst + (int64_t)r * j.ldd + 4 * c4) = v;
     }
 }
 
@@ -274,12 +275,18 @@ hipError_t launch_streamk_fixup(const GemmArgs& g, int bm, int bn, int sk_tiles,
     return hipGetLastError();
 }
 
-hipError_t launch_pack(const float* src, int64_t ld, int32_t rows, int32_t cols, float* dst, int64_t ldd,
-                       int32_t rows_p, int32_t cols_p, hipStream_t stream) {
-    if (ldd < cols_p || ldd % 4 != 0 || cols_p % 4 != 0) return hipErrorInvalidValue;
+hipError_t launch_pack(const PackJobs& jobs, hipStream_t stream) {
+    if (jobs.count < 1 || jobs.count > 2) return hipErrorInvalidValue;
+    int32_t cols_p = 0, rows_p = 0;
+    for (int i = 0; i < jobs.count; ++i) {
+        const PackJob& j = jobs.job[i];
+        if (j.ldd < j.cols_p || j.ldd % 4 != 0 || j.cols_p % 4 != 0) return hipErrorInvalidValue;
+        cols_p = std::max(cols_p, j.cols_p);
+        rows_p = std::max(rows_p, j.rows_p);
+    }
     const unsigned gx = (unsigned)((cols_p / 4 + 255) / 256);
-    const unsigned gy = (unsigned)std::min<int32_t>(rows_p, 65535);
-    hipLaunchKernelGGL(pack_kernel, dim3(gx, gy), dim3(256), 0, stream, src, ld, rows, cols, dst, ldd, rows_p, cols_p);
+    const unsigned gy = (unsigned)std::min<int32_t>(std::max<int32_t>(rows_p, 1), 65535);
+    hipLaunchKernelGGL(pack_kernel, dim3(gx, gy, (unsigned)jobs.count), dim3(256), 0, stream, jobs);
     return hipGetLastError();
 }
 

@@ -164,8 +164,9 @@ typedef struct sgemm_plan {
     int64_t k_chunk;         /* K elements per slice */
     int64_t workgroups;      /* workgroups of the main kernel */
     size_t workspace_bytes;  /* split-K / stream-K scratch (0 if none) */
-    int32_t launches;        /* kernels enqueued by the call (0 to 4: packing copies, the matrix
-                                kernel, a split-K reduction or stream-K fix-up) */
+    int32_t launches;        /* kernels enqueued by the call (0 to 3: one packing copy of the
+                                misaligned operands, the matrix kernel, a split-K reduction or
+                                stream-K fix-up) */
     int32_t decomposition;   /* sgemm_decomposition actually used */
     int64_t dp_tiles;        /* stream-K: tiles computed whole first */
     int64_t sk_tiles;        /* stream-K: tiles whose K-steps are shared out */

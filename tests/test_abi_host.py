@@ -213,7 +213,7 @@ def test_vector_loader_selection():
 
 def test_packing_plans():
     """Packed operands: which ones, K padded to a multiple of 4, the copies
-    at the front of the workspace, one launch per packed operand."""
+    at the front of the workspace, one packing launch for both operands."""
     M, N, K = 4097, 3001, 2049
     p = lib.sgemm_plan_query(M, N, K, lda=K, ldb=N, ldc=N, path="mfma", tile=0, decomposition="tiles",
                              split_k=1, pack="always")
@@ -221,7 +221,7 @@ def test_packing_plans():
     # copies with rows padded to 128 bytes: A 4097 x 2080, B 2052 x 3008
     r256 = lambda b: (b + 255) // 256 * 256
     assert p["workspace_bytes"] == r256(M * 2080 * 4) + r256(2052 * 3008 * 4)
-    assert p["launches"] == 3
+    assert p["launches"] == 2
     # only B misaligned (N odd, K a multiple of 4): A is read in place
     q = lib.sgemm_plan_query(512, 509, 512, path="mfma", tile=0, decomposition="tiles", split_k=1,
                              pack="always")
@@ -256,7 +256,7 @@ def test_default_plans_fill_the_chip():
         assert p["k_chunk"] * (p["split_k"] - 1) < Kg
         if p["split_k"] > 1:
             assert p["workspace_bytes"] >= p["split_k"] * M * N * 4
-            assert p["launches"] == 2 + bin(p["packed"]).count("1")
+            assert p["launches"] == 2 + (p["packed"] != 0)
         assert lib.sgemm_workspace_size(M, N, K) == p["workspace_bytes"]
     assert lib.sgemm_plan_query(16, 11008, 4096)["path_name"] == "skinny"
     p32 = lib.sgemm_plan_query(32, 11008, 4096)
