@@ -378,6 +378,7 @@ def main():
                    "bm": plan["bm"], "bn": plan["bn"], "bk": plan["bk"], "split_k": plan["split_k"],
                    "decomposition": plan["decomposition_name"],
                    "vector_loads": bool(plan["vector"]), "packed": plan["packed"], "workgroups": plan["workgroups"],
+                   "tail_rows": plan["tail_rows"],
                    "tile_order": args.tile_order},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -18,7 +18,7 @@ import os
 from typing import Optional
 
 __all__ = [
-    "SgemmError", "PATHS", "DECOMPOSITIONS", "PACK", "TILE_ORDERS",
+    "SgemmError", "PATHS", "DECOMPOSITIONS", "PACK", "TILE_ORDERS", "ROW_TAILS",
     "sgemm", "sgemm_ex", "sgemm_raw", "sgemm_plan_query", "sgemm_workspace_size",
     "gemm", "gemm_raw", "gemm_plan_query", "gemm_workspace_size", "gemm_noalloc", "gemm_noalloc_raw",
     "NOALLOC_SCRATCH_BYTES", "read_probe", "read_probe_raw", "READ_PROBE_PARTIALS",
@@ -52,7 +52,8 @@ _DECOMP_NAMES = {v: k for k, v in DECOMPOSITIONS.items()}
 class _Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("tile", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("vector", ctypes.c_int32), ("decomposition", ctypes.c_int32), ("pack", ctypes.c_int32),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("tile_order", ctypes.c_int32)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("tile_order", ctypes.c_int32),
+                ("row_tail", ctypes.c_int32)]
 
 
 class _Plan(ctypes.Structure):
@@ -62,7 +63,8 @@ class _Plan(ctypes.Structure):
                 ("tiles_n", ctypes.c_int64), ("k_chunk", ctypes.c_int64), ("workgroups", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_size_t), ("launches", ctypes.c_int32),
                 ("decomposition", ctypes.c_int32), ("dp_tiles", ctypes.c_int64), ("sk_tiles", ctypes.c_int64),
-                ("sk_units_per_wg", ctypes.c_int64), ("packed", ctypes.c_int32), ("k_padded", ctypes.c_int32)]
+                ("sk_units_per_wg", ctypes.c_int64), ("packed", ctypes.c_int32), ("k_padded", ctypes.c_int32),
+                ("tail_rows", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -120,9 +122,13 @@ PACK = {"auto": 0, "never": 1, "always": 2}
 TILE_ORDERS = {"xcd": 0, "plain": 1}
 
 
+ROW_TAILS = {"auto": 0, "never": 1, "always": 2}
+
+
 def _options(path="auto", tile=-1, split_k=0, vector=0, decomposition="auto", workspace=None,
-             workspace_bytes=0, pack="auto", tile_order="xcd") -> _Options:
+             workspace_bytes=0, pack="auto", tile_order="xcd", row_tail="auto") -> _Options:
     o = _Options()
+    o.row_tail = ROW_TAILS[row_tail] if isinstance(row_tail, str) else int(row_tail)
     o.tile_order = TILE_ORDERS[tile_order] if isinstance(tile_order, str) else int(tile_order)
     o.pack = PACK[pack] if isinstance(pack, str) else int(pack)
     o.path = PATHS[path] if isinstance(path, str) else int(path)
@@ -223,13 +229,13 @@ def sgemm(A, B, C=None, stream=None):
 
 
 def sgemm_ex(A, B, C=None, stream=None, *, path="auto", tile=-1, split_k=0, vector=0, decomposition="auto",
-             workspace=None, pack="auto", tile_order="xcd"):
+             workspace=None, pack="auto", tile_order="xcd", row_tail="auto"):
     """``sgemm`` with explicit options: ``path`` in PATHS, ``tile`` index, ``split_k``
     slices, ``vector=1`` to force 4-byte loads, ``decomposition`` in DECOMPOSITIONS,
     ``pack`` in PACK (aligned copies of misaligned operands), optional ``workspace``
-    tensor, ``tile_order`` in TILE_ORDERS."""
+    tensor, ``tile_order`` in TILE_ORDERS, ``row_tail`` in ROW_TAILS."""
     return _call(A, B, C, stream, _options(path, tile, split_k, vector, decomposition, workspace, pack=pack,
-                                           tile_order=tile_order))
+                                           tile_order=tile_order, row_tail=row_tail))
 
 
 def gemm_raw(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0,

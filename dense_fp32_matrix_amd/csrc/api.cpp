@@ -48,6 +48,16 @@ bool extent_ok(int64_t rows, int64_t cols, int64_t ld) {
     return (rows - 1) <= (lim - cols) / ld;
 }
 
+// One way to run a product (or its row tail): tile, decomposition, slices,
+// stream-K grid, and the time model's estimate.
+struct Candidate {
+    int tile = 0;
+    int decomposition = SGEMM_DECOMP_TILES;
+    int64_t splits = 1, k_chunk = 0;
+    int64_t dp_tiles = 0, sk_tiles = 0, sk_ipw = 0, k_steps = 0, grid = 0;
+    double time = 0;
+};
+
 struct Plan {
     sgemm_plan pub;
     int64_t ldw = 0;       // split-K workspace leading dimension (floats)
@@ -60,6 +70,13 @@ struct Plan {
     int64_t a_ld = 0, b_ld = 0;   // their leading dimensions: cols rounded up to 128 bytes, so that
                                   // every row starts on a cache line
     size_t pack_a_off = 0, pack_b_off = 0, gemm_ws_off = 0;
+    // row tail: rows M - tail_rows .. M - 1 computed by the skinny kernel after
+    // the main kernel has computed the rows above them
+    int64_t tail_rows = 0;
+    Candidate tail;            // its plan
+    int64_t tail_ldw = 0;      // its split-K slices' leading dimension (floats)
+    size_t tail_ws_off = 0;    // its partial products in the workspace
+    bool tail_second = false;  // a split-K reduce or stream-K fix-up follows it
 };
 
 const TileShape& tile_of(int path, int tile) {
@@ -96,6 +113,7 @@ constexpr double kStreamKBw = 1e13;          // bytes/s for stream-K partial til
                                              // by neighbouring workgroups, cache resident)
 constexpr double kLaunch = 8e-6;             // one more dependent kernel launch
 constexpr double kTileVisit = 2e-6;          // filling and draining one tile's pipeline, and its epilogue
+constexpr double kSkinnyBw = 4.3e12;         // bytes/s the skinny kernel streams B at from HBM (cold)
 
 // Share of the CU's peak one tile shape sustains when its CU is full, with
 // 16-byte (vec) or 4-byte load lanes (measured; the 256 x 256 tiles have no
@@ -128,14 +146,6 @@ double mfma_alone_efficiency(int tile, bool vec) {
 }
 
 int wgs_per_cu(const TileShape& t) { return std::max(1, t.waves_per_simd * 4 / (t.waves_m * t.waves_n)); }
-
-struct Candidate {
-    int tile = 0;
-    int decomposition = SGEMM_DECOMP_TILES;
-    int64_t splits = 1, k_chunk = 0;
-    int64_t dp_tiles = 0, sk_tiles = 0, sk_ipw = 0, k_steps = 0, grid = 0;
-    double time = 0;
-};
 
 // One tile per workgroup, K split into `splits` slices.
 Candidate tiles_candidate(int tile, bool vec, int64_t M, int64_t N, int64_t K, int64_t splits) {
@@ -322,6 +332,59 @@ bool mfma_best(const sgemm_options& o, bool vec, int ops, int64_t M, int64_t N, 
 
 constexpr double kPackBw = 3e12;   // bytes/s read + written by the pack kernel
 
+// The skinny path's plan for tile `tile` (N columns, K deep; M <= the
+// tile's bm).  The kernel streams B fastest when every CU holds one
+// workgroup from start to end.  A uniform K split into S slices of at least
+// four 64-deep steps gives tiles x S workgroups; where that fills the CUs in
+// whole rounds with at most a quarter of a round idle (64 strips x 4, 32 x 8,
+// 200 or 224 x 1) the split wins, and the slices are summed by the split-K
+// reduction.  Where no split does (172 strips: 172 or 344 workgroups; 344
+// strips), stream-K shares the (strip, K-step) units out evenly over two
+// workgroups per CU (one with two row blocks, whose A fragments and MFMAs
+// double) and the fix-up sums the shared strips.  Measured cold (B read from
+// HBM) on 18 shapes of 1-32 rows, 256-22016 columns and 4096-65536 deep, the
+// rule picks the fastest plan or one within 3 %, except 4 strips 65536 deep
+// (64 slices, 9 % behind stream-K).
+Candidate skinny_candidate(const sgemm_options& o, int tile, int64_t N, int64_t K) {
+    Candidate best;
+    best.tile = tile;
+    const TileShape& t = kSkinnyTiles[tile];
+    const int64_t tiles = cdiv(N, t.bn);
+    int64_t splits = 1;
+    if (o.split_k > 0) {
+        splits = o.split_k;
+    } else {
+        splits = std::max<int64_t>(1, kNumCUs / tiles);
+        splits = std::min<int64_t>(splits, std::max<int64_t>(1, K / (4 * t.bk)));
+    }
+    splits = std::min<int64_t>(splits, cdiv(K, t.bk));
+    const int64_t k_chunk = round_up(cdiv(K, splits), t.bk);
+    best.splits = cdiv(K, k_chunk);
+    best.k_chunk = k_chunk;
+    const int64_t wgs = tiles * best.splits;
+    const bool whole_rounds = 4 * wgs >= 3 * round_up(wgs, kNumCUs);
+    // stream-K units are the kernel's 64-deep K-steps
+    const bool sk_ok = o.split_k <= 1 && o.decomposition != SGEMM_DECOMP_TILES;
+    if (sk_ok && (o.decomposition == SGEMM_DECOMP_STREAM_K || !whole_rounds)) {
+        const int64_t k_steps = cdiv(K, 64);
+        const int64_t units = tiles * k_steps;
+        best.decomposition = SGEMM_DECOMP_STREAM_K;
+        best.splits = 1;
+        best.k_chunk = K;
+        best.grid = std::min<int64_t>(kNumCUs * (t.bm > 16 ? 1 : 2), units);
+        best.k_steps = k_steps;
+        best.sk_tiles = tiles;
+        best.dp_tiles = 0;
+        best.sk_ipw = cdiv(units, best.grid);
+    }
+    // time: B (and the few rows of A and C) streamed at the cold rate the
+    // kernel measured, plus the reduction or fix-up launch
+    best.time = 4.0 * ((double)K * N + (double)t.bm * (K + N)) / kSkinnyBw +
+                ((best.splits > 1 || best.decomposition == SGEMM_DECOMP_STREAM_K) ? kLaunch : 0.0);
+    return best;
+}
+
+
 // ws_cap: the most scratch the plan may use (the static buffer of
 // sgemm_gemm_noalloc; SIZE_MAX otherwise).
 sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t ws_cap, Plan* out) {
@@ -334,6 +397,7 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
     if (o.decomposition < SGEMM_DECOMP_AUTO || o.decomposition > SGEMM_DECOMP_STREAM_K) return SGEMM_ERR_INVALID_ARG;
     if (o.pack < 0 || o.pack > 2) return SGEMM_ERR_INVALID_ARG;
     if (o.tile_order < 0 || o.tile_order > 1) return SGEMM_ERR_INVALID_ARG;
+    if (o.row_tail < 0 || o.row_tail > 2) return SGEMM_ERR_INVALID_ARG;
     if (o.workspace != nullptr && !aligned(o.workspace, 256)) return SGEMM_ERR_INVALID_ARG;
     const int64_t M = c.M, N = c.N, K = c.K;
     const bool trans = c.ta || c.tb;
@@ -380,54 +444,15 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
         return SGEMM_ERR_INVALID_ARG;
 
     Candidate best;
+    size_t copies_bytes = 0;     // packed copies of the chosen MFMA plan
+    double best_pack_time = 0;   // and their cost in the time model
     if (path == SGEMM_PATH_NAIVE) {
         best.tile = 0;
         best.k_chunk = K;
     } else if (path == SGEMM_PATH_SKINNY) {
-        // The kernel streams B fastest when every CU holds one workgroup from
-        // start to end.  A uniform K split into S slices of at least four
-        // 64-deep steps gives tiles x S workgroups; where that fills the CUs
-        // in whole rounds with at most a quarter of a round idle (64 strips x
-        // 4, 32 x 8, 200 or 224 x 1) the split wins, and the slices are
-        // summed by the split-K reduction.  Where no split does (172 strips:
-        // 172 or 344 workgroups; 344 strips), stream-K shares the (strip,
-        // K-step) units out evenly over two workgroups per CU (one with two
-        // row blocks, whose A fragments and MFMAs double) and the fix-up sums
-        // the shared strips.  Measured cold (B read from HBM) on 18 shapes of
-        // 1-32 rows, 256-22016 columns and 4096-65536 deep, the rule picks
-        // the fastest plan or one within 3 %, except 4 strips 65536 deep (64
-        // slices, 9 % behind stream-K).
         best.tile = o.tile >= 0 ? o.tile : (M <= 16 ? 0 : 1);
-        const TileShape& t = kSkinnyTiles[best.tile];
-        if (M > t.bm) return SGEMM_ERR_INVALID_ARG;     // the tile holds at most bm rows of A
-        const int64_t tiles = cdiv(N, t.bn);
-        int64_t splits = 1;
-        if (o.split_k > 0) {
-            splits = o.split_k;
-        } else {
-            splits = std::max<int64_t>(1, kNumCUs / tiles);
-            splits = std::min<int64_t>(splits, std::max<int64_t>(1, K / (4 * t.bk)));
-        }
-        splits = std::min<int64_t>(splits, cdiv(K, t.bk));
-        const int64_t k_chunk = round_up(cdiv(K, splits), t.bk);
-        best.splits = cdiv(K, k_chunk);
-        best.k_chunk = k_chunk;
-        const int64_t wgs = tiles * best.splits;
-        const bool whole_rounds = 4 * wgs >= 3 * round_up(wgs, kNumCUs);
-        // stream-K units are the kernel's 64-deep K-steps
-        const bool sk_ok = o.split_k <= 1 && o.decomposition != SGEMM_DECOMP_TILES;
-        if (sk_ok && (o.decomposition == SGEMM_DECOMP_STREAM_K || !whole_rounds)) {
-            const int64_t k_steps = cdiv(K, 64);
-            const int64_t units = tiles * k_steps;
-            best.decomposition = SGEMM_DECOMP_STREAM_K;
-            best.splits = 1;
-            best.k_chunk = K;
-            best.grid = std::min<int64_t>(kNumCUs * (t.bm > 16 ? 1 : 2), units);
-            best.k_steps = k_steps;
-            best.sk_tiles = tiles;
-            best.dp_tiles = 0;
-            best.sk_ipw = cdiv(units, best.grid);
-        }
+        if (M > kSkinnyTiles[best.tile].bm) return SGEMM_ERR_INVALID_ARG;   // the tile holds at most bm rows of A
+        best = skinny_candidate(o, best.tile, N, K);
     } else if (path == SGEMM_PATH_MFMA) {
         // With 4-byte lanes only the narrow tiles are built; a forced tile
         // without them can still run on packed copies.
@@ -452,10 +477,13 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
                                   (pack_b ? align256((size_t)(br * round_up(bc, 32)) * sizeof(float)) : 0);
             Candidate cand;
             const bool fits = copies <= ws_cap && mfma_best(o, true, ops, M, N, kp, ws_cap - copies, &cand);
-            cand.time += bytes / kPackBw + kLaunch;
+            const double pack_time = bytes / kPackBw + kLaunch;
+            cand.time += pack_time;
             if (fits && (o.pack == 2 || !have || cand.time < best.time)) {
                 have = true;
                 best = cand;
+                copies_bytes = copies;
+                best_pack_time = pack_time;
                 q.vector = 1;
                 q.packed = (pack_a ? 1 : 0) | (pack_b ? 2 : 0);
                 p.kp = kp;
@@ -470,6 +498,37 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
         // otherwise every plan was left out for its scratch (a plan of one
         // tile per workgroup on unpacked operands needs none)
         if (!have) return ws_cap == SIZE_MAX ? SGEMM_ERR_INVALID_ARG : SGEMM_ERR_SCRATCH_LIMIT;
+        // Row tail.  With M a few rows (1 to 32) past a multiple of 64, the
+        // last row of tiles is mostly padding: every one of its tiles costs
+        // a full tile's multiply-adds (for M = 4097 and 128-row tiles, 24
+        // tiles for one row), and it is often what leaves a wave of tiles
+        // part-full.  Then the main kernel can take the rows above and the
+        // skinny kernel, which streams B once for up to 32 rows, the last
+        // ones.  Operands as stored (the skinny kernel's layout) only; taken
+        // when the time model prefers it (row_tail 0) or whenever possible
+        // (row_tail 2), if the scratch fits.
+        const int64_t r = M % 64;
+        if (!trans && o.row_tail != 1 && r >= 1 && r <= 32 && M - r >= 64) {
+            const int64_t kt = q.packed ? p.kp : K;
+            Candidate main_rows, tail;
+            sgemm_options to{};   // the tail's own plan: the options steer the main kernel
+            tail = skinny_candidate(to, r <= 16 ? 0 : 1, N, kt);
+            const size_t tail_ws =
+                tail.decomposition == SGEMM_DECOMP_STREAM_K
+                    ? partials_bytes(kSkinnyTiles[tail.tile], SGEMM_DECOMP_STREAM_K, 1, tail.grid, tail.sk_ipw,
+                                     tail.k_steps, r, N)
+                    : (tail.splits > 1 ? (size_t)(tail.splits * r * round_up(N, 4)) * sizeof(float) : 0);
+            const size_t room = ws_cap == SIZE_MAX ? SIZE_MAX : ws_cap - std::min(ws_cap, copies_bytes + tail_ws + 512);
+            if (copies_bytes + tail_ws + 512 <= ws_cap &&
+                mfma_best(o, q.vector != 0, ops, M - r, N, kt, room, &main_rows)) {
+                const double alt = main_rows.time + best_pack_time + tail.time + kLaunch;
+                if (o.row_tail == 2 || alt < best.time) {
+                    best = main_rows;
+                    p.tail_rows = r;
+                    p.tail = tail;
+                }
+            }
+        }
     } else {   // VALU
         best.tile = o.tile < 0 ? 0 : o.tile;
         const TileShape& t = kValuTiles[best.tile];
@@ -493,7 +552,9 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
     q.bn = t.bn;
     q.bk = t.bk;
     q.threads = path == SGEMM_PATH_NAIVE ? 256 : 64 * t.waves_m * t.waves_n;
-    q.tiles_m = cdiv(M, t.bm);
+    const int64_t Mm = M - p.tail_rows;      // rows of the main kernel
+    q.tail_rows = (int32_t)p.tail_rows;
+    q.tiles_m = cdiv(Mm, t.bm);
     q.tiles_n = cdiv(N, t.bn);
     q.decomposition = best.decomposition;
     if (q.tiles_m * q.tiles_n * (int64_t)q.threads >= (int64_t(1) << 32)) return SGEMM_ERR_UNSUPPORTED;
@@ -508,7 +569,7 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
         q.sk_tiles = best.sk_tiles;
         q.sk_units_per_wg = best.sk_ipw;
         p.k_steps = best.k_steps;
-        gemm_ws = partials_bytes(t, best.decomposition, 1, best.grid, best.sk_ipw, best.k_steps, M, N);
+        gemm_ws = partials_bytes(t, best.decomposition, 1, best.grid, best.sk_ipw, best.k_steps, Mm, N);
         p.second = gemm_ws > 0;
     } else {
         if (best.splits > 65535) return SGEMM_ERR_UNSUPPORTED;
@@ -517,9 +578,22 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
         q.workgroups = q.tiles_m * q.tiles_n * best.splits;
         if (best.splits > 1) {
             p.ldw = round_up(N, 4);
-            gemm_ws = partials_bytes(t, best.decomposition, best.splits, 0, 0, 0, M, N);
+            gemm_ws = partials_bytes(t, best.decomposition, best.splits, 0, 0, 0, Mm, N);
             p.second = true;
         }
+    }
+    // the row tail's partial products (split-K slices or stream-K slots)
+    size_t tail_ws = 0;
+    if (p.tail_rows > 0) {
+        const Candidate& tc = p.tail;
+        if (tc.decomposition == SGEMM_DECOMP_STREAM_K) {
+            tail_ws = partials_bytes(kSkinnyTiles[tc.tile], SGEMM_DECOMP_STREAM_K, 1, tc.grid, tc.sk_ipw, tc.k_steps,
+                                     p.tail_rows, N);
+        } else if (tc.splits > 1) {
+            p.tail_ldw = round_up(N, 4);
+            tail_ws = (size_t)(tc.splits * p.tail_rows * p.tail_ldw) * sizeof(float);
+        }
+        p.tail_second = tail_ws > 0;
     }
     // workspace: [packed A][packed B][partials], each 256-byte aligned
     size_t off = 0;
@@ -532,9 +606,14 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
         off += align256((size_t)(p.b_rows * p.b_ld) * sizeof(float));
     }
     p.gemm_ws_off = off;
-    q.workspace_bytes = gemm_ws > 0 ? off + gemm_ws : off;
+    if (gemm_ws > 0) off += align256(gemm_ws);
+    p.tail_ws_off = off;
+    off += tail_ws;
+    q.workspace_bytes = off;
     if (q.workspace_bytes > ws_cap) return SGEMM_ERR_SCRATCH_LIMIT;
-    q.launches = (q.packed != 0 ? 1 : 0) + 1 + (p.second ? 1 : 0);   // both operands pack in one launch
+    // both operands pack in one launch; the tail adds its kernel and its reduction or fix-up
+    q.launches = (q.packed != 0 ? 1 : 0) + 1 + (p.second ? 1 : 0) +
+                 (p.tail_rows > 0 ? 1 + (p.tail_second ? 1 : 0) : 0);
     *out = p;
     return SGEMM_OK;
 }
@@ -547,19 +626,20 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
 struct PlanKey {
     int64_t M, N, K;
     int32_t flags;                 // ta | tb | reads_ab | A, B 16-byte aligned | lda, ldb % 4 == 0
-    int32_t path, tile, split_k, vector, decomposition, pack;
+    int32_t path, tile, split_k, vector, decomposition, pack, row_tail;
     size_t ws_cap;
     bool operator==(const PlanKey& o) const {
-        return std::tie(M, N, K, flags, path, tile, split_k, vector, decomposition, pack, ws_cap) ==
+        return std::tie(M, N, K, flags, path, tile, split_k, vector, decomposition, pack, row_tail, ws_cap) ==
                std::tie(o.M, o.N, o.K, o.flags, o.path, o.tile, o.split_k, o.vector, o.decomposition, o.pack,
-                        o.ws_cap);
+                        o.row_tail, o.ws_cap);
     }
 };
 struct PlanKeyHash {
     size_t operator()(const PlanKey& k) const {
         uint64_t h = 1469598103934665603ull;
         for (int64_t v : {k.M, k.N, k.K, (int64_t)k.flags, (int64_t)k.path, (int64_t)k.tile, (int64_t)k.split_k,
-                          (int64_t)k.vector, (int64_t)k.decomposition, (int64_t)k.pack, (int64_t)k.ws_cap})
+                          (int64_t)k.vector, (int64_t)k.decomposition, (int64_t)k.pack, (int64_t)k.row_tail,
+                          (int64_t)k.ws_cap})
             h = (h ^ (uint64_t)v) * 1099511628211ull;
         return (size_t)h;
     }
@@ -577,7 +657,7 @@ sgemm_status make_plan(const Call& c, const sgemm_options* opts, Plan* out, size
     const PlanKey key{c.M, c.N, c.K,
                       (c.ta ? 1 : 0) | (c.tb ? 2 : 0) | (c.reads_ab() ? 4 : 0) | (aligned(c.A, 16) ? 8 : 0) |
                           (aligned(c.B, 16) ? 16 : 0) | (c.lda % 4 == 0 ? 32 : 0) | (c.ldb % 4 == 0 ? 64 : 0),
-                      o.path, o.tile, o.split_k, o.vector, o.decomposition, o.pack, ws_cap};
+                      o.path, o.tile, o.split_k, o.vector, o.decomposition, o.pack, o.row_tail, ws_cap};
     {
         std::lock_guard<std::mutex> lock(g_plan_mu);
         auto it = g_plans.find(key);
@@ -721,11 +801,12 @@ sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_option
     if (jobs.count > 0) e = launch_pack(jobs, stream);
     void* const gws = q.workspace_bytes > p.gemm_ws_off ? static_cast<void*>(wsb + p.gemm_ws_off) : nullptr;
 
+    const int64_t Mm = M - p.tail_rows;     // rows of the main kernel
     GemmArgs g;
     std::memset(&g, 0, sizeof(g));
     g.A = A;
     g.B = B;
-    g.M = (int32_t)M;
+    g.M = (int32_t)Mm;
     g.N = (int32_t)N;
     g.K = q.k_padded;
     g.alpha = c.alpha;
@@ -752,7 +833,7 @@ sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_option
     } else if (q.split_k > 1) {
         g.C = static_cast<float*>(gws);
         g.ldc = p.ldw;
-        g.c_slice = M * p.ldw;
+        g.c_slice = Mm * p.ldw;
     }
 
     if (e == hipSuccess) {
@@ -768,8 +849,52 @@ sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_option
         if (q.decomposition == SGEMM_DECOMP_STREAM_K)
             e = launch_streamk_fixup(g, q.bm, q.bn, (int)q.sk_tiles, stream);
         else
-            e = launch_splitk_reduce(static_cast<const float*>(gws), p.ldw, M * p.ldw, q.split_k, C, c.ldc,
-                                     (int32_t)M, (int32_t)N, c.alpha, c.beta, stream);
+            e = launch_splitk_reduce(static_cast<const float*>(gws), p.ldw, Mm * p.ldw, q.split_k, C, c.ldc,
+                                     (int32_t)Mm, (int32_t)N, c.alpha, c.beta, stream);
+    }
+    // the row tail: rows Mm .. M - 1 through the skinny kernel, on the same
+    // (packed) operands
+    if (e == hipSuccess && p.tail_rows > 0) {
+        const Candidate& tc = p.tail;
+        const int32_t r = (int32_t)p.tail_rows;
+        float* const c_tail = C + Mm * c.ldc;
+        float* const tws = reinterpret_cast<float*>(wsb + p.tail_ws_off);
+        GemmArgs gt = g;
+        gt.A = A + Mm * lda;
+        gt.M = r;
+        gt.k_chunk = (int32_t)tc.k_chunk;
+        gt.tiles_m = 1;
+        gt.tiles_n = (int32_t)cdiv(N, kSkinnyTiles[tc.tile].bn);
+        gt.group_m = g.group_m == 0 ? 0 : 1;
+        gt.C = c_tail;
+        gt.ldc = c.ldc;
+        gt.c_slice = 0;
+        gt.sk_grid = 0;
+        gt.dp_tiles = 0;
+        gt.k_steps = 0;
+        gt.sk_iters = 0;
+        gt.sk_ipw = 0;
+        gt.ws = nullptr;
+        if (tc.decomposition == SGEMM_DECOMP_STREAM_K) {
+            gt.sk_grid = (int32_t)tc.grid;
+            gt.k_steps = (int32_t)tc.k_steps;
+            gt.sk_iters = tc.sk_tiles * tc.k_steps;
+            gt.sk_ipw = tc.sk_ipw;
+            gt.ws = tws;
+        } else if (tc.splits > 1) {
+            gt.C = tws;
+            gt.ldc = p.tail_ldw;
+            gt.c_slice = r * p.tail_ldw;
+        }
+        e = launch_skinny(tc.tile, q.vector != 0, gt, (int)tc.splits, stream);
+        if (e == hipSuccess && p.tail_second) {
+            if (tc.decomposition == SGEMM_DECOMP_STREAM_K)
+                e = launch_streamk_fixup(gt, kSkinnyTiles[tc.tile].bm, kSkinnyTiles[tc.tile].bn, (int)tc.sk_tiles,
+                                         stream);
+            else
+                e = launch_splitk_reduce(tws, p.tail_ldw, r * p.tail_ldw, (int)tc.splits, c_tail, c.ldc, r,
+                                         (int32_t)N, c.alpha, c.beta, stream);
+        }
     }
     if (owned) {
         if (hipFreeAsync(ws, stream) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;

@@ -131,6 +131,14 @@ typedef enum sgemm_decomposition {
  *                   the rasterisation of "如何让计算受限问题真正达到计算受限" section
  *                   5.2), 1 = plain row-major (for comparison).  Results are the
  *                   same bits either way.
+ *   row_tail      : matrix-core path, operands as stored, M 1 to 32 rows past a
+ *                   multiple of 64: run those last rows through the skinny kernel
+ *                   after the main kernel has done the rows above, instead of a row
+ *                   of output tiles that is mostly padding (the edge handling of
+ *                   "GEMM from naive to tiled" section 七 moved to a kernel sized
+ *                   for it).  0 = when the time model favours it, 1 = never,
+ *                   2 = whenever possible (and the scratch fits).  The tail rows'
+ *                   sums are those of the skinny path.
  */
 typedef struct sgemm_options {
     int32_t path;
@@ -142,6 +150,7 @@ typedef struct sgemm_options {
     void* workspace;
     size_t workspace_bytes;
     int32_t tile_order;
+    int32_t row_tail;
 } sgemm_options;
 
 /* sgemm with explicit options (tests and benchmarks).  opts may be NULL. */
@@ -174,6 +183,9 @@ typedef struct sgemm_plan {
     int32_t packed;          /* bit 0: A, bit 1: B copied to aligned workspace first */
     int32_t k_padded;        /* K as the matrix kernel sees it (a multiple of 4 when
                                 packed; K otherwise) */
+    int32_t tail_rows;       /* last rows computed by the skinny kernel after the main
+                                kernel (0: none; tiles_m and workgroups describe the main
+                                kernel's M - tail_rows rows) */
 } sgemm_plan;
 
 sgemm_status sgemm_plan_query(int64_t M, int64_t N, int64_t K,

@@ -408,3 +408,21 @@ def test_fma_probe_rejects_bad_arguments():
     assert so.sgemm_fma_probe(-1, 4, 0x1000, None) == 1
     assert so.sgemm_fma_probe(4, 0, 0x1000, None) == 1
     assert so.sgemm_fma_probe(4, 4, None, None) == 1
+
+
+def test_row_tail_plans():
+    """The row tail: M 1-32 rows past a multiple of 64 with operands as
+    stored; the main kernel's tiles cover the rows above it."""
+    p = lib.sgemm_plan_query(4097, 3001, 2049, lda=2049, ldb=3001, ldc=3001)
+    assert p["tail_rows"] == 1 and p["tiles_m"] == 4096 // p["bm"] and p["packed"] == 3
+    q = lib.sgemm_plan_query(4097, 3001, 2049, lda=2049, ldb=3001, ldc=3001, row_tail="never")
+    assert q["tail_rows"] == 0 and q["tiles_m"] == -(-4097 // q["bm"])
+    assert lib.sgemm_plan_query(513, 385, 272, row_tail="always")["tail_rows"] == 1
+    assert lib.sgemm_plan_query(4128, 4096, 4096, row_tail="always")["tail_rows"] == 32
+    for M in (4096, 4129, 4160, 63, 100):          # none, 33 rows, a multiple, too few rows above
+        assert lib.sgemm_plan_query(M, 512, 512, row_tail="always")["tail_rows"] == 0, M
+    # operands stored transposed keep the full tile grid (the skinny kernel reads them as stored only)
+    assert lib.gemm_plan_query("N", "T", 4097, 512, 512, row_tail="always")["tail_rows"] == 0
+    assert lib.gemm_plan_query("N", "N", 4097, 512, 512, row_tail="always")["tail_rows"] == 1
+    with pytest.raises(lib.SgemmError):
+        lib.sgemm_plan_query(4097, 512, 512, row_tail=3)

@@ -326,6 +326,48 @@ def test_packed_operands(oracle_mod, case, decomposition, tile):
                pack="always", decomposition=decomposition)
 
 
+# --- the row tail: the last 1-32 rows of M through the skinny kernel ------------------------
+
+ROW_TAIL_CASES = [  # M, N, K, lda, ldb, forced main options
+    (513, 385, 272, None, None, {}),                                   # one row, 64x64 tile
+    (65, 64, 64, None, None, {}),                                      # one row past one tile
+    (80, 130, 70, None, None, {}),                                     # 16 rows (skinny tile 0), K tail
+    (96, 100, 300, None, None, {}),                                    # 32 rows (skinny tile 1)
+    (113, 200, 3000, None, None, {}),                                  # 49 rows: no tail (beyond 32)
+    (577, 301, 205, 205, 301, {}),                                     # packed operands, one row
+    (4097, 257, 1000, None, None, {"path": "mfma", "tile": 0}),       # 256x256 main tile
+    (1040, 600, 900, None, None, {"path": "mfma", "tile": 2, "decomposition": "stream_k"}),
+    (1040, 600, 900, None, None, {"path": "mfma", "tile": 3, "split_k": 3}),
+]
+
+
+@pytest.mark.parametrize("case", ROW_TAIL_CASES, ids=lambda c: "x".join(map(str, c[:3])) + str(c[5]))
+def test_row_tail(oracle_mod, case):
+    """row_tail = always: the main kernel takes the rows up to the last
+    multiple of 64, the skinny kernel the 1-32 rows after them (its own
+    split-K or stream-K plan), on aligned and packed operands and with the
+    main kernel's tile and decomposition forced."""
+    M, N, K, lda, ldb, opts = case
+    plan = lib.sgemm_plan_query(M, N, K, lda=lda or K, ldb=ldb or N, row_tail="always", **opts)
+    r = M % 64
+    assert plan["tail_rows"] == (r if 1 <= r <= 32 else 0), plan
+    check_case(oracle_mod, M, N, K, f"row tail {opts}", lda=lda, ldb=ldb, row_tail="always", **opts)
+
+
+def test_row_tail_with_alpha_beta(oracle_mod):
+    """The tail applies alpha and beta to its rows as the main kernel does to the others."""
+    M, N, K = 257, 300, 500
+    say("row tail alpha/beta")
+    A, B = inputs(M, N, K, "integer", 91)
+    C0 = workloads.draw(M, N, "integer", 92)
+    Cd = C0.to(DEV)
+    lib.gemm(to_dev(A), to_dev(B), Cd, alpha=2.0, beta=-0.5, row_tail="always")
+    torch.cuda.synchronize()
+    assert lib.gemm_plan_query("N", "N", M, N, K, alpha=2.0, beta=-0.5, row_tail="always")["tail_rows"] == 1
+    ref = oracle_mod.gemm(A.numpy(), B.numpy(), C0.numpy(), alpha=2.0, beta=-0.5)
+    assert_bit_exact(Cd.cpu().numpy(), oracle_mod.round_to_f32(ref), what="row tail alpha/beta")
+
+
 def test_packed_matches_unpacked_bits():
     """Packing copies values exactly and pads with zeros: the 16-byte kernel
     on packed copies returns the bits of the 16-byte kernel run on an
