@@ -290,7 +290,7 @@ def gemm(A, B, C=None, stream=None, *, trans_a=False, trans_b=False, alpha=1.0, 
     return C
 
 
-READ_PROBE_PARTIALS = 1024
+READ_PROBE_PARTIALS = 4096
 
 
 def read_probe_raw(x, n, partial, stream=0) -> int:

@@ -112,7 +112,7 @@ hipError_t launch_streamk_fixup(const GemmArgs& g, int bm, int bn, int sk_tiles,
 hipError_t launch_scale(float* C, int64_t ldc, int32_t M, int32_t N, float beta, hipStream_t stream);
 // The read-rate probe: reads x[0 .. n) once (n % 4 == 0, x 16-byte aligned)
 // and writes kReadGrid per-workgroup sums to partial.
-constexpr int kReadGrid = 1024;
+constexpr int kReadGrid = 4096;
 hipError_t launch_read_probe(const float* x, int64_t n, float* partial, hipStream_t stream);
 // The FMA-rate probe: `workgroups` x 256 lanes, each 16 x 8 x iters scalar
 // FP32 FMAs; one float per lane to out.

@@ -178,28 +178,31 @@ void streamk_fixup_kernel(GemmArgs g, int bm, int bn) {
 // Read-rate probe, the yardstick of the streaming (skinny) path: the rate
 // at which the chip reads a buffer it uses once, measured rather than taken
 // from the data sheet (the "realistic machine model" of the GEMV example in
-// "如何让计算受限问题真正达到计算受限", section 7).  x[0 .. 4 n4) is read once
-// with 16-byte loads, grid-stride in 16-byte groups (a wave's load covers
-// 1 KB), kReadU loads in flight per lane; each workgroup writes its sum to
-// partial[blockIdx.x], so no load is dead.  kReadGrid workgroups (4 per CU)
-// and 4 loads in flight measured the fastest of 1024-4096 workgroups and
-// 4-8 loads on a 180 MB buffer, warm and after a flush.
+// "如何让计算受限问题真正达到计算受限", section 7).  x[0 .. 4 n4) is cut into
+// kReadGrid contiguous chunks, one per workgroup (16 per CU), each read with
+// 16-byte loads, kReadU in flight per lane (a wave's load covers 1 KB);
+// each workgroup writes its sum to partial[blockIdx.x], so no load is dead.
+// Of grid-stride and chunked reads with 1024-16384 workgroups and 4-16 loads
+// in flight, chunks over 4096 workgroups with 4 loads read a 4 GiB buffer
+// fastest (6.16 TB/s; grid-stride at most 5.96).
 constexpr int kReadU = 4;
 
 __global__ __launch_bounds__(256)
 void read_probe_kernel(const f32x4* __restrict__ x, int64_t n4, float* __restrict__ partial) {
     __shared__ float red[4];
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t per = (n4 + gridDim.x - 1) / gridDim.x;
+    const int64_t b = (int64_t)blockIdx.x * per;
+    const int64_t e = b + per < n4 ? b + per : n4;
+    int64_t i = b + threadIdx.x;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (; i + (kReadU - 1) * stride < n4; i += kReadU * stride) {
+    for (; i + (kReadU - 1) * 256 < e; i += kReadU * 256) {
         f32x4 v[kReadU];
 #pragma unroll
-        for (int u = 0; u < kReadU; ++u) v[u] = x[i + u * stride];
+        for (int u = 0; u < kReadU; ++u) v[u] = x[i + u * 256];
 #pragma unroll
         for (int u = 0; u < kReadU; ++u) acc += v[u];
     }
-    for (; i < n4; i += stride) acc += x[i];
+    for (; i < e; i += 256) acc += x[i];
     float s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     for (int off = 32; off > 0; off >>= 1) s += __shfl_down(s, off);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;

@@ -293,7 +293,7 @@ sgemm_status sgemm_tile_info(int32_t path, int32_t tile, int32_t* count,
  * x: device, 16-byte aligned, n >= 0 and a multiple of 4 (SGEMM_ERR_INVALID_ARG
  * otherwise, nothing enqueued); partial: device, SGEMM_READ_PROBE_PARTIALS
  * floats, caller-owned.  Nothing is allocated. */
-#define SGEMM_READ_PROBE_PARTIALS 1024
+#define SGEMM_READ_PROBE_PARTIALS 4096
 sgemm_status sgemm_read_probe(const float* x, int64_t n, float* partial, hipStream_t stream);
 
 /* Measurement helper, outside the product path: the rate of scalar FP32

@@ -393,7 +393,7 @@ def test_read_probe_rejects_bad_arguments():
     """The read-rate probe validates on the host before any HIP call: n a
     multiple of 4, x 16-byte aligned, a partial buffer given."""
     so = lib.load_library()
-    assert lib.READ_PROBE_PARTIALS == 1024
+    assert lib.READ_PROBE_PARTIALS == 4096
     assert lib.read_probe_raw(0x1000, 6, 0x2000) == 1          # n % 4
     assert lib.read_probe_raw(0x1004, 8, 0x2000) == 1          # misaligned x
     assert lib.read_probe_raw(0x1000, -4, 0x2000) == 1         # negative n

@@ -644,8 +644,8 @@ def test_full_size_workload_integer(oracle_mod, name):
 def test_read_probe(n):
     """The read-rate probe reads every element once: on small integers its
     per-workgroup sums are exact, and together they give the buffer's sum
-    (ragged tails past the grid stride and past the unrolled loads
-    included)."""
+    (chunks that end inside the unrolled loads, workgroups left without a
+    chunk, and the empty buffer included)."""
     say(f"read probe n={n}")
     g = torch.Generator().manual_seed(n + 3)
     x = torch.randint(0, 3, (n,), generator=g, dtype=torch.int32).to(torch.float32)
