@@ -16,8 +16,14 @@
 //     section 九.2) and the other 56 lanes read the same addresses again;
 //   * per k each lane issues 4 16-byte LDS reads and 64 FP32 FMAs,
 //     acc[i][j] += a[i] * b[j] (the outer-product update, section 五.1).
-// Each k-step's FMAs are scalar v_fma_f32 (packed FP32 is not used), so the
-// path's ceiling is half the chip's FP32 vector peak.
+// Each k-step's FMAs are scalar v_fmac_f32 (packed FP32 is not used).  On
+// gfx950 these issue at the full FP32 vector rate when at least two waves
+// per SIMD have FMAs ready (measured with the library's FMA-rate probe: 69
+// TFLOP/s with one wave per SIMD, 123 with two, 145-150 with four or more);
+// this kernel's 214 VGPRs allow two, so a wave waiting on LDS or at the
+// barrier halves its SIMD's rate, which is where most of the gap to the
+// peak goes.  Four waves per SIMD would need at most 128 VGPRs: the 64
+// accumulators, the fragments and the prefetch registers then spill.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
