@@ -184,7 +184,7 @@ void streamk_fixup_kernel(GemmArgs g, int bm, int bn) {
 // each workgroup writes its sum to partial[blockIdx.x], so no load is dead.
 // Of grid-stride and chunked reads with 1024-16384 workgroups and 4-16 loads
 // in flight, chunks over 4096 workgroups with 4 loads read a 4 GiB buffer
-// fastest (6.16 TB/s; grid-stride at most 5.96).
+// fastest (6.16 TB/s in the sweep, 6.2 in later runs; grid-stride at most 5.96).
 constexpr int kReadU = 4;
 
 __global__ __launch_bounds__(256)
