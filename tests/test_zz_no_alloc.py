@@ -79,6 +79,8 @@ CASES = [
      [(32, 1000, 4100, False, False, None, None), (9, 300, 1000, False, False, None, None)]),
     ("valu split-K", {"path": "valu", "split_k": 5},
      [(300, 200, 2000, False, False, None, None), (130, 100, 700, False, False, None, None)]),
+    ("row tail, then packed operands with a row tail", {"row_tail": "always"},
+     [(1025, 600, 700, False, False, None, None), (577, 301, 205, False, False, 207, 303)]),
     ("default plan", None,
      [(512, 512, 8192, False, False, None, None), (300, 200, 20, False, False, None, None)]),
     ("default plan, unaligned operands", None,
