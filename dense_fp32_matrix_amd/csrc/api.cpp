@@ -595,7 +595,7 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
         }
         p.tail_second = tail_ws > 0;
     }
-    // workspace: [packed A][packed B][partials], each 256-byte aligned
+    // workspace: [packed A][packed B][main partials][tail partials], each 256-byte aligned
     size_t off = 0;
     if (q.packed & 1) {
         p.pack_a_off = off;
