@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--split-k", type=int, default=0)
     ap.add_argument("--decomposition", default="auto")
     ap.add_argument("--pack", default="auto", choices=["auto", "never", "always"])
+    ap.add_argument("--row-tail", default="auto", choices=["auto", "never", "always"],
+                    help="run the last 1-32 rows of M through the skinny kernel (planner default: auto)")
     ap.add_argument("--tile-order", default="xcd", choices=["xcd", "plain"],
                     help="matrix-core tile order: XCD-aware (default) or plain row-major, for comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -169,9 +171,10 @@ def main():
     C = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
     opts = {}
     if (args.path != "auto" or args.tile >= 0 or args.split_k or args.decomposition != "auto" or args.pack != "auto"
-            or args.tile_order != "xcd"):
+            or args.tile_order != "xcd" or args.row_tail != "auto"):
         opts = {"path": args.path, "tile": args.tile, "split_k": args.split_k,
-                "decomposition": args.decomposition, "pack": args.pack, "tile_order": args.tile_order}
+                "decomposition": args.decomposition, "pack": args.pack, "tile_order": args.tile_order,
+                "row_tail": args.row_tail}
     plan = lib.sgemm_plan_query(w.M, w.N, w.K, A.data_ptr(), w.lda, B.data_ptr(), w.ldb, C.data_ptr(), w.N,
                                 **opts)
 
