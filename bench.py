@@ -318,6 +318,12 @@ def main():
     roof["kernel"] = main_kernel
     roof["launch_ms"] = kernel_ms
     roof["launches_per_step"] = plan["launches"]
+    if not hbm_bound and clocks is not None:
+        # the same peak at the shader clock the GPU held while the workload ran
+        # (power management lowers it under some loads; HBM's peak does not move with it)
+        sclk = clocks["sclk_mhz_median_2nd_half"]
+        peak_clk = PEAK_FP32_TFLOPS * sclk / 2400.0
+        roof["clock_adjusted"] = {"sclk_mhz": sclk, "peak": peak_clk, "frac": achieved / peak_clk}
     if probe is not None:
         probe["call_vs_read_warm"] = probe["warm_ms"] / kernel_ms
         roof["read_probe"] = probe
