@@ -173,9 +173,10 @@ typedef struct sgemm_plan {
     int64_t k_chunk;         /* K elements per slice */
     int64_t workgroups;      /* workgroups of the main kernel */
     size_t workspace_bytes;  /* split-K / stream-K scratch (0 if none) */
-    int32_t launches;        /* kernels enqueued by the call (0 to 3: one packing copy of the
+    int32_t launches;        /* kernels enqueued by the call (0 to 5: one packing copy of the
                                 misaligned operands, the matrix kernel, a split-K reduction or
-                                stream-K fix-up) */
+                                stream-K fix-up, and for a row tail the skinny kernel and its
+                                reduction or fix-up) */
     int32_t decomposition;   /* sgemm_decomposition actually used */
     int64_t dp_tiles;        /* stream-K: tiles computed whole first */
     int64_t sk_tiles;        /* stream-K: tiles whose K-steps are shared out */
