@@ -113,7 +113,16 @@ constexpr double kStreamKBw = 1e13;          // bytes/s for stream-K partial til
                                              // by neighbouring workgroups, cache resident)
 constexpr double kLaunch = 8e-6;             // one more dependent kernel launch
 constexpr double kTileVisit = 2e-6;          // filling and draining one tile's pipeline, and its epilogue
-constexpr double kSkinnyBw = 4.3e12;         // bytes/s the skinny kernel streams B at from HBM (cold)
+// The skinny kernel as a row tail, B just read by the main kernel (measured
+// on 44 tails of 1 and 17 rows, 512 to 11008 columns, 1024 to 8192 deep):
+// launch to end of it and its reduction or fix-up on a small B, the rate it
+// streams a B that the main kernel has left in cache, and the cost of each
+// K slice or stream-K segment of a strip that its reduction sums.
+constexpr double kSkinnyBase = 4.4e-6;
+constexpr double kSkinnyWarmBw = 6.3e12;
+constexpr double kSkinnySlice = 0.22e-6;       // per split-K slice beyond two
+constexpr double kSkinnyFixup = 3e-6;          // the stream-K fix-up
+constexpr double kSkinnySegment = 0.1e-6;      // per stream-K segment of a strip beyond 16
 
 // Share of the CU's peak one tile shape sustains when its CU is full, with
 // 16-byte (vec) or 4-byte load lanes (measured; the 256 x 256 tiles have no
@@ -377,10 +386,16 @@ Candidate skinny_candidate(const sgemm_options& o, int tile, int64_t N, int64_t 
         best.dp_tiles = 0;
         best.sk_ipw = cdiv(units, best.grid);
     }
-    // time: B (and the few rows of A and C) streamed at the cold rate the
-    // kernel measured, plus the reduction or fix-up launch
-    best.time = 4.0 * ((double)K * N + (double)t.bm * (K + N)) / kSkinnyBw +
-                ((best.splits > 1 || best.decomposition == SGEMM_DECOMP_STREAM_K) ? kLaunch : 0.0);
+    // time as a row tail: B (and the few rows of A and C) streamed from
+    // cache; the 32-row tile's doubled A fragments and MFMAs cost a seventh
+    // more, and a shared strip's pieces add to its reduction
+    const bool two_blocks = t.bm > 16;
+    best.time = kSkinnyBase + 4.0 * ((double)K * N + (double)t.bm * (K + N)) * (two_blocks ? 1.15 : 1.0) / kSkinnyWarmBw +
+                (two_blocks ? 1.5e-6 : 0.0);
+    if (best.decomposition == SGEMM_DECOMP_STREAM_K)
+        best.time += kSkinnyFixup + kSkinnySegment * (double)std::max<int64_t>(0, cdiv(best.k_steps, best.sk_ipw) - 16);
+    else
+        best.time += kSkinnySlice * (double)std::max<int64_t>(0, best.splits - 2);
     return best;
 }
 
@@ -521,7 +536,7 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
             const size_t room = ws_cap == SIZE_MAX ? SIZE_MAX : ws_cap - std::min(ws_cap, copies_bytes + tail_ws + 512);
             if (copies_bytes + tail_ws + 512 <= ws_cap &&
                 mfma_best(o, q.vector != 0, ops, M - r, N, kt, room, &main_rows)) {
-                const double alt = main_rows.time + best_pack_time + tail.time + kLaunch;
+                const double alt = main_rows.time + best_pack_time + tail.time;   // the tail's time holds its launches
                 if (o.row_tail == 2 || alt < best.time) {
                     best = main_rows;
                     p.tail_rows = r;
