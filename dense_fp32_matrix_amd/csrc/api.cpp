@@ -104,15 +104,27 @@ int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 // ---------------------------------------------------------------------------
 // Planning.  Candidates are ranked by a simple time model: a CU retires
 // kMacRate multiply-adds per second times the tile's measured efficiency;
-// workgroups run in waves of (CUs x workgroups per CU); split-K and stream-K
-// add their partial-product traffic and one more launch.
+// workgroups run in waves of (CUs x workgroups per CU); each tile visit adds
+// its pipeline fill, drain and epilogue; split-K and stream-K add their
+// partial-product traffic and their second kernel; stream-K, whose
+// concurrent workgroups work on different K ranges and so share little in
+// L2, cannot read its operands faster than kStreamKReadBw.  The constants
+// were searched for the least loss against the fastest measured candidate
+// on 528 random shapes (432 with M, N, K log-uniform in 256-8192, every tile
+// with K split 1, 2, 4 and 8 ways and as stream-K; 48 with M, N in 256-1448
+// and K in 11600-65536, splits 4-32): the chosen candidate is then 0.6 %
+// slower than the fastest on average and over 5 % slower on 23 shapes (2.4 %
+// and 80 shapes with the constants before).
 // ---------------------------------------------------------------------------
 constexpr double kMacRate = 128.0 * 2.4e9;   // FP32 MACs per second per CU at peak
-constexpr double kPartialBw = 4e12;          // bytes/s for split-K partial slices (mostly cache resident)
-constexpr double kStreamKBw = 1e13;          // bytes/s for stream-K partial tiles (written and read back
+constexpr double kPartialBw = 5.5e12;        // bytes/s for split-K partial slices (mostly cache resident)
+constexpr double kSplitLaunch = 3e-6;        // the split-K reduction's launch
+constexpr double kStreamKBw = 9e12;          // bytes/s for stream-K partial tiles (written and read back
                                              // by neighbouring workgroups, cache resident)
-constexpr double kLaunch = 8e-6;             // one more dependent kernel launch
-constexpr double kTileVisit = 2e-6;          // filling and draining one tile's pipeline, and its epilogue
+constexpr double kStreamKReadBw = 6e12;      // bytes/s stream-K reads its operand slabs at, at most
+constexpr double kFixupLaunch = 4.5e-6;      // the stream-K fix-up's launch
+constexpr double kFixupSpan = 6.5e-6;        // more when some workgroup's range spans two tiles
+constexpr double kLaunch = 8e-6;             // the packing kernel's launch
 // The skinny kernel as a row tail, B just read by the main kernel (measured
 // on 44 tails of 1 and 17 rows, 512 to 11008 columns, 1024 to 8192 deep):
 // launch to end of it and its reduction or fix-up on a small B, the rate it
@@ -139,7 +151,7 @@ double mfma_efficiency(int tile, bool vec) {
         case 0: return 0.93;
         case 1: return 0.927;
         case 2: return 0.91;
-        case 3: return 0.80;
+        case 3: return 0.82;
         default: return 0.70;
     }
 }
@@ -148,11 +160,14 @@ double mfma_efficiency(int tile, bool vec) {
 // built for two or more per CU (a tail shorter than one wave of
 // workgroups).  The 64 x 64 tile, which moves twice the bytes per
 // multiply-add of the 128 x 128 tile through the CU's load path and LDS,
-// runs a little faster with them to itself.
+// runs faster with them to itself.
 double mfma_alone_efficiency(int tile, bool vec) {
     const double e = mfma_efficiency(tile, vec);
-    return tile == 3 ? 1.0375 * e : e;
+    return tile == 3 ? 1.05 * e : e;
 }
+
+// Filling and draining one tile's pipeline, and its epilogue (seconds).
+double tile_visit(int tile) { return tile == 3 ? 0.8e-6 : 2.4e-6; }
 
 int wgs_per_cu(const TileShape& t) { return std::max(1, t.waves_per_simd * 4 / (t.waves_m * t.waves_n)); }
 
@@ -170,16 +185,17 @@ Candidate tiles_candidate(int tile, bool vec, int64_t M, int64_t N, int64_t K, i
     const int64_t wgs = tiles * c.splits;
     const int64_t full_waves = wgs / (kNumCUs * per_cu);
     const int64_t tail = wgs - full_waves * kNumCUs * per_cu;
+    const double visit = tile_visit(tile);
     const double wg_time =
-        (double)t.bm * t.bn * c.k_chunk * per_cu / (kMacRate * mfma_efficiency(tile, vec)) + kTileVisit * per_cu;
+        (double)t.bm * t.bn * c.k_chunk * per_cu / (kMacRate * mfma_efficiency(tile, vec)) + visit * per_cu;
     // a tail of at most one workgroup per CU runs alone on its CU
     double tail_time = 0;
     if (tail > 0)
         tail_time = (tail <= kNumCUs && per_cu > 1)
-                        ? (double)t.bm * t.bn * c.k_chunk / (kMacRate * mfma_alone_efficiency(tile, vec)) + kTileVisit
+                        ? (double)t.bm * t.bn * c.k_chunk / (kMacRate * mfma_alone_efficiency(tile, vec)) + visit
                         : wg_time;
     c.time = full_waves * wg_time + tail_time;
-    if (c.splits > 1) c.time += (2.0 * c.splits + 1) * M * N * 4 / kPartialBw + kLaunch;
+    if (c.splits > 1) c.time += (2.0 * c.splits + 1) * M * N * 4 / kPartialBw + kSplitLaunch;
     return c;
 }
 
@@ -200,15 +216,14 @@ Candidate streamk_candidate(int tile, bool vec, int64_t M, int64_t N, int64_t K)
     const int64_t units = c.sk_tiles * c.k_steps;
     c.sk_ipw = cdiv(units, grid);
     const double step_time = (double)t.bm * t.bn * t.bk * wgs_per_cu(t) / (kMacRate * mfma_efficiency(tile, vec));
-    // a workgroup's shared range touches one or two tiles
-    c.time = (double)(c.dp_tiles / grid) * (c.k_steps * step_time + kTileVisit * wgs_per_cu(t)) +
-             c.sk_ipw * step_time + 2 * kTileVisit * wgs_per_cu(t);
     // partial tiles: count the workgroup ranges' segments that do not cover a
     // whole tile; each is written to a slot and read back once
     int64_t partial = 0;
+    bool spans = false;    // some range touches two tiles
     for (int64_t w = 0; w < grid; ++w) {
         int64_t it = w * c.sk_ipw;
         const int64_t end = std::min(it + c.sk_ipw, units);
+        if (it < end && it / c.k_steps != (end - 1) / c.k_steps) spans = true;
         while (it < end) {
             const int64_t ks0 = it % c.k_steps;
             const int64_t ks1 = std::min(c.k_steps, ks0 + (end - it));
@@ -216,7 +231,11 @@ Candidate streamk_candidate(int tile, bool vec, int64_t M, int64_t N, int64_t K)
             it += ks1 - ks0;
         }
     }
-    if (partial > 0) c.time += 2.0 * partial * t.bm * t.bn * 4 / kStreamKBw + kLaunch;
+    const double compute = (double)(c.dp_tiles / grid) * (c.k_steps * step_time + tile_visit(tile) * wgs_per_cu(t)) +
+                           c.sk_ipw * step_time;
+    const double reads = (double)tiles * c.k_steps * (t.bm + t.bn) * t.bk * 4 / kStreamKReadBw;
+    c.time = std::max(compute, reads) + (spans ? 2 : 1) * tile_visit(tile) * wgs_per_cu(t);
+    if (partial > 0) c.time += 2.0 * partial * t.bm * t.bn * 4 / kStreamKBw + kFixupLaunch + (spans ? kFixupSpan : 0.0);
     return c;
 }
 
@@ -312,10 +331,11 @@ bool mfma_best(const sgemm_options& o, bool vec, int ops, int64_t M, int64_t N, 
                 const TileShape& t = kMfmaTiles[tile];
                 const int64_t tiles = cdiv(M, t.bm) * cdiv(N, t.bn);
                 const int64_t slots = (int64_t)kNumCUs * wgs_per_cu(t);
-                cs.push_back(tiles_candidate(tile, vec, M, N, K, 1));
+                // K in 1, 2, 4 and 8 slices, and, with fewer tiles than
+                // workgroup slots, enough slices to fill every slot and half
+                // as many (less partial traffic, one short wave)
+                for (int64_t s : {1, 2, 4, 8}) cs.push_back(tiles_candidate(tile, vec, M, N, K, s));
                 if (tiles < slots) {
-                    // enough slices to fill every slot, and half as many
-                    // (less partial traffic, one short wave)
                     int64_t s = 1, kc = K;
                     choose_split(tiles, K, t.bk, slots, 32, &s, &kc);
                     cs.push_back(tiles_candidate(tile, vec, M, N, K, s));
