@@ -344,6 +344,26 @@ def test_skinny_plan_rule():
     assert lib.sgemm_plan_query(16, 256, 512)["decomposition_name"] == "stream_k"
 
 
+@pytest.mark.parametrize("shape,tile,decomposition,split", [
+    # (timed warm on MI355X: the fastest candidates, microseconds)
+    ((424, 384, 744), 3, "tiles", ">1"),       # 64x64 split 4: 11.1, split 2: 12.8, unsplit 15.7
+    ((508, 432, 1600), 3, "tiles", ">1"),      # 64x64 split 4: 14.8, 128x128 stream-K: 24.0
+    ((528, 448, 832), 3, "tiles", ">1"),       # 64x64 split 4: 12.1, unsplit 16.7
+    ((7380, 1184, 340), 3, "tiles", 1),        # 64x64: 64.3, 128x128 stream-K: 77.1
+    ((2468, 2160, 440), 3, "tiles", 1),        # 64x64: 52.0, 128x128 stream-K: 60.6
+    ((296, 7700, 7252), 3, "tiles", ">1"),     # 64x64 split 2: 299.0, 64x64 stream-K: 338.8
+    ((960, 700, 41032), 2, "stream_k", 1),     # 128x128 stream-K: 471.1, 64x64 stream-K: 571.0 (read-bound)
+    ((512, 512, 65536), 2, "stream_k", 1),     # 128x128 stream-K: 253.0, split 16: 264.4
+])
+def test_planner_calibrated_choices(shape, tile, decomposition, split):
+    """Plans the fitted time model must keep: shapes where the earlier
+    constants chose a candidate 8-59 % slower than the fastest timed one, and
+    the long-K workload."""
+    p = lib.sgemm_plan_query(*shape, row_tail="never")
+    assert (p["tile"], p["decomposition_name"]) == (tile, decomposition), (shape, p)
+    assert p["split_k"] > 1 if split == ">1" else p["split_k"] == split, (shape, p)
+
+
 def test_binding_rejects_overlapping_rows():
     """The binding passes a view's row stride as the leading dimension and
     never widens it: broadcast views (stride 0) and as_strided views whose
