@@ -110,11 +110,13 @@ int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 // concurrent workgroups work on different K ranges and so share little in
 // L2, cannot read its operands faster than kStreamKReadBw.  The constants
 // were searched for the least loss against the fastest measured candidate
-// on 528 random shapes (432 with M, N, K log-uniform in 256-8192, every tile
+// on 576 random shapes (528 with M, N, K log-uniform in 256-8192, every tile
 // with K split 1, 2, 4 and 8 ways and as stream-K; 48 with M, N in 256-1448
 // and K in 11600-65536, splits 4-32): the chosen candidate is then 0.6 %
-// slower than the fastest on average and over 5 % slower on 23 shapes (2.4 %
-// and 80 shapes with the constants before).
+// slower than the fastest on average and over 5 % slower on 23 shapes (2.7 %
+// and 112 shapes with the constants before).  The packing rate and launch
+// and the 4-byte-lane efficiencies come from 80 shapes with M, N, K odd
+// (every candidate on packed copies and on the operands as they are).
 // ---------------------------------------------------------------------------
 constexpr double kMacRate = 128.0 * 2.4e9;   // FP32 MACs per second per CU at peak
 constexpr double kPartialBw = 5.5e12;        // bytes/s for split-K partial slices (mostly cache resident)
@@ -124,7 +126,7 @@ constexpr double kStreamKBw = 9e12;          // bytes/s for stream-K partial til
 constexpr double kStreamKReadBw = 6e12;      // bytes/s stream-K reads its operand slabs at, at most
 constexpr double kFixupLaunch = 4.5e-6;      // the stream-K fix-up's launch
 constexpr double kFixupSpan = 6.5e-6;        // more when some workgroup's range spans two tiles
-constexpr double kLaunch = 8e-6;             // the packing kernel's launch
+constexpr double kPackLaunch = 5.5e-6;       // the packing kernel's launch
 // The skinny kernel as a row tail, B just read by the main kernel (measured
 // on 44 tails of 1 and 17 rows, 512 to 11008 columns, 1024 to 8192 deep):
 // launch to end of it and its reduction or fix-up on a small B, the rate it
@@ -142,8 +144,8 @@ constexpr double kSkinnySegment = 0.1e-6;      // per stream-K segment of a stri
 double mfma_efficiency(int tile, bool vec) {
     if (!vec) {
         switch (tile) {
-            case 2: return 0.58;
-            case 3: return 0.55;
+            case 2: return 0.64;
+            case 3: return 0.47;
             default: return 0.0;
         }
     }
@@ -359,7 +361,7 @@ bool mfma_best(const sgemm_options& o, bool vec, int ops, int64_t M, int64_t N, 
     return have;
 }
 
-constexpr double kPackBw = 3e12;   // bytes/s read + written by the pack kernel
+constexpr double kPackBw = 3.8e12;   // bytes/s read + written by the pack kernel
 
 // The skinny path's plan for tile `tile` (N columns, K deep; M <= the
 // tile's bm).  The kernel streams B fastest when every CU holds one
@@ -512,7 +514,7 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
                                   (pack_b ? align256((size_t)(br * round_up(bc, 32)) * sizeof(float)) : 0);
             Candidate cand;
             const bool fits = copies <= ws_cap && mfma_best(o, true, ops, M, N, kp, ws_cap - copies, &cand);
-            const double pack_time = bytes / kPackBw + kLaunch;
+            const double pack_time = bytes / kPackBw + kPackLaunch;
             cand.time += pack_time;
             if (fits && (o.pack == 2 || !have || cand.time < best.time)) {
                 have = true;
