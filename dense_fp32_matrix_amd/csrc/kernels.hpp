@@ -130,6 +130,11 @@ struct PackJob {
     float* dst;
     int64_t ldd;
     int32_t rows_p, cols_p;
+    // set by launch_pack: workgroups of this job, the 16-byte groups each
+    // moves, and how each covers its part (whole rows per workgroup when a
+    // row has at most that many groups, else pieces per row)
+    int64_t blocks;
+    int32_t groups, rows_per_block, pieces_per_row;
 };
 struct PackJobs {
     PackJob job[2];

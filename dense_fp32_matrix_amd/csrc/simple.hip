@@ -86,25 +86,62 @@ void scale_kernel(float* __restrict__ C, int64_t ldc, int32_t M, int32_t N, floa
 // padding rows and columns.  The copy is exact, and the zeros only add +0
 // terms to the product, so the matrix kernel's 16-byte loaders can then run
 // on operands that were not aligned.  One launch packs both operands when
-// both need it (blockIdx.z picks the job).  One thread writes one 16-byte
-// group of a row; blockIdx.y strides over the rows.
+// both need it: workgroups [0, job[0].blocks) copy the first, the rest the
+// second, so no workgroup is idle whatever the two shapes.  A workgroup
+// moves `groups` 16-byte groups (256 to kPackGroups, fewer for small copies
+// so that they still spread over every CU): whole rows when a row holds at
+// most that many (narrow rows: one workgroup copies several), else one piece
+// of a row.  Each thread first loads all its groups (up to kPackU, 4 loads
+// each, the source having no alignment), then stores them.
+constexpr int kPackU = 4;
+constexpr int kPackGroups = 256 * kPackU;
+constexpr int64_t kPackMinBlocks = 2048;
+
 __global__ __launch_bounds__(256)
 void pack_kernel(PackJobs jobs) {
-    const PackJob& j = jobs.job[blockIdx.z];
-    const int32_t c4 = (int32_t)blockIdx.x * 256 + (int32_t)threadIdx.x;
-    if (4 * c4 >= j.cols_p) return;
-    for (int32_t r = blockIdx.y; r < j.rows_p; r += gridDim.y) {
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < j.rows) {
-            const float* s = j.src + (int64_t)r * j.ld + 4 * c4;
-            const int32_t left = j.cols - 4 * c4;
-            if (left > 0) v.x = s[0];
-            if (left > 1) v.y = s[1];
-            if (left > 2) v.z = s[2];
-            if (left > 3) v.w = s[3];
+    const bool second = (int64_t)blockIdx.x >= jobs.job[0].blocks;
+    const PackJob& j = jobs.job[second ? 1 : 0];
+    const int64_t b = (int64_t)blockIdx.x - (second ? jobs.job[0].blocks : 0);
+    const int32_t cols4 = j.cols_p / 4;
+    int32_t row[kPackU], c4[kPackU];
+    if (j.pieces_per_row > 0) {
+        // one piece of one row: groups [p * groups, (p + 1) * groups)
+        const int32_t r = (int32_t)(b / j.pieces_per_row);
+        const int32_t c0 = (int32_t)(b - (int64_t)r * j.pieces_per_row) * j.groups;
+#pragma unroll
+        for (int u = 0; u < kPackU; ++u) {
+            const int32_t l = u * 256 + (int32_t)threadIdx.x;
+            row[u] = l < j.groups ? r : j.rows_p;                   // past the piece: nothing
+            c4[u] = c0 + l;
         }
-        *reinterpret_cast<float4*>(j.dst + (int64_t)r * j.ldd + 4 * c4) = v;
+    } else {
+        // rows_per_block whole rows, flattened
+        const int32_t r0 = (int32_t)b * j.rows_per_block;
+#pragma unroll
+        for (int u = 0; u < kPackU; ++u) {
+            const int32_t l = u * 256 + (int32_t)threadIdx.x;
+            const int32_t rl = l / cols4;
+            row[u] = rl < j.rows_per_block ? r0 + rl : j.rows_p;     // past the block's rows: nothing
+            c4[u] = l - rl * cols4;
+        }
     }
+    float4 v[kPackU];
+#pragma unroll
+    for (int u = 0; u < kPackU; ++u) {
+        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (row[u] < j.rows && c4[u] < cols4) {
+            const float* s = j.src + (int64_t)row[u] * j.ld + 4 * c4[u];
+            const int32_t left = j.cols - 4 * c4[u];
+            if (left > 0) v[u].x = s[0];
+            if (left > 1) v[u].y = s[1];
+            if (left > 2) v[u].z = s[2];
+            if (left > 3) v[u].w = s[3];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kPackU; ++u)
+        if (row[u] < j.rows_p && c4[u] < cols4)
+            *reinterpret_cast<float4*>(j.dst + (int64_t)row[u] * j.ldd + 4 * c4[u]) = v[u];
 }
 
 // Stream-K fix-up (see the stream-K decomposition of the MFMA kernel):
@@ -278,18 +315,40 @@ hipError_t launch_streamk_fixup(const GemmArgs& g, int bm, int bn, int sk_tiles,
     return hipGetLastError();
 }
 
-hipError_t launch_pack(const PackJobs& jobs, hipStream_t stream) {
-    if (jobs.count < 1 || jobs.count > 2) return hipErrorInvalidValue;
-    int32_t cols_p = 0, rows_p = 0;
+hipError_t launch_pack(const PackJobs& in, hipStream_t stream) {
+    if (in.count < 1 || in.count > 2) return hipErrorInvalidValue;
+    PackJobs jobs = in;
+    int64_t all_groups = 0;
     for (int i = 0; i < jobs.count; ++i) {
         const PackJob& j = jobs.job[i];
-        if (j.ldd < j.cols_p || j.ldd % 4 != 0 || j.cols_p % 4 != 0) return hipErrorInvalidValue;
-        cols_p = std::max(cols_p, j.cols_p);
-        rows_p = std::max(rows_p, j.rows_p);
+        if (j.ldd < j.cols_p || j.ldd % 4 != 0 || j.cols_p % 4 != 0 || j.cols_p <= 0 || j.rows_p <= 0 ||
+            j.rows > j.rows_p || j.cols > j.cols_p)
+            return hipErrorInvalidValue;
+        all_groups += (int64_t)j.rows_p * (j.cols_p / 4);
     }
-    const unsigned gx = (unsigned)((cols_p / 4 + 255) / 256);
-    const unsigned gy = (unsigned)std::min<int32_t>(std::max<int32_t>(rows_p, 1), 65535);
-    hipLaunchKernelGGL(pack_kernel, dim3(gx, gy, (unsigned)jobs.count), dim3(256), 0, stream, jobs);
+    // groups per workgroup: the most that still gives kPackMinBlocks workgroups, at least 256
+    int32_t groups = kPackGroups;
+    while (groups > 256 && all_groups / groups < kPackMinBlocks) groups /= 2;
+    int64_t total = 0;
+    for (int i = 0; i < 2; ++i) {
+        PackJob& j = jobs.job[i];
+        j.blocks = 0;
+        j.groups = groups;
+        j.rows_per_block = 0;
+        j.pieces_per_row = 0;
+        if (i >= jobs.count) continue;
+        const int32_t cols4 = j.cols_p / 4;
+        if (cols4 > groups) {
+            j.pieces_per_row = (cols4 + groups - 1) / groups;
+            j.blocks = (int64_t)j.rows_p * j.pieces_per_row;
+        } else {
+            j.rows_per_block = groups / cols4;
+            j.blocks = (j.rows_p + j.rows_per_block - 1) / j.rows_per_block;
+        }
+        total += j.blocks;
+    }
+    if (total > 0xffffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)total), dim3(256), 0, stream, jobs);
     return hipGetLastError();
 }
 

@@ -307,6 +307,8 @@ PACK_CASES = [
     (513, 385, 272, 273, 387, 3),       # both leading dimensions odd, NaN in the gaps
     (1, 1, 1, None, None, 3),
     (600, 517, 333, 335, None, 3),      # several 256 x 256 tiles, ragged in every dimension
+    (70, 40, 4501, None, None, 3),      # A rows of 1126 16-byte groups (two packing pieces), B rows of 10
+    (97, 4099, 33, 35, 4101, 3),        # B rows of 1025 groups (a one-group second piece), A rows of 9
 ]
 
 
