@@ -145,7 +145,7 @@ double mfma_efficiency(int tile, bool vec) {
     if (!vec) {
         switch (tile) {
             case 2: return 0.64;
-            case 3: return 0.47;
+            case 3: return 0.40;
             default: return 0.0;
         }
     }
@@ -361,7 +361,7 @@ bool mfma_best(const sgemm_options& o, bool vec, int ops, int64_t M, int64_t N, 
     return have;
 }
 
-constexpr double kPackBw = 3.8e12;   // bytes/s read + written by the pack kernel
+constexpr double kPackBw = 5.5e12;   // bytes/s read + written by the pack kernel
 
 // The skinny path's plan for tile `tile` (N columns, K deep; M <= the
 // tile's bm).  The kernel streams B fastest when every CU holds one
