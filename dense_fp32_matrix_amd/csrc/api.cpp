@@ -153,23 +153,13 @@ double mfma_efficiency(int tile, bool vec) {
         case 0: return 0.93;
         case 1: return 0.927;
         case 2: return 0.91;
-        case 3: return 0.82;
+        case 3: return 0.85;
         default: return 0.70;
     }
 }
 
-// Share of the CU's peak when the CU holds a single workgroup of a tile
-// built for two or more per CU (a tail shorter than one wave of
-// workgroups).  The 64 x 64 tile, which moves twice the bytes per
-// multiply-add of the 128 x 128 tile through the CU's load path and LDS,
-// runs faster with them to itself.
-double mfma_alone_efficiency(int tile, bool vec) {
-    const double e = mfma_efficiency(tile, vec);
-    return tile == 3 ? 1.05 * e : e;
-}
-
 // Filling and draining one tile's pipeline, and its epilogue (seconds).
-double tile_visit(int tile) { return tile == 3 ? 0.8e-6 : 2.4e-6; }
+double tile_visit(int tile) { return tile == 3 ? 0.3e-6 : 2.4e-6; }
 
 int wgs_per_cu(const TileShape& t) { return std::max(1, t.waves_per_simd * 4 / (t.waves_m * t.waves_n)); }
 
@@ -190,11 +180,12 @@ Candidate tiles_candidate(int tile, bool vec, int64_t M, int64_t N, int64_t K, i
     const double visit = tile_visit(tile);
     const double wg_time =
         (double)t.bm * t.bn * c.k_chunk * per_cu / (kMacRate * mfma_efficiency(tile, vec)) + visit * per_cu;
-    // a tail of at most one workgroup per CU runs alone on its CU
+    // a tail of at most one workgroup per CU runs alone on its CU, at the
+    // CU's rate (for a tile built for two per CU: in half the time)
     double tail_time = 0;
     if (tail > 0)
         tail_time = (tail <= kNumCUs && per_cu > 1)
-                        ? (double)t.bm * t.bn * c.k_chunk / (kMacRate * mfma_alone_efficiency(tile, vec)) + visit
+                        ? (double)t.bm * t.bn * c.k_chunk / (kMacRate * mfma_efficiency(tile, vec)) + visit
                         : wg_time;
     c.time = full_waves * wg_time + tail_time;
     if (c.splits > 1) c.time += (2.0 * c.splits + 1) * M * N * 4 / kPartialBw + kSplitLaunch;

@@ -70,7 +70,8 @@ constexpr TileShape kMfmaTiles[] = {
     {256, 256, 16, 4, 2, 2, 3},               // 1: as 0 with three stages (faster when both operands are k-contiguous)
     {128, 128, 16, 2, 4, 2, 4, true, true},   // 2: 8 waves of 64 x 32, four stages (three with 4-byte lanes):
                                               //    fewer tiles than CUs at 256 x 256, long K
-    {64, 64, 32, 2, 2, 2, 3, true, true},     // 3: 4 waves of 32 x 32: small products, thin M or N
+    {64, 64, 16, 2, 2, 2, 4, true, true},     // 3: 4 waves of 32 x 32, four stages (three with 4-byte lanes):
+                                              //    small products, thin M or N
 };
 constexpr int kNumMfmaTiles = sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]);
 

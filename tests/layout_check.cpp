@@ -184,9 +184,9 @@ int main() {
     check_rbk<64, 16>();
     check_rbk<128, 32>();
     // the matrix-core tile table: 256 x 256 x 16 (4 x 2 waves, two tiles),
-    // 128 x 128 x 16 (2 x 4 waves), 64 x 64 x 32 (2 x 2 waves)
+    // 128 x 128 x 16 (2 x 4 waves), 64 x 64 x 16 (2 x 2 waves)
     dump_all_ops<256, 256, 16, 4, 2>(0);
     dump_all_ops<128, 128, 16, 2, 4>(2);
-    dump_all_ops<64, 64, 32, 2, 2>(3);
+    dump_all_ops<64, 64, 16, 2, 2>(3);
     return failures == 0 ? 0 : 1;
 }
