@@ -815,14 +815,14 @@ sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_option
     if (q.packed & 1) {
         float* Ap = reinterpret_cast<float*>(wsb + p.pack_a_off);
         jobs.job[jobs.count++] = PackJob{A, lda, (int32_t)c.a_rows(), (int32_t)c.a_cols(), Ap, p.a_ld,
-                                         (int32_t)p.a_rows, (int32_t)p.a_cols};
+                                         (int32_t)p.a_rows, (int32_t)p.a_cols, 0, 0, 0, 0};   // launch_pack sets the rest
         A = Ap;
         lda = p.a_ld;
     }
     if (q.packed & 2) {
         float* Bp = reinterpret_cast<float*>(wsb + p.pack_b_off);
         jobs.job[jobs.count++] = PackJob{B, ldb, (int32_t)c.b_rows(), (int32_t)c.b_cols(), Bp, p.b_ld,
-                                         (int32_t)p.b_rows, (int32_t)p.b_cols};
+                                         (int32_t)p.b_rows, (int32_t)p.b_cols, 0, 0, 0, 0};
         B = Bp;
         ldb = p.b_ld;
     }
