@@ -436,9 +436,7 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
     sgemm_plan& q = p.pub;
     q.split_k = 1;
     q.decomposition = SGEMM_DECOMP_TILES;
-    if (o.path == SGEMM_PATH_VALU || o.path == SGEMM_PATH_SKINNY) {
-        if (trans) return SGEMM_ERR_INVALID_ARG;      // those kernels read row-major A and B only
-    }
+    if (o.path == SGEMM_PATH_VALU && trans) return SGEMM_ERR_INVALID_ARG;   // it reads A and B as stored only
     if (M == 0 || N == 0 || !c.reads_ab()) {
         // nothing to write, or C = beta * C (the empty sum, or alpha == 0)
         q.path = o.path == SGEMM_PATH_AUTO ? SGEMM_PATH_MFMA : o.path;
@@ -460,8 +458,15 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
 
     int path = o.path;
     if (path == SGEMM_PATH_AUTO) {
-        path = (M <= 32 && !trans) ? SGEMM_PATH_SKINNY : SGEMM_PATH_MFMA;
+        path = M <= 32 ? SGEMM_PATH_SKINNY : SGEMM_PATH_MFMA;
         o.tile = -1;                 // the tile index belongs to an explicit path
+    }
+    if (path == SGEMM_PATH_SKINNY) {
+        // the skinny kernel's 16-byte loads: B's rows (and A's, as stored,
+        // k-contiguous); A stored transposed is read as single floats
+        const bool a_ok = c.ta || (aligned(c.A, 16) && c.lda % 4 == 0 && K % 4 == 0);
+        const bool b_ok = aligned(c.B, 16) && c.ldb % 4 == 0 && (c.tb ? K % 4 == 0 : N % 4 == 0);
+        q.vector = (a_ok && b_ok && o.vector == 0) ? 1 : 0;
     }
     if (path == SGEMM_PATH_SKINNY && M > 32) return SGEMM_ERR_INVALID_ARG;
     const int ntiles = tile_count(path);
@@ -532,11 +537,10 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
         // tiles for one row), and it is often what leaves a wave of tiles
         // part-full.  Then the main kernel can take the rows above and the
         // skinny kernel, which streams B once for up to 32 rows, the last
-        // ones.  Operands as stored (the skinny kernel's layout) only; taken
-        // when the time model prefers it (row_tail 0) or whenever possible
-        // (row_tail 2), if the scratch fits.
+        // ones, in any operand layout; taken when the time model prefers it
+        // (row_tail 0) or whenever possible (row_tail 2), if the scratch fits.
         const int64_t r = M % 64;
-        if (!trans && o.row_tail != 1 && r >= 1 && r <= 32 && M - r >= 64) {
+        if (o.row_tail != 1 && r >= 1 && r <= 32 && M - r >= 64) {
             const int64_t kt = q.packed ? p.kp : K;
             Candidate main_rows, tail;
             sgemm_options to{};   // the tail's own plan: the options steer the main kernel
@@ -869,7 +873,7 @@ sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_option
         switch (q.path) {
             case SGEMM_PATH_NAIVE: e = launch_naive(g, stream); break;
             case SGEMM_PATH_VALU: e = launch_valu(q.tile, q.vector != 0, g, q.split_k, stream); break;
-            case SGEMM_PATH_SKINNY: e = launch_skinny(q.tile, q.vector != 0, g, q.split_k, stream); break;
+            case SGEMM_PATH_SKINNY: e = launch_skinny(q.tile, q.vector != 0, ops, g, q.split_k, stream); break;
             default: e = launch_mfma(q.tile, q.vector != 0, ops, g, q.split_k, stream); break;
         }
     }
@@ -888,7 +892,7 @@ sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_option
         float* const c_tail = C + Mm * c.ldc;
         float* const tws = reinterpret_cast<float*>(wsb + p.tail_ws_off);
         GemmArgs gt = g;
-        gt.A = A + Mm * lda;
+        gt.A = c.ta ? A + Mm : A + Mm * lda;     // rows Mm.. of op(A): columns of A stored transposed
         gt.M = r;
         gt.k_chunk = (int32_t)tc.k_chunk;
         gt.tiles_m = 1;
@@ -914,7 +918,7 @@ sgemm_status run(const Call& c, float* C, hipStream_t stream, const sgemm_option
             gt.ldc = p.tail_ldw;
             gt.c_slice = r * p.tail_ldw;
         }
-        e = launch_skinny(tc.tile, q.vector != 0, gt, (int)tc.splits, stream);
+        e = launch_skinny(tc.tile, q.vector != 0, (c.ta ? 1 : 0) | (c.tb ? 2 : 0), gt, (int)tc.splits, stream);
         if (e == hipSuccess && p.tail_second) {
             if (tc.decomposition == SGEMM_DECOMP_STREAM_K)
                 e = launch_streamk_fixup(gt, kSkinnyTiles[tc.tile].bm, kSkinnyTiles[tc.tile].bn, (int)tc.sk_tiles,

@@ -86,7 +86,7 @@ constexpr int kNumNaiveTiles = 1;
 
 // Skinny products (M <= 32): a workgroup of 4 waves owns 16 (or 32) rows x
 // 64 columns and one K slice, split over its waves; K slices are multiples
-// of bk = 64, the stream-K unit.
+// of bk = 64, the stream-K unit.  Built for the four operand layouts.
 constexpr TileShape kSkinnyTiles[] = {
     {16, 64, 64, 1, 4, 2},     // 0: one 16-row block of A (M <= 16)
     {32, 64, 64, 1, 4, 2},     // 1: two 16-row blocks of A (M <= 32)
@@ -98,7 +98,7 @@ hipError_t launch_naive(const GemmArgs& g, hipStream_t stream);
 // (4-byte lanes) only for the tiles marked `narrow`.
 hipError_t launch_mfma(int tile, bool vec, int ops, const GemmArgs& g, int splits, hipStream_t stream);
 hipError_t launch_valu(int tile, bool vec, const GemmArgs& g, int splits, hipStream_t stream);
-hipError_t launch_skinny(int tile, bool vec, const GemmArgs& g, int splits, hipStream_t stream);
+hipError_t launch_skinny(int tile, bool vec, int ops, const GemmArgs& g, int splits, hipStream_t stream);
 
 // C[i][j] = sum_{z=0}^{splits-1} W[z*w_slice + i*ldw + j], summed in order z = 0, 1, ...
 hipError_t launch_splitk_reduce(const float* W, int64_t ldw, int64_t w_slice, int splits,

@@ -20,6 +20,13 @@
 //   * A (M x K, at most 16 MT rows) is read from L2 as 16-byte runs of one
 //     row; with two 16-row blocks (MT = 2, M <= 32) each B vector feeds the
 //     MFMAs of both blocks, so B is still read once;
+//   * B stored transposed (N x K, k-contiguous, the weight layout of a
+//     linear layer): lane l = 16 * kk + jj instead loads row n + 16g + jj of
+//     the stored B at k = k0 + 4kk .. 4kk+3 for each column group g = 0..3,
+//     and component t of that vector is the B operand of MFMA (t, g): the
+//     four components are the MFMA's k = 4kk + t, the 16 lanes jj its 16
+//     columns; MFMA (t, g) accumulates columns n + 16g + j.  A stored
+//     transposed (K x M) is read as single floats (A is small and cached);
 //   * masked-off elements (rows >= M, columns >= N, k past the slice) load
 //     from a 16-byte zero block, so loads are never followed by a select;
 //   * two register stages of 2 k-groups of 16 each keep 2 x 2 x 4 = 16 16-byte
@@ -53,10 +60,13 @@ constexpr int kRegK = 16 * kGroups;        // K elements per register stage per 
 // written as alpha * sum + beta * out to out[i * ldo + c] for rows i < M and
 // strip columns c < col_lim.  MT: 16-row blocks of A (M <= 16 MT); every B
 // vector feeds MT x 4 MFMAs.
-template <bool VEC, int WAVES, int MT>
+// OPS: bit 0 = A stored transposed (K x M), bit 1 = B stored transposed (N x K).
+template <bool VEC, int WAVES, int MT, int OPS>
 __device__ __forceinline__ void skinny_segment(const GemmArgs& g, float (&red)[WAVES][16 * MT][64], int n_w,
                                                int kb, int ke, float* out, int64_t ldo, int col_lim, float alpha,
                                                float beta) {
+    constexpr bool TA = (OPS & 1) != 0;
+    constexpr bool TB = (OPS & 2) != 0;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -67,14 +77,17 @@ __device__ __forceinline__ void skinny_segment(const GemmArgs& g, float (&red)[W
     const int wkb = min(ke, kb + wave * kq);
     const int wke = min(ke, wkb + kq);
 
+    // this lane's row of A in each row block: element k of it at a_row[b][k * a_step]
     bool a_row_ok[MT];
     const float* a_row[MT];
+    const int64_t a_step = TA ? g.lda : 1;
 #pragma unroll
     for (int b = 0; b < MT; ++b) {
         a_row_ok[b] = 16 * b + jj < g.M;
-        a_row[b] = g.A + (int64_t)(a_row_ok[b] ? 16 * b + jj : 0) * g.lda;
+        const int64_t row = a_row_ok[b] ? 16 * b + jj : 0;
+        a_row[b] = g.A + (TA ? row : row * g.lda);
     }
-    const int ncol = n_w + 4 * jj;               // first of this lane's 4 columns
+    const int ncol = n_w + 4 * jj;               // B as stored: first of this lane's 4 columns
 
     static_assert(MT == 1 || MT == 2, "one or two row blocks");
     f32x4 ra[2][MT][kGroups];
@@ -83,32 +96,55 @@ __device__ __forceinline__ void skinny_segment(const GemmArgs& g, float (&red)[W
     auto load_stage = [&](int buf, int k0) {
 #pragma unroll
         for (int gi = 0; gi < kGroups; ++gi) {
-            const int ka = k0 + 16 * gi + 4 * kk;          // this lane's 4 k's
+            // this lane's 4 k's; with B transposed, a lane's two k-groups are
+            // adjacent, so the 4 lanes of a column read 128 contiguous bytes
+            // of its row per stage (A follows the same k order)
+            const int ka = TB ? k0 + 8 * kk + 4 * gi : k0 + 16 * gi + 4 * kk;
 #pragma unroll
             for (int b = 0; b < MT; ++b) {
-                if constexpr (VEC) {
+                if constexpr (VEC && !TA) {
                     const bool ok = a_row_ok[b] && ka < wke;
                     ra[buf][b][gi] = *reinterpret_cast<const f32x4*>(ok ? a_row[b] + ka : kZeroSkinny);
                 } else {
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const bool ok = a_row_ok[b] && ka + t < wke;
-                        ra[buf][b][gi][t] = *(ok ? a_row[b] + ka + t : kZeroSkinny);
+                        ra[buf][b][gi][t] = *(ok ? a_row[b] + (int64_t)(ka + t) * a_step : kZeroSkinny);
                     }
                 }
             }
+            if constexpr (TB) {
+                // rb[buf][gi][q]: stored row n_w + 16q + jj of B, k = ka .. ka + 3
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int k = ka + t;
-                const float* brow = g.B + (int64_t)k * g.ldb;
-                if constexpr (VEC) {
-                    const bool ok = k < wke && ncol < g.N;
-                    rb[buf][gi][t] = *reinterpret_cast<const f32x4*>(ok ? brow + ncol : kZeroSkinny);
-                } else {
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n_w + 16 * q + jj;
+                    const float* bcol = g.B + (int64_t)n * g.ldb;
+                    if constexpr (VEC) {
+                        const bool ok = n < g.N && ka < wke;
+                        rb[buf][gi][q] = *reinterpret_cast<const f32x4*>(ok ? bcol + ka : kZeroSkinny);
+                    } else {
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const bool ok = k < wke && ncol + c < g.N;
-                        rb[buf][gi][t][c] = *(ok ? brow + ncol + c : kZeroSkinny);
+                        for (int t = 0; t < 4; ++t) {
+                            const bool ok = n < g.N && ka + t < wke;
+                            rb[buf][gi][q][t] = *(ok ? bcol + ka + t : kZeroSkinny);
+                        }
+                    }
+                }
+            } else {
+                // rb[buf][gi][q]: row k = ka + q of B, this lane's 4 columns
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int k = ka + t;
+                    const float* brow = g.B + (int64_t)k * g.ldb;
+                    if constexpr (VEC) {
+                        const bool ok = k < wke && ncol < g.N;
+                        rb[buf][gi][t] = *reinterpret_cast<const f32x4*>(ok ? brow + ncol : kZeroSkinny);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const bool ok = k < wke && ncol + c < g.N;
+                            rb[buf][gi][t][c] = *(ok ? brow + ncol + c : kZeroSkinny);
+                        }
                     }
                 }
             }
@@ -121,6 +157,9 @@ __device__ __forceinline__ void skinny_segment(const GemmArgs& g, float (&red)[W
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[b][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // MFMA (t, c): A component t (k = 4kk + t); as stored, B vector t
+    // component c (columns 4j + c) into acc[c]; B transposed, B vector c
+    // component t (columns 16c + j) into acc[c]
     auto compute_stage = [&](int buf) {
 #pragma unroll
         for (int gi = 0; gi < kGroups; ++gi)
@@ -130,8 +169,8 @@ __device__ __forceinline__ void skinny_segment(const GemmArgs& g, float (&red)[W
                 for (int c = 0; c < 4; ++c)
 #pragma unroll
                     for (int b = 0; b < MT; ++b)
-                        acc[b][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[buf][b][gi][t], rb[buf][gi][t][c],
-                                                                         acc[b][c], 0, 0, 0);
+                        acc[b][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            ra[buf][b][gi][t], TB ? rb[buf][gi][c][t] : rb[buf][gi][t][c], acc[b][c], 0, 0, 0);
     };
 
     const int nst = (wke - wkb + kRegK - 1) / kRegK;
@@ -147,13 +186,20 @@ __device__ __forceinline__ void skinny_segment(const GemmArgs& g, float (&red)[W
         if (s < nst) compute_stage(0);
     }
 
-    // wave partials -> LDS: row block b, MFMA c, register r is row 16b + 4kk + r, column 4jj + c
+    // wave partials -> LDS: row block b, MFMA c, register r is row 16b + 4kk + r,
+    // column 4jj + c (B as stored) or 16c + jj (B transposed)
 #pragma unroll
     for (int b = 0; b < MT; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            *reinterpret_cast<f32x4*>(&red[wave][16 * b + 4 * kk + r][4 * jj]) =
-                f32x4{acc[b][0][r], acc[b][1][r], acc[b][2][r], acc[b][3][r]};
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (TB) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) red[wave][16 * b + 4 * kk + r][16 * c + jj] = acc[b][c][r];
+            } else {
+                *reinterpret_cast<f32x4*>(&red[wave][16 * b + 4 * kk + r][4 * jj]) =
+                    f32x4{acc[b][0][r], acc[b][1][r], acc[b][2][r], acc[b][3][r]};
+            }
+        }
     __syncthreads();
 
     // sum the wave partials in wave order and write rows < M, columns < col_lim
@@ -184,7 +230,7 @@ __device__ __forceinline__ void skinny_segment(const GemmArgs& g, float (&red)[W
 //    the stream-K fix-up kernel sums each strip's slots in workgroup order.
 //    Strip j of the unit order is tile_coords' column of tile j, as the
 //    fix-up kernel maps it.
-template <bool VEC, int WAVES, int MT>
+template <bool VEC, int WAVES, int MT, int OPS>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES), amdgpu_waves_per_eu(2, 2)))
 void skinny_gemm_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) float red[WAVES][16 * MT][64];
@@ -235,27 +281,38 @@ void skinny_gemm_kernel(GemmArgs g) {
         }
         if (!first) __syncthreads();       // the previous segment is done with the LDS
         first = false;
-        skinny_segment<VEC, WAVES, MT>(g, red, n_w, kb, ke, out, ldo, col_lim, alpha, beta);
+        skinny_segment<VEC, WAVES, MT, OPS>(g, red, n_w, kb, ke, out, ldo, col_lim, alpha, beta);
         it += step;
     }
 }
 
-template <int WAVES, int MT>
-hipError_t launch_waves(bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
+template <int WAVES, int MT, int OPS>
+hipError_t launch_ops(bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
     dim3 grid(g.sk_iters > 0 ? (unsigned)g.sk_grid : (unsigned)g.tiles_n, 1, g.sk_iters > 0 ? 1u : (unsigned)splits);
     if (vec)
-        hipLaunchKernelGGL((skinny_gemm_kernel<true, WAVES, MT>), grid, dim3(64 * WAVES), 0, stream, g);
+        hipLaunchKernelGGL((skinny_gemm_kernel<true, WAVES, MT, OPS>), grid, dim3(64 * WAVES), 0, stream, g);
     else
-        hipLaunchKernelGGL((skinny_gemm_kernel<false, WAVES, MT>), grid, dim3(64 * WAVES), 0, stream, g);
+        hipLaunchKernelGGL((skinny_gemm_kernel<false, WAVES, MT, OPS>), grid, dim3(64 * WAVES), 0, stream, g);
     return hipGetLastError();
+}
+
+template <int WAVES, int MT>
+hipError_t launch_waves(bool vec, int ops, const GemmArgs& g, int splits, hipStream_t stream) {
+    switch (ops) {
+        case 0: return launch_ops<WAVES, MT, 0>(vec, g, splits, stream);
+        case 1: return launch_ops<WAVES, MT, 1>(vec, g, splits, stream);
+        case 2: return launch_ops<WAVES, MT, 2>(vec, g, splits, stream);
+        case 3: return launch_ops<WAVES, MT, 3>(vec, g, splits, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_skinny(int tile, bool vec, const GemmArgs& g, int splits, hipStream_t stream) {
+hipError_t launch_skinny(int tile, bool vec, int ops, const GemmArgs& g, int splits, hipStream_t stream) {
     switch (tile) {
-        case 0: return launch_waves<kSkinnyTiles[0].waves_n, kSkinnyTiles[0].bm / 16>(vec, g, splits, stream);
-        case 1: return launch_waves<kSkinnyTiles[1].waves_n, kSkinnyTiles[1].bm / 16>(vec, g, splits, stream);
+        case 0: return launch_waves<kSkinnyTiles[0].waves_n, kSkinnyTiles[0].bm / 16>(vec, ops, g, splits, stream);
+        case 1: return launch_waves<kSkinnyTiles[1].waves_n, kSkinnyTiles[1].bm / 16>(vec, ops, g, splits, stream);
         default: return hipErrorInvalidValue;
     }
 }

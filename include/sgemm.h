@@ -131,7 +131,7 @@ typedef enum sgemm_decomposition {
  *                   the rasterisation of "如何让计算受限问题真正达到计算受限" section
  *                   5.2), 1 = plain row-major (for comparison).  Results are the
  *                   same bits either way.
- *   row_tail      : matrix-core path, operands as stored, M 1 to 32 rows past a
+ *   row_tail      : matrix-core path, any operand layout, M 1 to 32 rows past a
  *                   multiple of 64: run those last rows through the skinny kernel
  *                   after the main kernel has done the rows above, instead of a row
  *                   of output tiles that is mostly padding (the edge handling of
@@ -215,8 +215,9 @@ sgemm_status sgemm_plan_query(int64_t M, int64_t N, int64_t K,
  * fused beta * C + (alpha * sum).  sgemm(...) is sgemm_gemm(N, N, ..., 1,
  * ..., 0, ...).  C may not overlap A or B when they are read; errors,
  * streams and workspace as for sgemm / sgemm_ex.  Operands stored
- * transposed are read by the matrix-core path (or the naive path when
- * forced); forcing the VALU or skinny path with them is SGEMM_ERR_INVALID_ARG.
+ * transposed are read by the matrix-core path, by the skinny path (M <= 32)
+ * and by the naive path when forced; forcing the VALU path with them is
+ * SGEMM_ERR_INVALID_ARG.
  */
 typedef enum sgemm_op {
     SGEMM_OP_N = 0,   /* the operand as stored */

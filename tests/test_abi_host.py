@@ -109,14 +109,19 @@ def test_gemm_plans():
     q = lib.gemm_plan_query("N", "T", 512, 512, 511, path="mfma", tile=0, split_k=1, decomposition="tiles",
                             pack="always")
     assert q["packed"] == 3 and q["k_padded"] == 512
-    # the paths that read row-major operands only
-    for kw in ({"path": "valu"}, {"path": "skinny"}):
-        with pytest.raises(lib.SgemmError):
-            lib.gemm_plan_query("N", "T", 16, 512, 512, **kw)
+    # the VALU path reads operands as stored only
+    with pytest.raises(lib.SgemmError):
+        lib.gemm_plan_query("N", "T", 16, 512, 512, path="valu")
     assert lib.gemm_plan_query("T", "T", 300, 200, 20, path="naive")["path_name"] == "naive"
-    # M <= 32 with a transposed operand: the MFMA path, not the skinny one
-    assert lib.gemm_plan_query("N", "T", 16, 11008, 4096)["path_name"] == "mfma"
-    assert lib.gemm_plan_query("N", "T", 32, 11008, 4096)["path_name"] == "mfma"
+    # M <= 32 in every layout: the skinny path; its 16-byte loads need B's rows
+    # (k-contiguous when B is transposed) and, as stored, A's rows aligned
+    for ops in [("N", "T"), ("T", "N"), ("T", "T")]:
+        for m in (1, 16, 32):
+            q = lib.gemm_plan_query(*ops, m, 11008, 4096)
+            assert q["path_name"] == "skinny" and q["vector"] == 1, (ops, m, q)
+    assert lib.gemm_plan_query("N", "T", 16, 11008, 4095)["vector"] == 0          # odd K: B's rows misaligned
+    assert lib.gemm_plan_query("T", "N", 16, 11008, 4095, lda=17)["vector"] == 1  # A read as single floats
+    assert lib.gemm_plan_query("N", "N", 16, 11008, 4095)["vector"] == 0          # A's rows misaligned
     assert lib.gemm_workspace_size("N", "T", M, N, K) == p["workspace_bytes"]
 
 
@@ -431,8 +436,8 @@ def test_fma_probe_rejects_bad_arguments():
 
 
 def test_row_tail_plans():
-    """The row tail: M 1-32 rows past a multiple of 64 with operands as
-    stored; the main kernel's tiles cover the rows above it."""
+    """The row tail: M 1-32 rows past a multiple of 64, in every operand
+    layout; the main kernel's tiles cover the rows above it."""
     p = lib.sgemm_plan_query(4097, 3001, 2049, lda=2049, ldb=3001, ldc=3001)
     assert p["tail_rows"] == 1 and p["tiles_m"] == 4096 // p["bm"] and p["packed"] == 3
     q = lib.sgemm_plan_query(4097, 3001, 2049, lda=2049, ldb=3001, ldc=3001, row_tail="never")
@@ -441,8 +446,8 @@ def test_row_tail_plans():
     assert lib.sgemm_plan_query(4128, 4096, 4096, row_tail="always")["tail_rows"] == 32
     for M in (4096, 4129, 4160, 63, 100):          # none, 33 rows, a multiple, too few rows above
         assert lib.sgemm_plan_query(M, 512, 512, row_tail="always")["tail_rows"] == 0, M
-    # operands stored transposed keep the full tile grid (the skinny kernel reads them as stored only)
-    assert lib.gemm_plan_query("N", "T", 4097, 512, 512, row_tail="always")["tail_rows"] == 0
-    assert lib.gemm_plan_query("N", "N", 4097, 512, 512, row_tail="always")["tail_rows"] == 1
+    for ops in [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]:
+        q = lib.gemm_plan_query(*ops, 4097, 512, 512, row_tail="always")
+        assert q["tail_rows"] == 1 and q["tiles_m"] == 4096 // q["bm"], (ops, q)
     with pytest.raises(lib.SgemmError):
         lib.sgemm_plan_query(4097, 512, 512, row_tail=3)

@@ -191,3 +191,76 @@ def test_linear_layer_full_size(oracle_mod):
     rhs = oracle_mod.gemv(Xn, oracle_mod.gemv(Wtn, v))
     scale = oracle_mod.gemv(Xn, oracle_mod.gemv(Wtn, np.abs(v), absolute=True), absolute=True)
     assert np.all(np.abs(lhs - rhs) <= 1e-5 * scale + 1e-12)
+
+
+# --- the skinny path (M <= 32) in every operand layout ------------------------------------
+
+SKINNY_LAYOUT_SHAPES = [
+    (1, 1, 1),
+    (5, 300, 1000),       # ragged N and K
+    (16, 1000, 4100),     # K past a 64-deep step
+    (17, 257, 129),       # two row blocks, N one past a strip
+    (32, 65, 333),
+    (9, 11008, 512),      # many strips
+]
+SKINNY_PLANS = [
+    {"path": "skinny"},
+    {"path": "skinny", "decomposition": "tiles", "split_k": 1},
+    {"path": "skinny", "decomposition": "tiles", "split_k": 3},
+    {"path": "skinny", "decomposition": "stream_k"},
+    {"path": "skinny", "decomposition": "stream_k", "vector": 1},
+]
+
+
+@pytest.mark.parametrize("plan", SKINNY_PLANS, ids=lambda p: "-".join(f"{k}{v}" for k, v in p.items()))
+@pytest.mark.parametrize("shape", SKINNY_LAYOUT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("ta,tb", LAYOUTS, ids=lambda v: str(int(v)))
+def test_skinny_layouts(oracle_mod, ta, tb, shape, plan):
+    """The skinny kernel reads A stored K x M as single floats and B stored
+    N x K as 16-byte runs along k (four k of one column per lane), in every
+    decomposition, with alpha and beta."""
+    M, N, K = shape
+    q = lib.gemm_plan_query("T" if ta else "N", "T" if tb else "N", M, N, K, alpha=2.0, beta=-0.5, **plan)
+    assert q["path_name"] == "skinny"
+    check(oracle_mod, M, N, K, ta, tb, "skinny", **plan)
+
+
+@pytest.mark.parametrize("case", [
+    (513, 385, 272, {}),
+    (80, 130, 70, {}),                                                  # 16 rows, K tail
+    (96, 100, 300, {}),                                                 # 32 rows (two row blocks)
+    (577, 301, 205, {"pack": "always"}),                               # packed operands
+    (4097, 257, 1000, {"path": "mfma", "tile": 0}),
+    (1040, 600, 900, {"path": "mfma", "tile": 2, "decomposition": "stream_k"}),
+], ids=lambda c: "x".join(map(str, c[:3])))
+@pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)], ids=lambda v: str(int(v)))
+def test_row_tail_transposed(oracle_mod, ta, tb, case):
+    """The row tail with operands stored transposed: the skinny kernel takes
+    rows M - r .. M - 1 of op(A) (columns of A stored K x M) after the main
+    kernel."""
+    M, N, K, opts = case
+    q = lib.gemm_plan_query("T" if ta else "N", "T" if tb else "N", M, N, K, alpha=2.0, beta=-0.5,
+                            row_tail="always", **opts)
+    assert q["tail_rows"] == M % 64
+    check(oracle_mod, M, N, K, ta, tb, "row tail", row_tail="always", **opts)
+
+
+@pytest.mark.parametrize("kind", ["normal", "integer"])
+def test_decode_linear_full_size(oracle_mod, kind):
+    """The skinny workload in nn.Linear's layout: X (16 x 4096) . W^T with W
+    stored 11008 x 4096, as the default plan (the skinny path) runs it; every
+    element against the oracle."""
+    say(f"decode linear N/T full size {kind}")
+    M, N, K = 16, 11008, 4096
+    X = workloads.draw(M, K, kind, 4242)
+    W = workloads.draw(N, K, kind, 4243, std=(1.0 / 64 if kind == "normal" else 1.0))
+    plan = lib.gemm_plan_query("N", "T", M, N, K)
+    assert plan["path_name"] == "skinny" and plan["vector"] == 1
+    Cd = lib.gemm(X.to(DEV), W.to(DEV), trans_b=True)
+    torch.cuda.synchronize()
+    C = Cd.cpu().numpy()
+    ref, D = oracle_mod.gemm(X.numpy(), W.numpy(), trans_b=True, with_denominator=True)
+    if kind == "integer":
+        assert_bit_exact(C, oracle_mod.round_to_f32(ref), what="decode N/T integer, every element")
+    else:
+        assert_within_bound(C, ref, D, what="decode N/T, every element")
