@@ -110,13 +110,14 @@ int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 // concurrent workgroups work on different K ranges and so share little in
 // L2, cannot read its operands faster than kStreamKReadBw.  The constants
 // were searched for the least loss against the fastest measured candidate
-// on 576 random shapes (528 with M, N, K log-uniform in 256-8192, every tile
-// with K split 1, 2, 4 and 8 ways and as stream-K; 48 with M, N in 256-1448
-// and K in 11600-65536, splits 4-32): the chosen candidate is then 0.6 %
-// slower than the fastest on average and over 5 % slower on 23 shapes (2.7 %
-// and 112 shapes with the constants before).  The packing rate and launch
-// and the 4-byte-lane efficiencies come from 80 shapes with M, N, K odd
-// (every candidate on packed copies and on the operands as they are).
+// on random shapes with every candidate timed (M, N, K log-uniform in
+// 256-8192, every tile with K split 1, 2, 4 and 8 ways and as stream-K; M, N
+// in 256-1448 with K in 11600-65536, splits 4-32).  The packing rate and
+// launch and the 4-byte-lane efficiencies come from 80 shapes with M, N, K
+// odd (every candidate on packed copies and on the operands as they are).
+// On 196 fresh shapes timed afterwards the default plan is, on average, within
+// 1 % of the fastest fixed candidate timed beside it (short K, long K, odd
+// sizes, transposed operands).
 // ---------------------------------------------------------------------------
 constexpr double kMacRate = 128.0 * 2.4e9;   // FP32 MACs per second per CU at peak
 constexpr double kPartialBw = 5.5e12;        // bytes/s for split-K partial slices (mostly cache resident)
