@@ -299,6 +299,25 @@ void choose_split(int64_t tiles, int64_t K, int bk, int64_t target_wgs, int64_t 
     *k_chunk = kc;
 }
 
+// The matrix-core kernel addresses each direct-load lane by a 32-bit byte
+// offset from a wave-uniform base at its tile's first element (the
+// scalar-base form of the loads), so a tile runs only where the farthest
+// element of its K-step lies within 2^32 bytes of that base, for both
+// operands at the leading dimensions the kernel reads them with: for a
+// k-contiguous operand, a row stride below about 2^30 / (R - 1) floats (R the
+// tile's rows), for a k-major one below about 2^30 / 15.
+// One operand: k-contiguous (kc) or k-major, `extent` the tile's size
+// outside K (BM for A, BN for B).
+bool operand_fits(int tile, bool kc, int64_t extent, int64_t ld) {
+    const int64_t bk = kMfmaTiles[tile].bk;
+    const int64_t farthest = kc ? (extent - 1) * ld + (bk - 1) : (bk - 1) * ld + (extent - 1);   // floats
+    return farthest <= (int64_t(1) << 30) - 4;
+}
+bool offsets_fit(int tile, int ops, int64_t lda, int64_t ldb) {
+    return operand_fits(tile, (ops & 1) == 0, kMfmaTiles[tile].bm, lda) &&
+           operand_fits(tile, (ops & 2) != 0, kMfmaTiles[tile].bn, ldb);
+}
+
 // Best MFMA plan for the given operand alignment (vec), operand layouts
 // (ops: bit 0 = A stored transposed, bit 1 = B stored transposed) and K;
 // false when no tile fits (a forced 256 x 256 tile with 4-byte lanes).
@@ -306,10 +325,11 @@ void choose_split(int64_t tiles, int64_t K, int bk, int64_t target_wgs, int64_t 
 // k-contiguous and B k-major, or A k-major (NN, TN, TT: +0.3 to +1.4 %) and
 // the three-stage one (1) with both k-contiguous (NT: +1 %), so the
 // automatic choice takes each where it is faster.
-// Candidates whose partial products need more than ws_cap bytes of scratch
-// are left out.
-bool mfma_best(const sgemm_options& o, bool vec, int ops, int64_t M, int64_t N, int64_t K, size_t ws_cap,
-               Candidate* out) {
+// Candidates whose partial products need more than ws_cap bytes of scratch,
+// and tiles whose load offsets do not fit at these leading dimensions, are
+// left out.
+bool mfma_best(const sgemm_options& o, bool vec, int ops, int64_t M, int64_t N, int64_t K, int64_t lda,
+               int64_t ldb, size_t ws_cap, Candidate* out) {
     std::vector<int> cands;
     if (o.tile >= 0) cands.push_back(o.tile);
     else cands = {ops == 2 ? 1 : 0, 2, 3};
@@ -317,6 +337,7 @@ bool mfma_best(const sgemm_options& o, bool vec, int ops, int64_t M, int64_t N, 
     bool have = false;
     for (int tile : cands) {
         if (!vec && !kMfmaTiles[tile].narrow) continue;   // built for 16-byte lanes only
+        if (!offsets_fit(tile, ops, lda, ldb)) continue;
         std::vector<Candidate> cs;
         if (o.decomposition != SGEMM_DECOMP_STREAM_K) {
             if (o.split_k > 0) {
@@ -477,6 +498,23 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
         ((path != SGEMM_PATH_MFMA && path != SGEMM_PATH_SKINNY) || o.split_k > 1))
         return SGEMM_ERR_INVALID_ARG;
 
+    // Leading dimensions too long for the load offsets of every matrix-core
+    // tile, as stored and as packed copies: the vector-ALU kernel (operands
+    // as stored) or the one-thread-per-output kernel, which address with
+    // 64-bit offsets, take the product.
+    const int64_t kp4 = round_up(K, 4);
+    const int64_t packed_lda = round_up(c.ta ? round_up(M, 4) : kp4, 32);
+    const int64_t packed_ldb = round_up(c.tb ? kp4 : round_up(N, 4), 32);
+    bool mfma_fits = false;
+    for (int t = 0; t < kNumMfmaTiles; ++t) {
+        if (o.path == SGEMM_PATH_MFMA && o.tile >= 0 && t != o.tile) continue;
+        mfma_fits = mfma_fits || offsets_fit(t, ops, c.lda, c.ldb) || offsets_fit(t, ops, packed_lda, packed_ldb);
+    }
+    if (path == SGEMM_PATH_MFMA && !mfma_fits) {
+        if (o.path != SGEMM_PATH_AUTO) return SGEMM_ERR_UNSUPPORTED;
+        path = trans ? SGEMM_PATH_NAIVE : SGEMM_PATH_VALU;
+    }
+
     Candidate best;
     size_t copies_bytes = 0;     // packed copies of the chosen MFMA plan
     double best_pack_time = 0;   // and their cost in the time model
@@ -490,27 +528,36 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
     } else if (path == SGEMM_PATH_MFMA) {
         // With 4-byte lanes only the narrow tiles are built; a forced tile
         // without them can still run on packed copies.
-        bool have = mfma_best(o, q.vector != 0, ops, M, N, K, ws_cap, &best);
+        bool have = mfma_best(o, q.vector != 0, ops, M, N, K, c.lda, c.ldb, ws_cap, &best);
         const bool built = q.vector != 0 || o.tile < 0 || kMfmaTiles[o.tile].narrow;
         if (!have && !built && (o.vector == 1 || o.pack == 1)) return SGEMM_ERR_INVALID_ARG;
         // Alternative: copy the misaligned operand(s), in their stored
         // orientation, into aligned, zero-padded workspace first and run the
         // 16-byte loaders.  A K that the KC layout would cut mid-chunk is
         // padded to a multiple of 4, which both operands must then carry.
-        if (!vec_ok && o.vector == 0 && o.pack != 1) {
+        // Without a plan on the operands as they are (leading dimensions too
+        // long for the load offsets), the copies also shorten them.
+        if ((!vec_ok || !have) && o.vector == 0 && o.pack != 1) {
             const int64_t kp = k_ok ? K : round_up(K, 4);
-            const bool pack_a = !a_rows_ok || kp != K;
-            const bool pack_b = !b_rows_ok || kp != K;
             // packed stored shapes: the K dimension padded to kp, the contiguous one to a multiple of 4
             const int64_t ar = c.ta ? kp : M, ac = c.ta ? round_up(M, 4) : kp;
             const int64_t br = c.tb ? N : kp, bc = c.tb ? kp : round_up(N, 4);
+            bool a_fits = false, b_fits = false;   // some candidate tile's offsets fit the operand as stored
+            for (int t = 0; t < kNumMfmaTiles; ++t) {
+                if (o.tile >= 0 && t != o.tile) continue;
+                a_fits = a_fits || operand_fits(t, !c.ta, kMfmaTiles[t].bm, c.lda);
+                b_fits = b_fits || operand_fits(t, c.tb, kMfmaTiles[t].bn, c.ldb);
+            }
+            const bool pack_a = !a_rows_ok || kp != K || (!have && !a_fits);
+            const bool pack_b = !b_rows_ok || kp != K || (!have && !b_fits);
             double bytes = 0;
             if (pack_a) bytes += 4.0 * (c.a_rows() * c.a_cols() + ar * ac);
             if (pack_b) bytes += 4.0 * (c.b_rows() * c.b_cols() + br * bc);
             const size_t copies = (pack_a ? align256((size_t)(ar * round_up(ac, 32)) * sizeof(float)) : 0) +
                                   (pack_b ? align256((size_t)(br * round_up(bc, 32)) * sizeof(float)) : 0);
             Candidate cand;
-            const bool fits = copies <= ws_cap && mfma_best(o, true, ops, M, N, kp, ws_cap - copies, &cand);
+            const bool fits = copies <= ws_cap && mfma_best(o, true, ops, M, N, kp, pack_a ? round_up(ac, 32) : c.lda,
+                                                            pack_b ? round_up(bc, 32) : c.ldb, ws_cap - copies, &cand);
             const double pack_time = bytes / kPackBw + kPackLaunch;
             cand.time += pack_time;
             if (fits && (o.pack == 2 || !have || cand.time < best.time)) {
@@ -553,7 +600,8 @@ sgemm_status make_plan_uncached(const Call& c, const sgemm_options* opts, size_t
                     : (tail.splits > 1 ? (size_t)(tail.splits * r * round_up(N, 4)) * sizeof(float) : 0);
             const size_t room = ws_cap == SIZE_MAX ? SIZE_MAX : ws_cap - std::min(ws_cap, copies_bytes + tail_ws + 512);
             if (copies_bytes + tail_ws + 512 <= ws_cap &&
-                mfma_best(o, q.vector != 0, ops, M - r, N, kt, room, &main_rows)) {
+                mfma_best(o, q.vector != 0, ops, M - r, N, kt, (q.packed & 1) ? p.a_ld : c.lda,
+                          (q.packed & 2) ? p.b_ld : c.ldb, room, &main_rows)) {
                 const double alt = main_rows.time + best_pack_time + tail.time;   // the tail's time holds its launches
                 if (o.row_tail == 2 || alt < best.time) {
                     best = main_rows;

@@ -47,6 +47,7 @@ SGEMM_HD int a_swizzle(int r) {
 template <int R, int BK, int W>
 struct KcLayout {
     static constexpr bool KC = true;
+    static constexpr int EXTENT = R;                      // rows (the non-K dimension) of the stage
     static constexpr int SEG = 64 * W;                    // floats one instruction writes
     static constexpr int FLOATS = R * BK;
     static constexpr int INSTR = FLOATS / SEG;
@@ -65,6 +66,7 @@ struct KcLayout {
 template <int R, int BK, int W>
 struct KmLayout {
     static constexpr bool KC = false;
+    static constexpr int EXTENT = R;                      // floats per k row (the non-K dimension)
     static constexpr int SEG = 64 * W;
     static constexpr int ROWS = 256 / R;                  // k rows per 1 KB block
     static constexpr int GS = 256 + 8 * ROWS;            // floats between blocks

@@ -192,41 +192,54 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void glb_void_t;
 
 // The direct loads of one operand that one wave issues per K-step: PER
-// instructions, ins = i * waves + wave.  Each keeps a running per-lane
-// source pointer that one issue advances by one K-step (steps are issued in
-// order), so a step inside the K range costs one 64-bit add per load.
+// instructions, ins = i * waves + wave.  Each lane's element of load i sits
+// at a fixed byte offset off[i] from a wave-uniform base, the tile's first
+// element at the current K-step, which an issue moves on by one K-step with
+// a scalar add (steps are issued in order).  Inside the K range the loads
+// take the scalar-base form of global_load_lds (the base in scalar
+// registers, one 32-bit offset register per lane); a per-lane 64-bit pointer
+// per load, advanced with a 64-bit vector add every step, measured 1.8 %
+// slower for the 256 x 256 tile at 4096^3, 3 % for the 128 x 128 tile and
+// 6.5 % for the 64 x 64 tile.  The offsets are 32-bit: the dispatcher runs
+// a tile only where the farthest element of its K-step lies within 2^32
+// bytes of the base (for a k-contiguous operand a row stride below about
+// 2^30 / (R - 1) floats, R the tile's extent outside K).
 // r0 is the tile's first non-K index and lim its bound (M or N): lanes past
 // it read the last valid row (k-contiguous layout), or the last whole lane
 // group of columns (k-major layout: a lane fetches L::SEG / 64 consecutive
 // columns, so the clamp keeps its first column a multiple of that width and
 // its last one inside the stored row), instead; that data only reaches
-// outputs outside C that are never written.  Only the K range needs the zero block,
-// on the steps that cross its end (checked()).
+// outputs outside C that are never written.  The clamped index is never
+// below r0, so no offset is negative.  Only the K range needs the zero
+// block, on the steps that cross its end (checked()).
 template <class L, int PER>
 struct DtlLoads {
-    const float* ptr[PER];
+    const float* base;
+    uint32_t off[PER];
     int kk[PER];
     int64_t step;
     __device__ __forceinline__ void init(const float* X, int64_t ld, int wave, int waves, int lane, int r0, int lim,
                                          int kb, int bk) {
+        base = X + (L::KC ? (int64_t)r0 * ld + kb : (int64_t)kb * ld + r0);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             int r, k;
             L::elem(i * waves + wave, lane, r, k);
-            const int rr = clamp_index<L>(r0 + r, lim);
-            ptr[i] = X + (L::KC ? (int64_t)rr * ld + kb + k : (int64_t)(kb + k) * ld + rr);
+            const int d = clamp_index<L>(r0 + r, lim) - r0;
+            off[i] = (uint32_t)((L::KC ? (int64_t)d * ld + k : (int64_t)k * ld + d) * 4);
             kk[i] = k;
         }
         step = L::KC ? (int64_t)bk : (int64_t)bk * ld;
     }
+    // this lane's source of load i at the current K-step
+    __device__ __forceinline__ const float* src(int i) const {
+        return reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + off[i]);
+    }
     // source of load i for the step starting at k0, zero block past ke
     __device__ __forceinline__ const float* checked(int i, int k0, int ke) const {
-        return k0 + kk[i] < ke ? ptr[i] : kZeroMfma;
+        return k0 + kk[i] < ke ? src(i) : kZeroMfma;
     }
-    __device__ __forceinline__ void advance() {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) ptr[i] += step;
-    }
+    __device__ __forceinline__ void advance() { base += step; }
 };
 
 // s_waitcnt that waits for vmcnt <= N and nothing else (gfx9 encoding).
@@ -260,6 +273,17 @@ __device__ __forceinline__ void dma_lanes(const float* src, const float* lds) {
         asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base));
     else
         asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(base));
+}
+
+// The same load with a wave-uniform source base in scalar registers and a
+// 32-bit byte offset per lane (global_load_lds with saddr).
+template <int W>
+__device__ __forceinline__ void dma_lanes_s(uint32_t off, const float* src_base, const float* lds) {
+    const uint32_t base = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+    if constexpr (W == 4)
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(src_base), "{m0}"(base));
+    else
+        asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(src_base), "{m0}"(base));
 }
 
 // Race check (built with SGEMM_LDS_POISON=1, never in the product library):
@@ -317,6 +341,7 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
 
     // issue the direct loads of the next K-step (`step`) into stage `st`;
     // FULL: the whole step lies inside [kb, ke), so no lane needs the check
+    // (the scalar-base form)
     auto issue = [&](int step, float* st, auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
         const int k0 = kb + step * BK;
@@ -327,12 +352,19 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
             for (int i = 0; i < B_PER; ++i) poison_lanes<W>(st + LA::FLOATS + LB::dst(i * WAVES + wave), lane);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
+        if constexpr (FULL) {
 #pragma unroll
-        for (int i = 0; i < A_PER; ++i)
-            dma_lanes<W>(FULL ? la.ptr[i] : la.checked(i, k0, ke), st + LA::dst(i * WAVES + wave));
+            for (int i = 0; i < A_PER; ++i) dma_lanes_s<W>(la.off[i], la.base, st + LA::dst(i * WAVES + wave));
 #pragma unroll
-        for (int i = 0; i < B_PER; ++i)
-            dma_lanes<W>(FULL ? lb.ptr[i] : lb.checked(i, k0, ke), st + LA::FLOATS + LB::dst(i * WAVES + wave));
+            for (int i = 0; i < B_PER; ++i)
+                dma_lanes_s<W>(lb.off[i], lb.base, st + LA::FLOATS + LB::dst(i * WAVES + wave));
+        } else {
+#pragma unroll
+            for (int i = 0; i < A_PER; ++i) dma_lanes<W>(la.checked(i, k0, ke), st + LA::dst(i * WAVES + wave));
+#pragma unroll
+            for (int i = 0; i < B_PER; ++i)
+                dma_lanes<W>(lb.checked(i, k0, ke), st + LA::FLOATS + LB::dst(i * WAVES + wave));
+        }
         la.advance();
         lb.advance();
     };
@@ -448,7 +480,7 @@ __device__ __forceinline__ void mfma_tile_dtl(const GemmArgs& g, float* st0, flo
         // The first loop runs whole trips of iterations whose refill step lies
         // inside the K range (s + DS - 1 < full_steps); the second finishes
         // with the checked loads (and the loads past the end, which read zeros).
-        // (4-byte lanes, with 8x the loads, keep one checked loop: a second
+        // (4-byte lanes, with 4x the loads, keep one checked loop: a second
         // copy of the loop would not fit their registers.)
         int s = 1;
         if constexpr (W == 4) {

@@ -451,3 +451,44 @@ def test_row_tail_plans():
         assert q["tail_rows"] == 1 and q["tiles_m"] == 4096 // q["bm"], (ops, q)
     with pytest.raises(lib.SgemmError):
         lib.sgemm_plan_query(4097, 512, 512, row_tail=3)
+
+
+def test_long_leading_dimensions():
+    """The matrix-core loads address each lane by a 32-bit byte offset from
+    its tile's first element, so a tile runs only where the farthest element
+    of its K-step is within 2^32 bytes: (R - 1) * ld + 15 floats for a
+    k-contiguous operand with R rows, 15 * ld + R - 1 for a k-major one.
+    Longer strides take a smaller tile, packed copies (which shorten the
+    stride), or, when even those are too long, the vector-ALU kernel
+    (operands as stored) or the one-thread-per-output kernel."""
+    lim = (1 << 30) - 4
+
+    def fits(rows, ld):          # k-contiguous operand of a tile with `rows` rows
+        return (rows - 1) * ld + 15 <= lim
+
+    ld = 5_000_000               # too long for the 256-row tiles, not for the 128-row one
+    assert not fits(256, ld) and fits(128, ld)
+    p = lib.gemm_plan_query("N", "N", 300, 64, 48, lda=ld)
+    assert p["path_name"] == "mfma" and p["tile"] in (2, 3) and p["packed"] == 0, p
+    for tile in (0, 1):
+        with pytest.raises(lib.SgemmError):
+            lib.gemm_plan_query("N", "N", 300, 64, 48, lda=ld, path="mfma", tile=tile, pack="never")
+        q = lib.gemm_plan_query("N", "N", 300, 64, 48, lda=ld, path="mfma", tile=tile)
+        assert q["tile"] == tile and q["packed"] & 1, q          # the packed copy's stride fits
+    ld = 20_000_000              # too long for every tile: A is packed (its copy's stride is 64)
+    assert not fits(64, ld)
+    p = lib.gemm_plan_query("N", "N", 40, 64, 48, lda=ld)
+    assert p["path_name"] == "mfma" and p["packed"] == 1, p
+    p = lib.gemm_plan_query("N", "N", 64, 64, 16, ldb=72_000_000)   # k-major B: 15 * ldb > 2^30
+    assert p["path_name"] == "mfma" and p["packed"] == 2, p
+    p = lib.gemm_plan_query("T", "N", 64, 64, 16, lda=72_000_000)   # k-major A
+    assert p["path_name"] == "mfma" and p["packed"] == 1, p
+    # K itself too long for any tile's rows, packed or not
+    K = 17_100_000
+    assert not fits(64, K)
+    assert lib.gemm_plan_query("N", "N", 33, 4, K)["path_name"] == "valu"
+    assert lib.gemm_plan_query("N", "T", 33, 4, K)["path_name"] == "naive"
+    with pytest.raises(lib.SgemmError):
+        lib.gemm_plan_query("N", "N", 33, 4, K, path="mfma")
+    # the skinny path does not use these loads
+    assert lib.gemm_plan_query("N", "N", 32, 4, K)["path_name"] == "skinny"

@@ -264,3 +264,48 @@ def test_decode_linear_full_size(oracle_mod, kind):
         assert_bit_exact(C, oracle_mod.round_to_f32(ref), what="decode N/T integer, every element")
     else:
         assert_within_bound(C, ref, D, what="decode N/T, every element")
+
+
+def _long_stride_dev(x, ld):
+    """Device view of the CPU (rows, cols) tensor x with row stride ld; only
+    the rows' own elements are written (the gap between them is never read)."""
+    rows, cols = x.shape
+    buf = torch.empty((rows - 1) * ld + cols, device=DEV)
+    v = buf.as_strided((rows, cols), (ld, 1))
+    v.copy_(x.to(DEV))
+    return v
+
+
+# Leading dimensions too long for the matrix-core loads' 32-bit lane offsets
+# at some or every tile: (op A, op B, M, N, K, lda, ldb, forced plan, path
+# taken).  The operands take several GB of device memory.
+LONG_STRIDES = [
+    (False, False, 300, 64, 48, 5_000_000, None, {}, "mfma"),                      # 128/64-row tiles as stored
+    (False, False, 300, 64, 48, 5_000_000, None, {"path": "mfma", "tile": 0}, "mfma"),   # packed copy of A
+    (False, False, 64, 64, 16, None, 72_000_000, {}, "mfma"),                      # k-major B, packed
+    (False, False, 33, 4, 17_100_000, None, None, {}, "valu"),                      # K too long for any tile
+    (False, True, 33, 4, 17_100_000, None, None, {}, "naive"),
+]
+
+
+@pytest.mark.parametrize("case", LONG_STRIDES, ids=lambda c: f"{'NT'[c[0]]}{'NT'[c[1]]}-{c[2]}x{c[3]}x{c[4]}-"
+                         f"lda{c[5]}-ldb{c[6]}-{c[8]}-{'forced' if c[7] else 'auto'}")
+def test_long_leading_dimensions(oracle_mod, case):
+    """Products whose leading dimensions (or K) exceed what the matrix-core
+    loads can address with 32-bit lane offsets give the oracle's result
+    through a smaller tile, packed copies, or the 64-bit-addressed kernels."""
+    ta, tb, M, N, K, lda, ldb, opts, path = case
+    say(f"long strides ta={ta} tb={tb} M={M} N={N} K={K} lda={lda} ldb={ldb} opts={opts}")
+    A, B, _ = stored(M, N, K, ta, tb, "uniform", 900 + M + N)
+    Ad = _long_stride_dev(A, lda) if lda else A.to(DEV)
+    Bd = _long_stride_dev(B, ldb) if ldb else B.to(DEV)
+    p = lib.gemm_plan_query("T" if ta else "N", "T" if tb else "N", M, N, K, lda=Ad.stride(0), ldb=Bd.stride(0),
+                            **opts)
+    assert p["path_name"] == path, p
+    C = torch.full((M, N), float("nan"), device=DEV)
+    lib.gemm(Ad, Bd, C, trans_a=ta, trans_b=tb, **opts)
+    torch.cuda.synchronize()
+    del Ad, Bd
+    torch.cuda.empty_cache()
+    ref, D = oracle_mod.gemm(A.numpy(), B.numpy(), trans_a=ta, trans_b=tb, with_denominator=True)
+    assert_within_bound(C.cpu().numpy(), ref, D, what=f"long strides {case}")
