@@ -151,10 +151,10 @@ double mfma_efficiency(int tile, bool vec) {
         }
     }
     switch (tile) {
-        case 0: return 0.93;
-        case 1: return 0.927;
-        case 2: return 0.91;
-        case 3: return 0.85;
+        case 0: return 0.947;
+        case 1: return 0.944;
+        case 2: return 0.938;
+        case 3: return 0.905;
         default: return 0.70;
     }
 }
