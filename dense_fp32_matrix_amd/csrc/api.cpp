@@ -145,8 +145,8 @@ constexpr double kSkinnySegment = 0.1e-6;      // per stream-K segment of a stri
 double mfma_efficiency(int tile, bool vec) {
     if (!vec) {
         switch (tile) {
-            case 2: return 0.64;
-            case 3: return 0.40;
+            case 2: return 0.89;
+            case 3: return 0.83;
             default: return 0.0;
         }
     }
