@@ -322,9 +322,10 @@ bool offsets_fit(int tile, int ops, int64_t lda, int64_t ldb) {
 // (ops: bit 0 = A stored transposed, bit 1 = B stored transposed) and K;
 // false when no tile fits (a forced 256 x 256 tile with 4-byte lanes).
 // Of the two 256 x 256 tiles, the two-stage one (0) measured faster with A
-// k-contiguous and B k-major, or A k-major (NN, TN, TT: +0.3 to +1.4 %) and
-// the three-stage one (1) with both k-contiguous (NT: +1 %), so the
-// automatic choice takes each where it is faster.
+// k-contiguous and B k-major (NN: +0.1 to +0.9 %) or A k-major (TN, TT:
+// +0.1 to +0.9 %) and the three-stage one (1) with both k-contiguous (NT:
+// +0.15 to +0.3 % from K = 4096 up, -0.4 % at K = 1024), so the automatic
+// choice takes each where it is faster.
 // Candidates whose partial products need more than ws_cap bytes of scratch,
 // and tiles whose load offsets do not fit at these leading dimensions, are
 // left out.
