@@ -59,7 +59,9 @@ typedef enum sgemm_status {
     SGEMM_OK = 0,
     SGEMM_ERR_INVALID_ARG = 1,  /* negative size, ld too small, NULL pointer with a
                                    nonzero extent, C overlapping A or B, bad option */
-    SGEMM_ERR_UNSUPPORTED = 2,  /* a size beyond the kernels' index range */
+    SGEMM_ERR_UNSUPPORTED = 2,  /* a size beyond the kernels' index range, or a forced
+                                   matrix-core plan whose leading dimensions are too long
+                                   for its loads' 32-bit offsets (see sgemm_ex) */
     SGEMM_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed */
     SGEMM_ERR_ALLOC = 4,        /* scratch allocation failed, or the caller's
                                    workspace is too small */
@@ -101,6 +103,14 @@ typedef enum sgemm_decomposition {
 
 /*
  * Options for sgemm_ex.  Zero-initialised options mean "same as sgemm".
+ * The matrix-core tiles address each load lane by a 32-bit byte offset from
+ * its tile's first element, so a tile runs only where its K-step spans less
+ * than 2^32 bytes: for A stored as is (and B stored transposed) a row stride
+ * below about 2^30 / (rows of the tile - 1) floats, for the other layouts
+ * below about 2^30 / 15.  The automatic choice then takes a smaller tile or
+ * packed copies, and where neither fits (K itself that long) the vector-ALU
+ * path (operands as stored) or the naive path; forcing the matrix-core path
+ * on such operands is SGEMM_ERR_UNSUPPORTED.
  *   path          : an sgemm_path.
  *   tile          : index into the path's tile table (sgemm_tile_info), or -1 to choose;
  *                   ignored when path is SGEMM_PATH_AUTO.
