@@ -62,9 +62,9 @@ struct TileShape {
 // Matrix-core tiles.  Every one reads its operands with direct global -> LDS
 // loads and is built for the four operand layouts (A and B each as stored or
 // stored transposed).  The 256 x 256 tiles are built for 16-byte load lanes
-// only: with 4-byte lanes their running load pointers do not fit the
-// registers left next to 128 accumulators per lane, so unaligned operands
-// take the 128 x 128 or 64 x 64 tile, or are packed.
+// only: with 4-byte lanes their four times as many load offsets do not fit
+// the registers left next to 128 accumulators per lane, so unaligned
+// operands take the 128 x 128 or 64 x 64 tile, or are packed.
 constexpr TileShape kMfmaTiles[] = {
     {256, 256, 16, 4, 2, 2, 2},               // 0: 8 waves (two per SIMD) of 64 x 128; step s + 1 loads during step s
     {256, 256, 16, 4, 2, 2, 3},               // 1: as 0 with three stages (faster when both operands are k-contiguous)
