@@ -492,3 +492,39 @@ def test_long_leading_dimensions():
         lib.gemm_plan_query("N", "N", 33, 4, K, path="mfma")
     # the skinny path does not use these loads
     assert lib.gemm_plan_query("N", "N", 32, 4, K)["path_name"] == "skinny"
+
+
+def test_planned_tiles_fit_their_load_offsets():
+    """Across random shapes, layouts and long leading dimensions, every
+    matrix-core plan (main rows, after packing) uses a tile whose K-step lies
+    within the loads' 32-bit byte offsets, restated from the rule."""
+    import random
+    rng = random.Random(20261203)
+    info = [lib.sgemm_tile_info("mfma", t) for t in range(lib.sgemm_tile_info("mfma", 0)["count"])]
+    lim = (1 << 30) - 4
+
+    def fits(kc, extent, bk, ld):
+        return (extent - 1) * ld + bk - 1 <= lim if kc else (bk - 1) * ld + extent - 1 <= lim
+
+    checked = restricted = 0
+    for _ in range(400):
+        M, N, K = rng.randint(33, 5000), rng.randint(1, 5000), rng.randint(1, 3000)
+        ta, tb = rng.random() < 0.5, rng.random() < 0.5
+        a_cols, b_cols = (M if ta else K), (K if tb else N)
+        lda = a_cols + rng.choice([0, 1, 7, rng.randint(0, 30_000_000)])
+        ldb = b_cols + rng.choice([0, 3, rng.randint(0, 90_000_000)])
+        # stand-in addresses far enough apart that these long strides do not make C overlap A or B
+        p = lib.gemm_plan_query("T" if ta else "N", "T" if tb else "N", M, N, K, lda=lda, ldb=ldb,
+                                A=1 << 20, B=1 << 42, C=1 << 45)
+        if p["path_name"] != "mfma":
+            continue
+        t = info[p["tile"]]
+        kp = p["k_padded"]
+        # the stride the kernel reads each operand with: a packed copy's rows are padded to 32 floats
+        la = -(-((-(-M // 4) * 4) if ta else kp) // 32) * 32 if p["packed"] & 1 else lda
+        lb = -(-(kp if tb else (-(-N // 4) * 4)) // 32) * 32 if p["packed"] & 2 else ldb
+        assert fits(not ta, t["bm"], t["bk"], la) and fits(tb, t["bn"], t["bk"], lb), (M, N, K, ta, tb, lda, ldb, p)
+        checked += 1
+        # the stride as stored would not fit the 256 x 256 tiles
+        restricted += not (fits(not ta, 256, 16, lda) and fits(tb, 256, 16, ldb))
+    assert checked > 200 and restricted > 50, (checked, restricted)
