@@ -26,7 +26,7 @@ import workloads
 from checks import assert_bit_exact, assert_within_bound
 
 DEV = "cuda:0"
-CASES = 96
+CASES = 400
 
 
 def say(msg):
